@@ -1,0 +1,203 @@
+/*
+ * snrvq.h -- C ABI of the MI355X (gfx950) streaming RVQ codec decoder.
+ *
+ * The library is stage 1 of a two-stage TTS pipeline: it turns batched
+ * per-stream multi-codebook RVQ frames into PCM.  Each stream keeps its
+ * causal-conv left context (and, for configurations with one, its windowed
+ * transformer's K/V), every call decodes only the new frames, and the
+ * concatenated output of a stream equals the decode of its whole utterance
+ * (AREX article on vLLM-Omni / Fish Audio Drama 3, section "two stages share
+ * one card: one forward per frame, stateful streaming decode").
+ *
+ * Codes arrive as [T, Q] frames of Q codebook indices (AI-infra handbook,
+ * "Qwen3-TTS" case, second stop, the stream output builder).  Reference-audio
+ * codes prefixed once to a stream warm its left context without producing
+ * audio (same case, self-test answer 4 and exercise 3): that is
+ * stream_prefill.  The codec's weights, state slots and workspace are all
+ * allocated when it is opened, before any decode (same case, topology: the
+ * vocoder is built before the engine so its memory is resident first; and
+ * the note that incremental-decode state slots cost GPU memory).
+ *
+ * Conventions
+ *   - Every function returns CODEC_OK (0) or one of the CODEC_E* codes; the
+ *     message of the last failure is returned by codec_last_error().
+ *   - Every argument check runs before anything is enqueued: a call that
+ *     fails changes no state, on the host or on the device.
+ *   - Device work is enqueued on the caller's HIP stream (passed as an opaque
+ *     codec_hip_stream, NULL = the default stream) and the call returns
+ *     without waiting for it.  All calls on one codec must be ordered by the
+ *     caller (one host thread at a time, one stream or explicit ordering).
+ *   - Memory: host pointers are read during the call only; device pointers
+ *     (pcm, capture destinations) are written asynchronously on the stream
+ *     and belong to the caller.
+ */
+#ifndef SNRVQ_H
+#define SNRVQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define CODEC_OK 0
+#define CODEC_EINVAL 1  /* null pointer, non-positive size, bad cfg or weight manifest, pcm too small */
+#define CODEC_ESTREAM 2 /* unknown or closed stream id */
+#define CODEC_EDUP 3    /* the same stream twice in one call */
+#define CODEC_ERANGE 4  /* a code outside [0, E), e.g. an EOS id such as 2150 */
+#define CODEC_ENOSLOT 5 /* every state slot is in use */
+#define CODEC_ETOOBIG 6 /* more frames in one call than max_frames_per_call */
+#define CODEC_ENOMEM 7  /* device or pinned allocation failed */
+#define CODEC_EHIP 8    /* a HIP runtime error (its string is in the message) */
+
+/* ---- enums -------------------------------------------------------------- */
+#define CODEC_DTYPE_F32 0
+#define CODEC_DTYPE_BF16 1
+#define CODEC_DTYPE_F16 2
+
+#define CODEC_ACT_SNAKE 0 /* x + sin^2(alpha x) / alpha, per-channel alpha */
+#define CODEC_ACT_ELU 1   /* x > 0 ? x : exp(x) - 1 */
+
+#define CODEC_MAX_STAGES 8
+
+typedef struct codec codec_t;     /* opaque, owned by the library */
+typedef void *codec_hip_stream;   /* a hipStream_t; NULL = default stream */
+
+/* One named parameter in host memory.  dtype CODEC_DTYPE_F32 (float) or
+ * CODEC_DTYPE_BF16 (uint16 bit patterns); row-major with the given shape. */
+typedef struct {
+    const char *name;
+    int32_t dtype;
+    int32_t ndim;
+    int64_t shape[4];
+    const void *host_data;
+} codec_tensor;
+
+/* Decoder shape.  Channels start at d_lat and halve at every upsample stage;
+ * stage i upsamples by strides[i] with a transposed conv of kernel
+ * 2 strides[i] followed by residual units of dilation 1 and 3; hop =
+ * product of strides.  tf_layers = 0 means no transformer.  weight_dtype
+ * F32 runs the fp32 path (fp32 MFMA operands); BF16 weights run on fp16 MFMA
+ * operands with fp32 accumulation and an fp32 residual stream. */
+typedef struct {
+    int32_t K, E, d_cb, d_lat;
+    int32_t n_stages;
+    int32_t strides[CODEC_MAX_STAGES];
+    int32_t sample_rate;
+    int32_t act;        /* CODEC_ACT_* */
+    int32_t final_tanh; /* 0: raw PCM out of the last conv */
+    int32_t tf_layers, tf_heads, tf_head_dim, tf_window, tf_mlp;
+    int32_t weight_dtype; /* CODEC_DTYPE_F32 or CODEC_DTYPE_BF16 */
+    int32_t max_streams;
+    int32_t max_frames_per_call;
+} codec_cfg;
+
+typedef struct {
+    int32_t hop;                 /* PCM samples per frame */
+    int32_t sample_rate;
+    int32_t K, E;
+    int32_t left_context_frames; /* frames of history an output frame depends on */
+    int32_t max_streams, max_frames_per_call, open_streams;
+    int32_t compute_dtype;       /* CODEC_DTYPE_F32 or CODEC_DTYPE_F16 (MFMA operands) */
+    int64_t state_bytes_per_stream;
+    int64_t weight_bytes;
+    int64_t workspace_bytes;
+} codec_info_t;
+
+/* ---- lifetime ----------------------------------------------------------- */
+
+/* Validates cfg and the weight manifest (every canonical parameter present
+ * once with the right shape and dtype), uploads and repacks the weights into
+ * library-owned device memory on the current HIP device, and preallocates
+ * the state slots of max_streams streams and the workspace of
+ * max_frames_per_call frames.  Nothing is allocated later.  The caller's
+ * host arrays may be freed on return.  On failure *out is NULL and the
+ * message is available from codec_last_error(NULL). */
+int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *cfg,
+               codec_t **out);
+
+/* Waits for the codec's device work, frees everything it owns. */
+int codec_close(codec_t *codec);
+
+int codec_info(const codec_t *codec, codec_info_t *out);
+
+/* Message of the last failure on this codec, or of the calling thread's last
+ * codec_open failure when codec is NULL.  Never NULL. */
+const char *codec_last_error(const codec_t *codec);
+
+/* ---- streams ------------------------------------------------------------ */
+
+/* Takes a free state slot; the stream starts with all-zero left context and
+ * position 0.  Host-only bookkeeping: the slot is cleared on the stream's
+ * first decode.  Ids are positive and never reused by this codec. */
+int stream_open(codec_t *codec, int32_t *stream_id_out);
+
+/* Releases the stream's slot.  Later use of the id fails with CODEC_ESTREAM. */
+int stream_close(codec_t *codec, int32_t stream_id);
+
+/* Decodes n frames of codes [n][K] (host memory) into the stream's state and
+ * discards the audio: reference-audio codes used as left context.  n may
+ * exceed max_frames_per_call (it is split into several decodes). */
+int stream_prefill(codec_t *codec, int32_t stream_id, const int32_t *codes, int32_t n,
+                   codec_hip_stream stream);
+
+/* ---- the hot path ------------------------------------------------------- */
+
+/* One batched decode step over B distinct open streams.
+ *   stream_ids [B]    streams in this step (no duplicates)
+ *   n_frames  [B]     new frames per stream, each >= 1 (any mix of sizes)
+ *   codes             host int32, packed stream after stream, then frame,
+ *                     then codebook: [sum n][K]
+ *   pcm               device float32, caller-owned, pcm_capacity elements;
+ *                     stream b's n_b * hop samples are written at
+ *                     pcm[hop * sum_{b' < b} n_b'], in stream order
+ * The dense form decode_chunk(ids, codes[B, n, K]) is the case where every
+ * n_frames[b] == n.  Checks: CODEC_EINVAL (nulls, B < 1, n < 1, capacity),
+ * CODEC_ESTREAM, CODEC_EDUP, CODEC_ETOOBIG (sum n > max_frames_per_call),
+ * CODEC_ERANGE (a code outside [0, E)). */
+int decode_chunk(codec_t *codec, int32_t B, const int32_t *stream_ids, const int32_t *n_frames,
+                 const int32_t *codes, float *pcm, int64_t pcm_capacity,
+                 codec_hip_stream stream);
+
+/* ---- inspection (tests) -------------------------------------------------- */
+
+#define CODEC_CAPTURE_LATENT 0    /* projected RVQ sum, [sum n][d_lat] */
+#define CODEC_CAPTURE_DEC_INPUT 1 /* input of the conv decoder (after the transformer) */
+
+/* Copies an intermediate of the last decode step, as float32, packed like
+ * the codes: [sum n][d_lat].  dst is device memory with capacity elements. */
+int codec_debug_capture(codec_t *codec, int32_t what, float *dst, int64_t capacity,
+                        codec_hip_stream stream);
+
+/* Per-kernel-class device time of the decode steps since the last reset,
+ * measured with HIP events on the decode stream while profiling is on.
+ * names/ms/launches receive up to cap entries; returns the entry count
+ * through *n_out. */
+int codec_profile_enable(codec_t *codec, int32_t on);
+int codec_profile_read(codec_t *codec, int32_t cap, const char **names, double *ms,
+                       int64_t *launches, int64_t *units, int32_t *n_out);
+
+/* ---- host-only chunk policy (no device needed) --------------------------- */
+
+/* New-frame counts of the decodes of an utterance of `total` generated
+ * frames arriving one at a time (AI-infra handbook, "Qwen3-TTS" case, third
+ * stop: decode when the generated count reaches the next threshold; the
+ * threshold grows by the ramp entries, each clamped to `steady`, then by
+ * `steady`; the final chunk decodes the remainder).  initial > 0 replaces
+ * the first ramp entry.  Writes up to cap values to out; *n_out receives the
+ * number of decodes (CODEC_EINVAL when it exceeds cap or arguments are bad). */
+int codec_chunk_plan(int32_t total, const int32_t *ramp, int32_t n_ramp, int32_t steady,
+                     int32_t initial, int32_t *out, int32_t cap, int32_t *n_out);
+
+/* Per-request initial chunk size (same section): has_value = 0 uses
+ * default_frames; the result is clamped to steady.  CODEC_EINVAL when steady
+ * <= 0 or the value is negative. */
+int codec_resolve_initial_chunk_frames(int64_t value, int32_t has_value, int32_t steady,
+                                       int32_t default_frames, int32_t *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SNRVQ_H */

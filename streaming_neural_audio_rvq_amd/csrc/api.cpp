@@ -1,0 +1,1100 @@
+// api.cpp -- the C ABI: validation, weight repacking, the state-slot store,
+// the ragged batcher and the per-step launch sequence.
+//
+// Decode step (all on the caller's stream):
+//   H2D of the packed step metadata (codes, frame->stream map, cu, slots,
+//   fresh flags, positions) from a pinned ring buffer;
+//   halo fill (every conv layer's left context, all streams, one launch);
+//   RVQ gather-and-sum -> projection GEMM -> input conv -> per stage
+//   [ConvT -> RU(d=1) -> RU(d=3)], each RU = conv7 launch + conv1 launch with
+//   the residual add fused into the conv1 epilogue -> final conv to PCM;
+//   halo save (last rows of every extended input back into the slots).
+// Every activation (Snake / ELU) is applied once, in the epilogue of the
+// layer that produces its input, so the stored left context is exactly the
+// operand the next conv multiplies.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "internal.h"
+#include "snrvq.h"
+
+using namespace snrvq;
+
+namespace {
+
+thread_local std::string g_err = "";
+
+int set_err(std::string *dst, int code, const char *fmt, ...)
+{
+    char buf[1024];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (dst)
+        *dst = buf;
+    g_err = buf;
+    return code;
+}
+
+struct Lin {
+    void *Wt = nullptr;
+    float *bias = nullptr;
+    int N = 0, Cout = 0, Cin = 0, taps = 1, dil = 1, s = 1;
+};
+
+struct ActP {
+    float *alpha = nullptr, *ialpha = nullptr;
+};
+
+struct ProfRec {
+    int cls;
+    hipEvent_t a, b;
+    int64_t units;
+};
+
+struct ParamSpec {
+    std::string name;
+    std::vector<int64_t> shape;
+};
+
+const int RU_DIL[2] = {1, 3};
+
+}  // namespace
+
+struct codec {
+    codec_cfg cfg{};
+    int dev = 0;
+    int dtype = 1;  // 1: fp16 MFMA operands, 0: fp32
+    int esz = 2;
+    int S = 0, hop = 1;
+    int ch[CODEC_MAX_STAGES + 1]{};
+    int rate[CODEC_MAX_STAGES + 1]{};
+    int left_ctx = 0;
+    int maxF = 0, maxB = 0;
+
+    std::vector<void *> allocs;
+    void *cb = nullptr;
+    int cb_dtype = 0;
+    Lin proj, in_conv, convT[CODEC_MAX_STAGES], conv7[CODEC_MAX_STAGES][2],
+        conv1[CODEC_MAX_STAGES][2];
+    ActP a_stage[CODEC_MAX_STAGES], a_ru1[CODEC_MAX_STAGES][2], a_ru2[CODEC_MAX_STAGES][2], a_out;
+    float *out_w = nullptr;
+    float out_b = 0.f;
+
+    void *z = nullptr, *u_ext = nullptr, *aT[CODEC_MAX_STAGES]{}, *a1[CODEC_MAX_STAGES]{},
+         *a2[CODEC_MAX_STAGES]{}, *h = nullptr, *a_outb = nullptr;
+    float *x = nullptr, *pcm_scratch = nullptr;
+
+    void *state = nullptr;
+    int64_t slot_elems = 0;
+    HaloTable halo{};
+
+    void *meta_dev = nullptr;
+    size_t meta_cap = 0;  // int32 elements
+    void *pinned[2]{};
+    hipEvent_t pin_ev[2]{};
+    int pin_i = 0;
+    StepMeta last_meta{};
+    int lastF = 0, lastB = 0;
+
+    std::unordered_map<int32_t, int> id2slot;
+    std::vector<int> free_slots;
+    std::vector<int64_t> slot_pos;
+    std::vector<char> slot_fresh;
+    int32_t next_id = 1;
+
+    std::string err;
+    int64_t weight_bytes = 0, workspace_bytes = 0;
+
+    bool prof = false;
+    std::vector<std::string> cls_names;
+    std::vector<double> cls_ms;
+    std::vector<int64_t> cls_launches, cls_units;
+    std::vector<ProfRec> recs;
+    std::vector<hipEvent_t> ev_pool;
+};
+
+namespace {
+
+int fail(codec *c, int code, const char *fmt, ...)
+{
+    char buf[1024];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (c)
+        c->err = buf;
+    g_err = buf;
+    return code;
+}
+
+#define HIPCHK(c, expr)                                                                        \
+    do {                                                                                       \
+        hipError_t e_ = (expr);                                                                \
+        if (e_ != hipSuccess)                                                                  \
+            return fail((c), CODEC_EHIP, "HIP error %s (%d) at %s", hipGetErrorString(e_),     \
+                        (int)e_, #expr);                                                       \
+    } while (0)
+
+int dev_alloc(codec *c, void **p, size_t bytes, int64_t *counter)
+{
+    if (bytes == 0)
+        bytes = 16;
+    hipError_t e = hipMalloc(p, bytes);
+    if (e != hipSuccess) {
+        *p = nullptr;
+        return fail(c, CODEC_ENOMEM, "hipMalloc of %zu bytes failed: %s", bytes,
+                    hipGetErrorString(e));
+    }
+    c->allocs.push_back(*p);
+    if (counter)
+        *counter += (int64_t)bytes;
+    return CODEC_OK;
+}
+
+// ---- canonical parameter list ----------------------------------------------
+std::vector<ParamSpec> param_specs(const codec_cfg &g, const int *ch)
+{
+    std::vector<ParamSpec> v;
+    char n[128];
+    for (int k = 0; k < g.K; k++) {
+        snprintf(n, sizeof n, "rvq.codebook.%d", k);
+        v.push_back({n, {g.E, g.d_cb}});
+    }
+    v.push_back({"rvq.proj.weight", {g.d_lat, g.d_cb}});
+    v.push_back({"rvq.proj.bias", {g.d_lat}});
+    v.push_back({"dec.in_conv.weight", {ch[0], g.d_lat, 7}});
+    v.push_back({"dec.in_conv.bias", {ch[0]}});
+    for (int i = 0; i < g.n_stages; i++) {
+        int ci = ch[i], co = ch[i + 1], s = g.strides[i];
+        snprintf(n, sizeof n, "dec.stage.%d.snake.alpha", i);
+        v.push_back({n, {ci}});
+        snprintf(n, sizeof n, "dec.stage.%d.convT.weight", i);
+        v.push_back({n, {ci, co, 2 * s}});
+        snprintf(n, sizeof n, "dec.stage.%d.convT.bias", i);
+        v.push_back({n, {co}});
+        for (int j = 0; j < 2; j++) {
+            const char *parts[6] = {"snake1.alpha", "conv7.weight", "conv7.bias",
+                                    "snake2.alpha", "conv1.weight", "conv1.bias"};
+            std::vector<int64_t> shp[6] = {{co}, {co, co, 7}, {co}, {co}, {co, co, 1}, {co}};
+            for (int q = 0; q < 6; q++) {
+                snprintf(n, sizeof n, "dec.stage.%d.ru.%d.%s", i, j, parts[q]);
+                v.push_back({n, shp[q]});
+            }
+        }
+    }
+    int cs = ch[g.n_stages];
+    v.push_back({"dec.out.snake.alpha", {cs}});
+    v.push_back({"dec.out.conv.weight", {1, cs, 7}});
+    v.push_back({"dec.out.conv.bias", {1}});
+    return v;
+}
+
+// Host values of a tensor as fp32 (bf16 widening is exact).
+std::vector<float> host_f32(const codec_tensor &t, int64_t n)
+{
+    std::vector<float> out((size_t)n);
+    if (t.dtype == CODEC_DTYPE_F32) {
+        memcpy(out.data(), t.host_data, sizeof(float) * (size_t)n);
+    } else {
+        const uint16_t *b = (const uint16_t *)t.host_data;
+        for (int64_t i = 0; i < n; i++) {
+            uint32_t u = (uint32_t)b[i] << 16;
+            memcpy(&out[(size_t)i], &u, 4);
+        }
+    }
+    return out;
+}
+
+// Upload values in the compute type.
+int upload_compute(codec *c, const std::vector<float> &v, void **dst)
+{
+    size_t n = v.size();
+    int rc = dev_alloc(c, dst, n * c->esz, &c->weight_bytes);
+    if (rc)
+        return rc;
+    if (c->dtype) {
+        std::vector<half_t> h(n);
+        for (size_t i = 0; i < n; i++)
+            h[i] = (half_t)v[i];
+        HIPCHK(c, hipMemcpy(*dst, h.data(), n * 2, hipMemcpyHostToDevice));
+    } else {
+        HIPCHK(c, hipMemcpy(*dst, v.data(), n * 4, hipMemcpyHostToDevice));
+    }
+    return CODEC_OK;
+}
+
+int upload_f32(codec *c, const std::vector<float> &v, float **dst)
+{
+    int rc = dev_alloc(c, (void **)dst, v.size() * 4, &c->weight_bytes);
+    if (rc)
+        return rc;
+    HIPCHK(c, hipMemcpy(*dst, v.data(), v.size() * 4, hipMemcpyHostToDevice));
+    return CODEC_OK;
+}
+
+int upload_act(codec *c, const std::vector<float> &alpha, ActP *a)
+{
+    std::vector<float> inv(alpha.size());
+    for (size_t i = 0; i < alpha.size(); i++)
+        inv[i] = 1.0f / alpha[i];
+    int rc = upload_f32(c, alpha, &a->alpha);
+    if (rc)
+        return rc;
+    return upload_f32(c, inv, &a->ialpha);
+}
+
+// Conv1d weight W[Co][Ci][k] -> Wt[o][tap Ci + c].
+std::vector<float> pack_conv(const std::vector<float> &W, int Co, int Ci, int k)
+{
+    std::vector<float> o((size_t)Co * Ci * k);
+    for (int oc = 0; oc < Co; oc++)
+        for (int c = 0; c < Ci; c++)
+            for (int j = 0; j < k; j++)
+                o[((size_t)oc * k + j) * Ci + c] = W[((size_t)oc * Ci + c) * k + j];
+    return o;
+}
+
+// ConvTranspose1d weight W[Ci][Co][2s] -> polyphase Wt[r Co + o][tap Ci + c]:
+// tap 0 multiplies x[q-1] (kernel index r + s), tap 1 multiplies x[q] (r).
+std::vector<float> pack_convT(const std::vector<float> &W, int Ci, int Co, int s)
+{
+    std::vector<float> o((size_t)s * Co * 2 * Ci);
+    int k = 2 * s;
+    for (int r = 0; r < s; r++)
+        for (int oc = 0; oc < Co; oc++)
+            for (int c = 0; c < Ci; c++) {
+                size_t n = (size_t)r * Co + oc;
+                o[(n * 2 + 0) * Ci + c] = W[((size_t)c * Co + oc) * k + r + s];
+                o[(n * 2 + 1) * Ci + c] = W[((size_t)c * Co + oc) * k + r];
+            }
+    return o;
+}
+
+int make_lin(codec *c, const std::vector<float> &packed, const std::vector<float> &bias, int N,
+             int Cout, int Cin, int taps, int dil, int s, Lin *L)
+{
+    L->N = N;
+    L->Cout = Cout;
+    L->Cin = Cin;
+    L->taps = taps;
+    L->dil = dil;
+    L->s = s;
+    int rc = upload_compute(c, packed, &L->Wt);
+    if (rc)
+        return rc;
+    return upload_f32(c, bias, &L->bias);
+}
+
+// Frames of history that one output frame depends on: walk back from every
+// sample of a frame through the layers (causal conv: i - (k-1) d; transposed
+// conv: floor(i / s) - 1).
+int left_context_frames(const codec_cfg &g, int hop)
+{
+    int best = 0;
+    for (long n = 4L * hop; n < 5L * hop; n++) {
+        long i = n - 6;
+        for (int st = g.n_stages - 1; st >= 0; st--) {
+            i -= 18;
+            i -= 6;
+            long s = g.strides[st];
+            i = (i >= 0 ? i / s : -((-i + s - 1) / s)) - 1;
+        }
+        i -= 6;
+        i -= (long)g.tf_layers * (g.tf_window > 0 ? g.tf_window - 1 : 0);
+        long L = n / hop - i;
+        if (L > best)
+            best = (int)L;
+    }
+    return best;
+}
+
+hipEvent_t get_ev(codec *c)
+{
+    if (c->ev_pool.empty()) {
+        hipEvent_t e;
+        hipEventCreate(&e);
+        return e;
+    }
+    hipEvent_t e = c->ev_pool.back();
+    c->ev_pool.pop_back();
+    return e;
+}
+
+int cls_id(codec *c, const std::string &name)
+{
+    for (size_t i = 0; i < c->cls_names.size(); i++)
+        if (c->cls_names[i] == name)
+            return (int)i;
+    c->cls_names.push_back(name);
+    c->cls_ms.push_back(0.0);
+    c->cls_launches.push_back(0);
+    c->cls_units.push_back(0);
+    return (int)c->cls_names.size() - 1;
+}
+
+template <class Fn>
+int timed(codec *c, const char *name, int64_t units, hipStream_t s, Fn &&fn)
+{
+    hipEvent_t a = nullptr, b = nullptr;
+    if (c->prof) {
+        a = get_ev(c);
+        b = get_ev(c);
+        hipEventRecord(a, s);
+    }
+    hipError_t e = fn();
+    if (c->prof) {
+        hipEventRecord(b, s);
+        c->recs.push_back({cls_id(c, name), a, b, units});
+    }
+    if (e != hipSuccess)
+        return fail(c, CODEC_EHIP, "kernel launch '%s' failed: %s", name, hipGetErrorString(e));
+    return CODEC_OK;
+}
+
+ConvArgs conv_args(codec *c, const Lin &L, const void *A, int A_H, int rate_in, int M,
+                   const StepMeta &m)
+{
+    ConvArgs a{};
+    a.A = A;
+    a.Wt = L.Wt;
+    a.bias = L.bias;
+    a.frame_stream = m.frame_stream;
+    a.M = M;
+    a.A_H = A_H;
+    a.Cin = L.Cin;
+    a.taps = L.taps;
+    a.dil = L.dil;
+    a.rate_in = rate_in;
+    a.N = L.N;
+    a.Cout = L.Cout;
+    a.s = L.s;
+    a.out_ld = L.Cout;
+    a.act = ACT_NONE;
+    return a;
+}
+
+void set_act(codec *c, ConvArgs &a, const ActP &p)
+{
+    a.act = c->cfg.act == CODEC_ACT_ELU ? ACT_ELU : ACT_SNAKE;
+    a.alpha = p.alpha;
+    a.inv_alpha = p.ialpha;
+}
+
+int run_conv(codec *c, const char *name, const ConvArgs &a, hipStream_t s)
+{
+    return timed(c, name, (int64_t)a.M, s, [&] { return launch_conv_gemm(a, c->dtype, s, -1); });
+}
+
+size_t round4(size_t n) { return (n + 3) & ~(size_t)3; }
+
+// One decode step over B streams (slots[] / n[] / codes[] already validated).
+int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int32_t *codes,
+                 float *pcm, hipStream_t s)
+{
+    const codec_cfg &g = c->cfg;
+    int F = 0;
+    for (int b = 0; b < B; b++)
+        F += n[b];
+
+    // ---- batch assembly into the pinned ring, one H2D copy ----
+    size_t o_codes = 0, o_fs = round4(o_codes + (size_t)F * g.K), o_cu = round4(o_fs + F),
+           o_slot = round4(o_cu + B + 1), o_fresh = round4(o_slot + B),
+           o_pos = round4(o_fresh + B), total = round4(o_pos + B);
+    int pi = c->pin_i;
+    c->pin_i ^= 1;
+    HIPCHK(c, hipEventSynchronize(c->pin_ev[pi]));  // the copy that last read this buffer is done
+    int32_t *hp = (int32_t *)c->pinned[pi];
+    memcpy(hp + o_codes, codes, sizeof(int32_t) * (size_t)F * g.K);
+    int acc = 0;
+    hp[o_cu] = 0;
+    for (int b = 0; b < B; b++) {
+        for (int f = 0; f < n[b]; f++)
+            hp[o_fs + acc + f] = b;
+        acc += n[b];
+        hp[o_cu + b + 1] = acc;
+        hp[o_slot + b] = slots[b];
+        hp[o_fresh + b] = c->slot_fresh[slots[b]] ? 1 : 0;
+        hp[o_pos + b] = (int32_t)c->slot_pos[slots[b]];
+    }
+    int32_t *dm = (int32_t *)c->meta_dev;
+    StepMeta m{dm + o_codes, dm + o_fs, dm + o_cu, dm + o_slot, dm + o_fresh, dm + o_pos};
+    int rc = timed(c, "h2d_meta", (int64_t)total * 4, s, [&] {
+        return hipMemcpyAsync(c->meta_dev, hp, total * 4, hipMemcpyHostToDevice, s);
+    });
+    if (rc)
+        return rc;
+    HIPCHK(c, hipEventRecord(c->pin_ev[pi], s));
+
+    // ---- device work ----
+    rc = timed(c, "halo_fill", B, s,
+               [&] { return launch_halo_fill(c->halo, c->state, m, B, s); });
+    if (rc)
+        return rc;
+    rc = timed(c, "rvq_gather", F, s, [&] {
+        return launch_rvq_gather(c->cb, c->cb_dtype, m.codes, F, g.K, g.E, g.d_cb, c->z, c->dtype,
+                                 s);
+    });
+    if (rc)
+        return rc;
+
+    ConvArgs a = conv_args(c, c->proj, c->z, 0, 1, F, m);
+    a.out16 = c->u_ext;
+    a.out_H = 6;
+    if ((rc = run_conv(c, "proj", a, s)))
+        return rc;
+
+    a = conv_args(c, c->in_conv, c->u_ext, 6, 1, F, m);
+    a.out16 = c->aT[0];
+    a.out_H = 1;
+    set_act(c, a, c->a_stage[0]);
+    if ((rc = run_conv(c, "in_conv", a, s)))
+        return rc;
+
+    char nm[64];
+    for (int i = 0; i < c->S; i++) {
+        int ri = c->rate[i], ro = c->rate[i + 1];
+        a = conv_args(c, c->convT[i], c->aT[i], 1, ri, F * ri, m);
+        a.out32 = c->x;
+        a.out16 = c->a1[i];
+        a.out_H = 6;
+        set_act(c, a, c->a_ru1[i][0]);
+        snprintf(nm, sizeof nm, "s%d.convT", i);
+        if ((rc = run_conv(c, nm, a, s)))
+            return rc;
+        for (int j = 0; j < 2; j++) {
+            void *in = j == 0 ? c->a1[i] : c->a2[i];
+            int inH = 6 * RU_DIL[j];
+            a = conv_args(c, c->conv7[i][j], in, inH, ro, F * ro, m);
+            a.out16 = c->h;
+            a.out_H = 0;
+            set_act(c, a, c->a_ru2[i][j]);
+            snprintf(nm, sizeof nm, "s%d.ru%d.conv7", i, j);
+            if ((rc = run_conv(c, nm, a, s)))
+                return rc;
+            a = conv_args(c, c->conv1[i][j], c->h, 0, ro, F * ro, m);
+            a.res = c->x;
+            if (j == 0) {
+                a.out32 = c->x;  // in place: each element is read then written by one thread
+                a.out16 = c->a2[i];
+                a.out_H = 18;
+                set_act(c, a, c->a_ru1[i][1]);
+            } else if (i + 1 < c->S) {
+                a.out16 = c->aT[i + 1];
+                a.out_H = 1;
+                set_act(c, a, c->a_stage[i + 1]);
+            } else {
+                a.out16 = c->a_outb;
+                a.out_H = 6;
+                set_act(c, a, c->a_out);
+            }
+            snprintf(nm, sizeof nm, "s%d.ru%d.conv1", i, j);
+            if ((rc = run_conv(c, nm, a, s)))
+                return rc;
+        }
+    }
+    rc = timed(c, "final_conv", (int64_t)F * c->hop, s, [&] {
+        return launch_final_conv(c->a_outb, c->dtype, 6, c->ch[c->S], c->hop, c->out_w, c->out_b,
+                                 g.final_tanh, m.frame_stream, F * c->hop, pcm, s);
+    });
+    if (rc)
+        return rc;
+    rc = timed(c, "halo_save", B, s,
+               [&] { return launch_halo_save(c->halo, c->state, m, B, s); });
+    if (rc)
+        return rc;
+
+    for (int b = 0; b < B; b++) {
+        c->slot_pos[slots[b]] += n[b];
+        c->slot_fresh[slots[b]] = 0;
+    }
+    c->last_meta = m;
+    c->lastF = F;
+    c->lastB = B;
+    return CODEC_OK;
+}
+
+int check_cfg(const codec_cfg *g, int *ch, int *hop)
+{
+    if (g->K < 1 || g->K > 64 || g->E < 1 || g->d_cb < 1 || g->d_lat < 1)
+        return set_err(nullptr, CODEC_EINVAL, "cfg: K=%d (1..64), E=%d, d_cb=%d, d_lat=%d", g->K,
+                       g->E, g->d_cb, g->d_lat);
+    if (g->n_stages < 1 || g->n_stages > CODEC_MAX_STAGES)
+        return set_err(nullptr, CODEC_EINVAL, "cfg: n_stages=%d (1..%d)", g->n_stages,
+                       CODEC_MAX_STAGES);
+    if (g->act != CODEC_ACT_SNAKE && g->act != CODEC_ACT_ELU)
+        return set_err(nullptr, CODEC_EINVAL, "cfg: act=%d", g->act);
+    if (g->weight_dtype != CODEC_DTYPE_F32 && g->weight_dtype != CODEC_DTYPE_BF16)
+        return set_err(nullptr, CODEC_EINVAL, "cfg: weight_dtype=%d (F32 or BF16)",
+                       g->weight_dtype);
+    if (g->max_streams < 1 || g->max_frames_per_call < 1)
+        return set_err(nullptr, CODEC_EINVAL, "cfg: max_streams=%d, max_frames_per_call=%d",
+                       g->max_streams, g->max_frames_per_call);
+    if (g->tf_layers != 0)
+        return set_err(nullptr, CODEC_EINVAL,
+                       "cfg: tf_layers=%d: the windowed transformer is not in this build",
+                       g->tf_layers);
+    int gran = g->weight_dtype == CODEC_DTYPE_BF16 ? 32 : 16;
+    ch[0] = g->d_lat;
+    *hop = 1;
+    for (int i = 0; i < g->n_stages; i++) {
+        if (g->strides[i] < 1 || g->strides[i] > 64)
+            return set_err(nullptr, CODEC_EINVAL, "cfg: strides[%d]=%d", i, g->strides[i]);
+        if (ch[i] % 2)
+            return set_err(nullptr, CODEC_EINVAL, "cfg: channel width %d of stage %d is odd",
+                           ch[i], i);
+        ch[i + 1] = ch[i] / 2;
+        *hop *= g->strides[i];
+    }
+    for (int i = 0; i <= g->n_stages; i++)
+        if (ch[i] % gran)
+            return set_err(nullptr, CODEC_EINVAL,
+                           "cfg: channel width %d is not a multiple of %d (the MFMA K step of "
+                           "this weight dtype)",
+                           ch[i], gran);
+    if (g->d_cb % gran)
+        return set_err(nullptr, CODEC_EINVAL, "cfg: d_cb=%d is not a multiple of %d", g->d_cb,
+                       gran);
+    if ((int64_t)g->max_frames_per_call * *hop >= (int64_t)1 << 31)
+        return set_err(nullptr, CODEC_EINVAL, "cfg: max_frames_per_call * hop overflows int32");
+    return CODEC_OK;
+}
+
+}  // namespace
+
+// ============================================================================
+extern "C" {
+
+const char *codec_last_error(const codec_t *c)
+{
+    if (c)
+        return c->err.c_str();
+    return g_err.c_str();
+}
+
+int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *cfg,
+               codec_t **out)
+{
+    if (!out)
+        return set_err(nullptr, CODEC_EINVAL, "codec_open: out is NULL");
+    *out = nullptr;
+    if (!cfg || (!weights && n_weights > 0) || n_weights < 0)
+        return set_err(nullptr, CODEC_EINVAL, "codec_open: null cfg or weights");
+    int ch[CODEC_MAX_STAGES + 1];
+    int hop = 1;
+    int rc = check_cfg(cfg, ch, &hop);
+    if (rc)
+        return rc;
+
+    // ---- weight manifest: every canonical parameter exactly once ----
+    std::vector<ParamSpec> specs = param_specs(*cfg, ch);
+    std::unordered_map<std::string, int> by_name;
+    for (int i = 0; i < n_weights; i++) {
+        const codec_tensor &t = weights[i];
+        if (!t.name || !t.host_data)
+            return set_err(nullptr, CODEC_EINVAL, "weights[%d]: null name or data", i);
+        if (by_name.count(t.name))
+            return set_err(nullptr, CODEC_EINVAL, "weights: '%s' given twice", t.name);
+        by_name[t.name] = i;
+    }
+    for (const ParamSpec &p : specs) {
+        auto it = by_name.find(p.name);
+        if (it == by_name.end())
+            return set_err(nullptr, CODEC_EINVAL, "weights: '%s' missing", p.name.c_str());
+        const codec_tensor &t = weights[it->second];
+        bool ok = t.ndim == (int)p.shape.size();
+        for (int d = 0; ok && d < t.ndim; d++)
+            ok = t.shape[d] == p.shape[d];
+        if (!ok) {
+            std::string want, got;
+            for (auto v : p.shape)
+                want += std::to_string(v) + ",";
+            for (int d = 0; d < t.ndim && d < 4; d++)
+                got += std::to_string(t.shape[d]) + ",";
+            return set_err(nullptr, CODEC_EINVAL, "weights: '%s' has shape (%s), expected (%s)",
+                           p.name.c_str(), got.c_str(), want.c_str());
+        }
+        if (t.dtype != cfg->weight_dtype)
+            return set_err(nullptr, CODEC_EINVAL, "weights: '%s' dtype %d, cfg weight_dtype %d",
+                           p.name.c_str(), t.dtype, cfg->weight_dtype);
+    }
+    if ((size_t)n_weights != specs.size()) {
+        std::unordered_set<std::string> known;
+        for (auto &p : specs)
+            known.insert(p.name);
+        for (int i = 0; i < n_weights; i++)
+            if (!known.count(weights[i].name))
+                return set_err(nullptr, CODEC_EINVAL, "weights: unknown parameter '%s'",
+                               weights[i].name);
+    }
+
+    int dev = 0;
+    int ndev = 0;
+    hipError_t he = hipGetDeviceCount(&ndev);
+    if (he != hipSuccess || ndev < 1)
+        return set_err(nullptr, CODEC_EHIP, "codec_open: no HIP device (%s)",
+                       hipGetErrorString(he));
+    he = hipGetDevice(&dev);
+    if (he != hipSuccess)
+        return set_err(nullptr, CODEC_EHIP, "codec_open: hipGetDevice: %s",
+                       hipGetErrorString(he));
+
+    codec *c = new codec();
+    c->cfg = *cfg;
+    c->dev = dev;
+    c->dtype = cfg->weight_dtype == CODEC_DTYPE_BF16 ? 1 : 0;
+    c->esz = c->dtype ? 2 : 4;
+    c->S = cfg->n_stages;
+    c->hop = hop;
+    memcpy(c->ch, ch, sizeof ch);
+    c->rate[0] = 1;
+    for (int i = 0; i < c->S; i++)
+        c->rate[i + 1] = c->rate[i] * cfg->strides[i];
+    c->left_ctx = left_context_frames(*cfg, hop);
+    c->maxF = cfg->max_frames_per_call;
+    c->maxB = cfg->max_streams;
+
+    auto W = [&](const std::string &name) {
+        const codec_tensor &t = weights[by_name[name]];
+        int64_t n = 1;
+        for (int d = 0; d < t.ndim; d++)
+            n *= t.shape[d];
+        return host_f32(t, n);
+    };
+    auto cleanup_fail = [&](int code) {
+        std::string msg = c->err;
+        codec_close(c);
+        g_err = msg;
+        return code;
+    };
+    char nm[128];
+    const codec_cfg &g = *cfg;
+
+    // ---- codebooks: one contiguous [K][E][d_cb] array in the given dtype ----
+    {
+        size_t per = (size_t)g.E * g.d_cb;
+        c->cb_dtype = c->dtype;  // bf16 tables for the fp16 path, fp32 tables otherwise
+        size_t esz = c->cb_dtype ? 2 : 4;
+        if ((rc = dev_alloc(c, &c->cb, per * g.K * esz, &c->weight_bytes)))
+            return cleanup_fail(rc);
+        for (int k = 0; k < g.K; k++) {
+            snprintf(nm, sizeof nm, "rvq.codebook.%d", k);
+            const codec_tensor &t = weights[by_name[nm]];
+            hipError_t e = hipMemcpy((char *)c->cb + per * esz * k, t.host_data, per * esz,
+                                     hipMemcpyHostToDevice);
+            if (e != hipSuccess) {
+                fail(c, CODEC_EHIP, "codebook upload: %s", hipGetErrorString(e));
+                return cleanup_fail(CODEC_EHIP);
+            }
+        }
+    }
+    // ---- dense layers, repacked K-major for the implicit GEMM ----
+    if ((rc = make_lin(c, W("rvq.proj.weight"), W("rvq.proj.bias"), g.d_lat, g.d_lat, g.d_cb, 1,
+                       1, 1, &c->proj)))
+        return cleanup_fail(rc);
+    if ((rc = make_lin(c, pack_conv(W("dec.in_conv.weight"), ch[0], g.d_lat, 7),
+                       W("dec.in_conv.bias"), ch[0], ch[0], g.d_lat, 7, 1, 1, &c->in_conv)))
+        return cleanup_fail(rc);
+    for (int i = 0; i < c->S; i++) {
+        int ci = ch[i], co = ch[i + 1], s = g.strides[i];
+        snprintf(nm, sizeof nm, "dec.stage.%d.snake.alpha", i);
+        if ((rc = upload_act(c, W(nm), &c->a_stage[i])))
+            return cleanup_fail(rc);
+        snprintf(nm, sizeof nm, "dec.stage.%d.convT.weight", i);
+        std::vector<float> wt = pack_convT(W(nm), ci, co, s);
+        snprintf(nm, sizeof nm, "dec.stage.%d.convT.bias", i);
+        if ((rc = make_lin(c, wt, W(nm), s * co, co, ci, 2, 1, s, &c->convT[i])))
+            return cleanup_fail(rc);
+        for (int j = 0; j < 2; j++) {
+            std::string p = "dec.stage." + std::to_string(i) + ".ru." + std::to_string(j) + ".";
+            if ((rc = upload_act(c, W(p + "snake1.alpha"), &c->a_ru1[i][j])))
+                return cleanup_fail(rc);
+            if ((rc = upload_act(c, W(p + "snake2.alpha"), &c->a_ru2[i][j])))
+                return cleanup_fail(rc);
+            if ((rc = make_lin(c, pack_conv(W(p + "conv7.weight"), co, co, 7), W(p + "conv7.bias"),
+                               co, co, co, 7, RU_DIL[j], 1, &c->conv7[i][j])))
+                return cleanup_fail(rc);
+            if ((rc = make_lin(c, W(p + "conv1.weight"), W(p + "conv1.bias"), co, co, co, 1, 1, 1,
+                               &c->conv1[i][j])))
+                return cleanup_fail(rc);
+        }
+    }
+    if ((rc = upload_act(c, W("dec.out.snake.alpha"), &c->a_out)))
+        return cleanup_fail(rc);
+    if ((rc = upload_f32(c, W("dec.out.conv.weight"), &c->out_w)))
+        return cleanup_fail(rc);
+    c->out_b = W("dec.out.conv.bias")[0];
+
+    // ---- workspace for max_frames_per_call frames of max_streams streams ----
+    const size_t F = (size_t)c->maxF, B = (size_t)c->maxB, es = (size_t)c->esz;
+    int64_t *ws = &c->workspace_bytes;
+    if ((rc = dev_alloc(c, &c->z, F * g.d_cb * es, ws)))
+        return cleanup_fail(rc);
+    if ((rc = dev_alloc(c, &c->u_ext, (B * 6 + F) * g.d_lat * es, ws)))
+        return cleanup_fail(rc);
+    size_t hmax = 0;
+    for (int i = 0; i < c->S; i++) {
+        size_t ro = (size_t)c->rate[i + 1], co = (size_t)ch[i + 1];
+        if ((rc = dev_alloc(c, &c->aT[i], (B * 1 + F * c->rate[i]) * ch[i] * es, ws)))
+            return cleanup_fail(rc);
+        if ((rc = dev_alloc(c, &c->a1[i], (B * 6 + F * ro) * co * es, ws)))
+            return cleanup_fail(rc);
+        if ((rc = dev_alloc(c, &c->a2[i], (B * 18 + F * ro) * co * es, ws)))
+            return cleanup_fail(rc);
+        hmax = std::max(hmax, F * ro * co);
+    }
+    if ((rc = dev_alloc(c, &c->h, hmax * es, ws)))
+        return cleanup_fail(rc);
+    if ((rc = dev_alloc(c, (void **)&c->x, hmax * 4, ws)))
+        return cleanup_fail(rc);
+    if ((rc = dev_alloc(c, &c->a_outb, (B * 6 + F * hop) * ch[c->S] * es, ws)))
+        return cleanup_fail(rc);
+    if ((rc = dev_alloc(c, (void **)&c->pcm_scratch, F * hop * 4, ws)))
+        return cleanup_fail(rc);
+
+    // ---- halo table and state slots ----
+    HaloTable &t = c->halo;
+    t.elem_bytes = c->esz;
+    int64_t off = 0;
+    auto add = [&](void *ext, int H, int C, int rate) {
+        HaloLayer &L = t.l[t.n++];
+        L.ext = ext;
+        L.H = H;
+        L.C = C;
+        L.rate = rate;
+        L.state_off = off;
+        off += (int64_t)H * C;
+    };
+    add(c->u_ext, 6, g.d_lat, 1);
+    for (int i = 0; i < c->S; i++) {
+        add(c->aT[i], 1, ch[i], c->rate[i]);
+        add(c->a1[i], 6, ch[i + 1], c->rate[i + 1]);
+        add(c->a2[i], 18, ch[i + 1], c->rate[i + 1]);
+    }
+    add(c->a_outb, 6, ch[c->S], hop);
+    c->slot_elems = off;
+    t.slot_elems = off;
+    if ((rc = dev_alloc(c, &c->state, (size_t)c->maxB * off * es, ws)))
+        return cleanup_fail(rc);
+
+    // ---- step metadata: device buffer + two pinned staging buffers ----
+    c->meta_cap = round4(F * g.K) + round4(F) + round4(B + 1) + 3 * round4(B) + 4;
+    if ((rc = dev_alloc(c, &c->meta_dev, c->meta_cap * 4, ws)))
+        return cleanup_fail(rc);
+    for (int i = 0; i < 2; i++) {
+        hipError_t e = hipHostMalloc(&c->pinned[i], c->meta_cap * 4, hipHostMallocDefault);
+        if (e != hipSuccess) {
+            c->pinned[i] = nullptr;
+            fail(c, CODEC_ENOMEM, "hipHostMalloc: %s", hipGetErrorString(e));
+            return cleanup_fail(CODEC_ENOMEM);
+        }
+        e = hipEventCreateWithFlags(&c->pin_ev[i], hipEventDisableTiming);
+        if (e != hipSuccess) {
+            fail(c, CODEC_EHIP, "hipEventCreate: %s", hipGetErrorString(e));
+            return cleanup_fail(CODEC_EHIP);
+        }
+    }
+
+    c->slot_pos.assign(c->maxB, 0);
+    c->slot_fresh.assign(c->maxB, 1);
+    for (int i = c->maxB - 1; i >= 0; i--)
+        c->free_slots.push_back(i);
+    *out = c;
+    return CODEC_OK;
+}
+
+int codec_close(codec_t *c)
+{
+    if (!c)
+        return set_err(nullptr, CODEC_EINVAL, "codec_close: NULL codec");
+    hipDeviceSynchronize();
+    for (auto &r : c->recs) {
+        hipEventDestroy(r.a);
+        hipEventDestroy(r.b);
+    }
+    for (auto e : c->ev_pool)
+        hipEventDestroy(e);
+    for (int i = 0; i < 2; i++) {
+        if (c->pin_ev[i])
+            hipEventDestroy(c->pin_ev[i]);
+        if (c->pinned[i])
+            hipHostFree(c->pinned[i]);
+    }
+    for (void *p : c->allocs)
+        hipFree(p);
+    delete c;
+    return CODEC_OK;
+}
+
+int codec_info(const codec_t *c, codec_info_t *o)
+{
+    if (!c || !o)
+        return set_err(nullptr, CODEC_EINVAL, "codec_info: NULL argument");
+    memset(o, 0, sizeof *o);
+    o->hop = c->hop;
+    o->sample_rate = c->cfg.sample_rate;
+    o->K = c->cfg.K;
+    o->E = c->cfg.E;
+    o->left_context_frames = c->left_ctx;
+    o->max_streams = c->maxB;
+    o->max_frames_per_call = c->maxF;
+    o->open_streams = (int32_t)c->id2slot.size();
+    o->compute_dtype = c->dtype ? CODEC_DTYPE_F16 : CODEC_DTYPE_F32;
+    o->state_bytes_per_stream = c->slot_elems * c->esz;
+    o->weight_bytes = c->weight_bytes;
+    o->workspace_bytes = c->workspace_bytes;
+    return CODEC_OK;
+}
+
+int stream_open(codec_t *c, int32_t *id_out)
+{
+    if (!c || !id_out)
+        return set_err(c ? &c->err : nullptr, CODEC_EINVAL, "stream_open: NULL argument");
+    if (c->free_slots.empty())
+        return fail(c, CODEC_ENOSLOT, "stream_open: all %d state slots are in use", c->maxB);
+    if (c->next_id == INT32_MAX)
+        return fail(c, CODEC_ENOSLOT, "stream_open: stream ids exhausted");
+    int slot = c->free_slots.back();
+    c->free_slots.pop_back();
+    int32_t id = c->next_id++;
+    c->id2slot[id] = slot;
+    c->slot_pos[slot] = 0;
+    c->slot_fresh[slot] = 1;
+    *id_out = id;
+    return CODEC_OK;
+}
+
+int stream_close(codec_t *c, int32_t id)
+{
+    if (!c)
+        return set_err(nullptr, CODEC_EINVAL, "stream_close: NULL codec");
+    auto it = c->id2slot.find(id);
+    if (it == c->id2slot.end())
+        return fail(c, CODEC_ESTREAM, "stream_close: stream %d is not open", id);
+    c->free_slots.push_back(it->second);
+    c->id2slot.erase(it);
+    return CODEC_OK;
+}
+
+static int check_codes(codec *c, const int32_t *codes, int64_t F, const int32_t *ids,
+                       const int32_t *n, int B)
+{
+    const int K = c->cfg.K, E = c->cfg.E;
+    for (int64_t i = 0; i < F * K; i++) {
+        uint32_t v = (uint32_t)codes[i];
+        if (v >= (uint32_t)E) {
+            int64_t f = i / K;
+            int b = 0;
+            int64_t acc = 0;
+            while (b < B && acc + n[b] <= f)
+                acc += n[b++];
+            return fail(c, CODEC_ERANGE,
+                        "code %d at stream %d frame %lld codebook %lld is outside [0, %d)",
+                        codes[i], ids ? ids[b] : -1, (long long)(f - acc),
+                        (long long)(i % K), E);
+        }
+    }
+    return CODEC_OK;
+}
+
+int decode_chunk(codec_t *c, int32_t B, const int32_t *ids, const int32_t *n, const int32_t *codes,
+                 float *pcm, int64_t pcm_capacity, codec_hip_stream stream)
+{
+    if (!c)
+        return set_err(nullptr, CODEC_EINVAL, "decode_chunk: NULL codec");
+    if (B < 1 || !ids || !n || !codes || !pcm)
+        return fail(c, CODEC_EINVAL,
+                    "decode_chunk: B=%d (must be >= 1) and ids, n_frames, codes, pcm non-NULL", B);
+    if (B > c->maxB)
+        return fail(c, CODEC_ETOOBIG, "decode_chunk: B=%d exceeds max_streams=%d", B, c->maxB);
+    int64_t F = 0;
+    for (int b = 0; b < B; b++) {
+        if (n[b] < 1)
+            return fail(c, CODEC_EINVAL, "decode_chunk: n_frames[%d]=%d (must be >= 1)", b, n[b]);
+        F += n[b];
+    }
+    std::vector<int> slots((size_t)B);
+    std::unordered_set<int32_t> seen;
+    for (int b = 0; b < B; b++) {
+        auto it = c->id2slot.find(ids[b]);
+        if (it == c->id2slot.end())
+            return fail(c, CODEC_ESTREAM, "decode_chunk: stream %d (index %d) is not open", ids[b],
+                        b);
+        if (!seen.insert(ids[b]).second)
+            return fail(c, CODEC_EDUP, "decode_chunk: stream %d appears twice", ids[b]);
+        slots[b] = it->second;
+    }
+    if (F > c->maxF)
+        return fail(c, CODEC_ETOOBIG,
+                    "decode_chunk: %lld frames in one call exceed max_frames_per_call=%d",
+                    (long long)F, c->maxF);
+    if (pcm_capacity < F * c->hop)
+        return fail(c, CODEC_EINVAL, "decode_chunk: pcm capacity %lld < %lld samples",
+                    (long long)pcm_capacity, (long long)(F * c->hop));
+    int rc = check_codes(c, codes, F, ids, n, B);
+    if (rc)
+        return rc;
+    HIPCHK(c, hipSetDevice(c->dev));
+    return enqueue_step(c, B, slots.data(), n, codes, pcm, (hipStream_t)stream);
+}
+
+int stream_prefill(codec_t *c, int32_t id, const int32_t *codes, int32_t n,
+                   codec_hip_stream stream)
+{
+    if (!c)
+        return set_err(nullptr, CODEC_EINVAL, "stream_prefill: NULL codec");
+    if (n < 0 || (n > 0 && !codes))
+        return fail(c, CODEC_EINVAL, "stream_prefill: n=%d, codes=%p", n, (const void *)codes);
+    auto it = c->id2slot.find(id);
+    if (it == c->id2slot.end())
+        return fail(c, CODEC_ESTREAM, "stream_prefill: stream %d is not open", id);
+    int rc = check_codes(c, codes, n, &id, &n, 1);
+    if (rc)
+        return rc;
+    HIPCHK(c, hipSetDevice(c->dev));
+    int slot = it->second;
+    for (int32_t at = 0; at < n;) {
+        int32_t piece = std::min<int32_t>(n - at, c->maxF);
+        rc = enqueue_step(c, 1, &slot, &piece, codes + (size_t)at * c->cfg.K, c->pcm_scratch,
+                          (hipStream_t)stream);
+        if (rc)
+            return rc;
+        at += piece;
+    }
+    return CODEC_OK;
+}
+
+int codec_debug_capture(codec_t *c, int32_t what, float *dst, int64_t capacity,
+                        codec_hip_stream stream)
+{
+    if (!c || !dst)
+        return set_err(c ? &c->err : nullptr, CODEC_EINVAL, "codec_debug_capture: NULL argument");
+    if (what != CODEC_CAPTURE_LATENT && what != CODEC_CAPTURE_DEC_INPUT)
+        return fail(c, CODEC_EINVAL, "codec_debug_capture: what=%d", what);
+    if (c->lastF == 0)
+        return fail(c, CODEC_EINVAL, "codec_debug_capture: no decode step yet");
+    int64_t need = (int64_t)c->lastF * c->cfg.d_lat;
+    if (capacity < need)
+        return fail(c, CODEC_EINVAL, "codec_debug_capture: capacity %lld < %lld",
+                    (long long)capacity, (long long)need);
+    HIPCHK(c, hipSetDevice(c->dev));
+    HIPCHK(c, launch_unextend(c->u_ext, c->dtype, 6, c->cfg.d_lat, 1, c->last_meta.frame_stream,
+                              c->lastF, dst, (hipStream_t)stream));
+    return CODEC_OK;
+}
+
+int codec_profile_enable(codec_t *c, int32_t on)
+{
+    if (!c)
+        return set_err(nullptr, CODEC_EINVAL, "codec_profile_enable: NULL codec");
+    c->prof = on != 0;
+    return CODEC_OK;
+}
+
+int codec_profile_read(codec_t *c, int32_t cap, const char **names, double *ms, int64_t *launches,
+                       int64_t *units, int32_t *n_out)
+{
+    if (!c || !n_out)
+        return set_err(c ? &c->err : nullptr, CODEC_EINVAL, "codec_profile_read: NULL argument");
+    for (auto &r : c->recs) {
+        HIPCHK(c, hipEventSynchronize(r.b));
+        float t = 0.f;
+        HIPCHK(c, hipEventElapsedTime(&t, r.a, r.b));
+        c->cls_ms[r.cls] += t;
+        c->cls_launches[r.cls] += 1;
+        c->cls_units[r.cls] += r.units;
+        c->ev_pool.push_back(r.a);
+        c->ev_pool.push_back(r.b);
+    }
+    c->recs.clear();
+    int n = (int)c->cls_names.size();
+    for (int i = 0; i < n && i < cap; i++) {
+        if (names)
+            names[i] = c->cls_names[i].c_str();
+        if (ms)
+            ms[i] = c->cls_ms[i];
+        if (launches)
+            launches[i] = c->cls_launches[i];
+        if (units)
+            units[i] = c->cls_units[i];
+    }
+    *n_out = n;
+    // reset the accumulators for the next window (names stay valid)
+    std::fill(c->cls_ms.begin(), c->cls_ms.end(), 0.0);
+    std::fill(c->cls_launches.begin(), c->cls_launches.end(), 0);
+    std::fill(c->cls_units.begin(), c->cls_units.end(), 0);
+    return CODEC_OK;
+}
+
+int codec_chunk_plan(int32_t total, const int32_t *ramp, int32_t n_ramp, int32_t steady,
+                     int32_t initial, int32_t *out, int32_t cap, int32_t *n_out)
+{
+    if (total < 0 || steady <= 0 || n_ramp < 0 || (n_ramp > 0 && !ramp) || !n_out ||
+        (cap > 0 && !out))
+        return set_err(nullptr, CODEC_EINVAL,
+                       "codec_chunk_plan: total=%d steady=%d n_ramp=%d", total, steady, n_ramp);
+    for (int i = 0; i < n_ramp; i++)
+        if (ramp[i] <= 0)
+            return set_err(nullptr, CODEC_EINVAL, "codec_chunk_plan: ramp[%d]=%d", i, ramp[i]);
+    // stride sequence: initial (or ramp[0]), ramp[1..], then steady; each <= steady
+    auto stride = [&](int i) -> int32_t {
+        int32_t v;
+        if (i == 0)
+            v = initial > 0 ? initial : (n_ramp > 0 ? ramp[0] : steady);
+        else if (i < n_ramp)
+            v = ramp[i];
+        else
+            v = steady;
+        return std::min(v, steady);
+    };
+    int cnt = 0, si = 0;
+    int64_t threshold = stride(si++), done = 0;
+    for (int64_t g = 1; g <= total; g++) {
+        if (g >= threshold) {
+            if (cnt < cap)
+                out[cnt] = (int32_t)(g - done);
+            cnt++;
+            done = g;
+            threshold = g + stride(si++);
+        }
+    }
+    if (done < total) {
+        if (cnt < cap)
+            out[cnt] = (int32_t)(total - done);
+        cnt++;
+    }
+    *n_out = cnt;
+    if (cnt > cap)
+        return set_err(nullptr, CODEC_EINVAL, "codec_chunk_plan: %d decodes exceed cap %d", cnt,
+                       cap);
+    return CODEC_OK;
+}
+
+int codec_resolve_initial_chunk_frames(int64_t value, int32_t has_value, int32_t steady,
+                                       int32_t default_frames, int32_t *out)
+{
+    if (!out)
+        return set_err(nullptr, CODEC_EINVAL, "codec_resolve_initial_chunk_frames: NULL out");
+    if (steady <= 0)
+        return set_err(nullptr, CODEC_EINVAL, "steady_chunk_frames must be positive, got %d",
+                       steady);
+    int64_t v = has_value ? value : default_frames;
+    if (v < 0)
+        return set_err(nullptr, CODEC_EINVAL, "initial chunk frames must be >= 0, got %lld",
+                       (long long)v);
+    *out = (int32_t)std::min<int64_t>(v, steady);
+    return CODEC_OK;
+}
+
+}  // extern "C"

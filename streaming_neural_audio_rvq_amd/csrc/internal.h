@@ -1,0 +1,95 @@
+// internal.h -- declarations shared by the library's host code and kernels.
+//
+// Activation layout.  Every activation is channels-last (one row per sample,
+// C contiguous values).  Rows of all streams in a step are packed stream
+// after stream ("packed rows"); at a layer running at r rows per frame,
+// stream b owns packed rows [cu[b] r, cu[b+1] r).  A conv input buffer that
+// needs left context is "extended": each stream's rows are preceded by H
+// halo rows, so packed row m of stream b sits at extended row (b+1) H + m,
+// and its halo rows are b H + cu[b] r .. + H.  The halo is filled from the
+// stream's state slot before the step and the last H rows of every stream's
+// extended segment are saved back after it, which also handles n r < H.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace snrvq {
+
+typedef _Float16 half_t;
+
+enum Act : int { ACT_NONE = 0, ACT_SNAKE = 1, ACT_ELU = 2, ACT_GELU = 3 };
+
+// One implicit-GEMM convolution (also transposed conv in polyphase form,
+// and plain GEMMs as k = 1 convs).
+//   out[m, n] = bias[n % Cout] + sum_{tap, c} A_ext[row(m) - (taps-1-tap) dil, c] * Wt[n, tap Cin + c]
+// where row(m) is the extended row of packed input row m.  For a transposed
+// conv of stride s the output row of (m, n) is m s + n / Cout, channel n % Cout.
+struct ConvArgs {
+    const void *A;          // input, compute type, extended with A_H halo rows per stream
+    const void *Wt;         // packed weights [N][taps Cin], compute type
+    const float *bias;      // [Cout]
+    const int32_t *frame_stream;  // [F] batch index of each packed frame
+    const float *res;       // fp32 residual [M][Cout] (s == 1) or null
+    float *out32;           // fp32 output [M s][Cout] or null
+    void *out16;            // compute-type output, extended with out_H halo rows, or null
+    const float *alpha;     // [Cout] activation parameter for out16
+    const float *inv_alpha; // [Cout]
+    int M;                  // packed input rows = F * rate_in
+    int A_H, Cin, taps, dil, rate_in;
+    int N, Cout, s;
+    int out_H, act;
+    int out_ld;             // row width of out16 / out32 (== Cout)
+};
+
+// Halo layers: fill before a step, save after it.
+#define SNRVQ_MAX_HALO 24
+struct HaloLayer {
+    void *ext;        // extended buffer (compute type)
+    int64_t state_off;// element offset of this layer inside one slot
+    int H, C, rate, pad;
+};
+struct HaloTable {
+    HaloLayer l[SNRVQ_MAX_HALO];
+    int n;
+    int elem_bytes;
+    int64_t slot_elems;
+};
+
+// Per-step device metadata (one H2D copy).
+struct StepMeta {
+    int32_t *codes;        // [F][K]
+    int32_t *frame_stream; // [F]
+    int32_t *cu;           // [B+1]
+    int32_t *slot;         // [B]
+    int32_t *fresh;        // [B]
+    int32_t *pos;          // [B]
+};
+
+// ---- launchers (kernels_*.hip) ----
+// dtype: 0 = fp32 operands, 1 = fp16 operands
+hipError_t launch_conv_gemm(const ConvArgs &a, int dtype, hipStream_t st, int tile_hint);
+int conv_gemm_tile_choice(const ConvArgs &a, int dtype);
+const char *conv_gemm_tile_name(int dtype, int tile);
+
+hipError_t launch_halo_fill(const HaloTable &t, void *state, const StepMeta &m, int B,
+                            hipStream_t st);
+hipError_t launch_halo_save(const HaloTable &t, void *state, const StepMeta &m, int B,
+                            hipStream_t st);
+
+// z[f][:] = sum_k cb[k][codes[f][k]][:] (cb is one [K][E][d_cb] array),
+// written in the compute type.  cb_dtype: 0 fp32 tables, 1 bf16 tables.
+// out_dtype: 0 fp32, 1 fp16.
+hipError_t launch_rvq_gather(const void *cb, int cb_dtype, const int32_t *codes, int F, int K,
+                             int E, int d_cb, void *z, int out_dtype, hipStream_t st);
+
+// pcm[m] = b + sum_{j, c} w[c][j] A_ext[row(m) - (6 - j), c], m < M (k = 7, Cout = 1).
+hipError_t launch_final_conv(const void *A, int dtype, int A_H, int C, int rate,
+                             const float *w /*[C][7]*/, float b, int final_tanh,
+                             const int32_t *frame_stream, int M, float *pcm, hipStream_t st);
+
+// Copies packed rows out of an extended buffer as fp32 [M][C].
+hipError_t launch_unextend(const void *ext, int dtype, int H, int C, int rate,
+                           const int32_t *frame_stream, int M, float *dst, hipStream_t st);
+
+}  // namespace snrvq

@@ -1,0 +1,256 @@
+// kernels_misc.hip -- the non-GEMM kernels of a decode step:
+//   * halo fill / save: move each stream's left context between its state
+//     slot and the halo rows of every extended conv input (one launch each
+//     per step, all layers at once);
+//   * RVQ gather-and-sum of the codebook rows of every frame;
+//   * the final causal conv to one channel (an N = 1 reduction, VALU);
+//   * unextend: packed fp32 copy of an extended buffer (inspection only).
+#include "internal.h"
+
+namespace snrvq {
+namespace {
+
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+
+// blockIdx.x = batch index b, blockIdx.y = halo layer.  Copies the slot's H
+// rows into the halo of stream b (zeros for a fresh stream).
+__global__ __launch_bounds__(256) void halo_fill_kernel(HaloTable t, const char *state,
+                                                        const int32_t *cu, const int32_t *slot,
+                                                        const int32_t *fresh)
+{
+    const int b = blockIdx.x;
+    const HaloLayer L = t.l[blockIdx.y];
+    const long row_bytes = (long)L.C * t.elem_bytes;
+    const long bytes = (long)L.H * row_bytes;
+    char *dst = (char *)L.ext + ((long)b * L.H + (long)cu[b] * L.rate) * row_bytes;
+    const char *src = state + ((long)slot[b] * t.slot_elems + L.state_off) * t.elem_bytes;
+    const bool zero = fresh[b] != 0;
+    for (long i = (long)threadIdx.x * 16; i < bytes; i += 256 * 16) {
+        u4 v = zero ? u4{0u, 0u, 0u, 0u} : *(const u4 *)(src + i);
+        *(u4 *)(dst + i) = v;
+    }
+}
+
+// Saves the last H rows of stream b's extended segment (which start at
+// extended row b H + cu[b+1] rate) into its slot.
+__global__ __launch_bounds__(256) void halo_save_kernel(HaloTable t, char *state,
+                                                        const int32_t *cu, const int32_t *slot)
+{
+    const int b = blockIdx.x;
+    const HaloLayer L = t.l[blockIdx.y];
+    const long row_bytes = (long)L.C * t.elem_bytes;
+    const long bytes = (long)L.H * row_bytes;
+    const char *src = (const char *)L.ext + ((long)b * L.H + (long)cu[b + 1] * L.rate) * row_bytes;
+    char *dst = state + ((long)slot[b] * t.slot_elems + L.state_off) * t.elem_bytes;
+    for (long i = (long)threadIdx.x * 16; i < bytes; i += 256 * 16)
+        *(u4 *)(dst + i) = *(const u4 *)(src + i);
+}
+
+__device__ __forceinline__ void load8(const uint16_t *p, float *v)
+{
+    // bf16 -> fp32 is exact: the bits move to the top half
+    u4 w = *(const u4 *)p;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load8(const float *p, float *v)
+{
+    f4 a = *(const f4 *)p, b = *(const f4 *)(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        v[i] = a[i];
+        v[4 + i] = b[i];
+    }
+}
+__device__ __forceinline__ void store8(half_t *p, const float *v)
+{
+    h8 h;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        h[i] = (half_t)v[i];
+    *(h8 *)p = h;
+}
+__device__ __forceinline__ void store8(float *p, const float *v)
+{
+    *(f4 *)p = f4{v[0], v[1], v[2], v[3]};
+    *(f4 *)(p + 4) = f4{v[4], v[5], v[6], v[7]};
+}
+
+// One thread owns 8 consecutive latent values of one frame and sums the K
+// selected codebook rows in codebook order, in fp32.  The codebooks are one
+// contiguous [K][E][d_cb] array.
+template <typename CB, typename OUT>
+__global__ __launch_bounds__(256) void rvq_gather_kernel(const CB *cb, const int32_t *codes,
+                                                         int F, int K, int E, int d_cb, OUT *z)
+{
+    const int per_frame = d_cb / 8;
+    long g = (long)blockIdx.x * 256 + threadIdx.x;
+    long f = g / per_frame;
+    if (f >= F)
+        return;
+    int d = (int)(g - f * per_frame) * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const int32_t *cf = codes + f * K;
+    for (int k = 0; k < K; k++) {
+        int e = cf[k];
+        float v[8];
+        load8(cb + ((long)k * E + e) * d_cb + d, v);
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            acc[i] += v[i];
+    }
+    store8(z + f * d_cb + d, acc);
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack(const T *p, int n, float *v);
+template <>
+__device__ __forceinline__ void unpack<half_t>(const half_t *p, int n, float *v)
+{
+    h8 h = *(const h8 *)p;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        v[i] = (float)h[i];
+}
+template <>
+__device__ __forceinline__ void unpack<float>(const float *p, int n, float *v)
+{
+    f4 a = *(const f4 *)p;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        v[i] = a[i];
+}
+
+// pcm[m] = b + sum_j sum_c w[j][c] A[row(m) - (6 - j)][c]; one thread per
+// output sample, fp32 accumulation, taps then channels ascending.
+template <typename T>
+__global__ __launch_bounds__(256) void final_conv_kernel(const T *A, int A_H, int C, int rate,
+                                                         const float *w, float bias, int tanh_out,
+                                                         const int32_t *frame_stream, int M,
+                                                         float *pcm)
+{
+    extern __shared__ float wsh[];  // [7][C]
+    for (int i = threadIdx.x; i < 7 * C; i += blockDim.x) {
+        int c = i / 7, j = i - c * 7;  // input layout [C][7]
+        wsh[j * C + c] = w[i];
+    }
+    __syncthreads();
+    long m = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (m >= M)
+        return;
+    int b = frame_stream[m / rate];
+    long ext = (long)(b + 1) * A_H + m;
+    constexpr int VEC = 16 / (int)sizeof(T);
+    float acc = bias;
+    for (int j = 0; j < 7; j++) {
+        const T *row = A + (ext - (6 - j)) * C;
+        const float *wj = wsh + j * C;
+        for (int c = 0; c < C; c += VEC) {
+            float v[8];
+            unpack<T>(row + c, VEC, v);
+#pragma unroll
+            for (int e = 0; e < VEC; e++)
+                acc += wj[c + e] * v[e];
+        }
+    }
+    pcm[m] = tanh_out ? tanhf(acc) : acc;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void unextend_kernel(const T *ext, int H, int C, int rate,
+                                                       const int32_t *frame_stream, int M,
+                                                       float *dst)
+{
+    long g = (long)blockIdx.x * 256 + threadIdx.x;
+    long total = (long)M * C;
+    if (g >= total)
+        return;
+    long m = g / C;
+    int c = (int)(g - m * C);
+    int b = frame_stream[m / rate];
+    dst[g] = (float)ext[((long)(b + 1) * H + m) * C + c];
+}
+
+}  // namespace
+
+hipError_t launch_halo_fill(const HaloTable &t, void *state, const StepMeta &m, int B,
+                            hipStream_t st)
+{
+    if (t.n == 0 || B == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(halo_fill_kernel, dim3(B, t.n), dim3(256), 0, st, t,
+                       (const char *)state, m.cu, m.slot, m.fresh);
+    return hipGetLastError();
+}
+
+hipError_t launch_halo_save(const HaloTable &t, void *state, const StepMeta &m, int B,
+                            hipStream_t st)
+{
+    if (t.n == 0 || B == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(halo_save_kernel, dim3(B, t.n), dim3(256), 0, st, t, (char *)state, m.cu,
+                       m.slot);
+    return hipGetLastError();
+}
+
+hipError_t launch_rvq_gather(const void *cb, int cb_dtype, const int32_t *codes, int F, int K,
+                             int E, int d_cb, void *z, int out_dtype, hipStream_t st)
+{
+    if (F <= 0)
+        return hipSuccess;
+    long threads = (long)F * (d_cb / 8);
+    dim3 grid((unsigned)((threads + 255) / 256));
+    if (cb_dtype == 1 && out_dtype == 1)
+        hipLaunchKernelGGL((rvq_gather_kernel<uint16_t, half_t>), grid, dim3(256), 0, st,
+                           (const uint16_t *)cb, codes, F, K, E, d_cb, (half_t *)z);
+    else if (cb_dtype == 0 && out_dtype == 0)
+        hipLaunchKernelGGL((rvq_gather_kernel<float, float>), grid, dim3(256), 0, st,
+                           (const float *)cb, codes, F, K, E, d_cb, (float *)z);
+    else if (cb_dtype == 1 && out_dtype == 0)
+        hipLaunchKernelGGL((rvq_gather_kernel<uint16_t, float>), grid, dim3(256), 0, st,
+                           (const uint16_t *)cb, codes, F, K, E, d_cb, (float *)z);
+    else
+        hipLaunchKernelGGL((rvq_gather_kernel<float, half_t>), grid, dim3(256), 0, st,
+                           (const float *)cb, codes, F, K, E, d_cb, (half_t *)z);
+    return hipGetLastError();
+}
+
+hipError_t launch_final_conv(const void *A, int dtype, int A_H, int C, int rate, const float *w,
+                             float b, int final_tanh, const int32_t *frame_stream, int M,
+                             float *pcm, hipStream_t st)
+{
+    if (M <= 0)
+        return hipSuccess;
+    dim3 grid((M + 255) / 256);
+    size_t sh = sizeof(float) * 7 * C;
+    if (dtype)
+        hipLaunchKernelGGL(final_conv_kernel<half_t>, grid, dim3(256), sh, st, (const half_t *)A,
+                           A_H, C, rate, w, b, final_tanh, frame_stream, M, pcm);
+    else
+        hipLaunchKernelGGL(final_conv_kernel<float>, grid, dim3(256), sh, st, (const float *)A,
+                           A_H, C, rate, w, b, final_tanh, frame_stream, M, pcm);
+    return hipGetLastError();
+}
+
+hipError_t launch_unextend(const void *ext, int dtype, int H, int C, int rate,
+                           const int32_t *frame_stream, int M, float *dst, hipStream_t st)
+{
+    long total = (long)M * C;
+    if (total <= 0)
+        return hipSuccess;
+    dim3 grid((unsigned)((total + 255) / 256));
+    if (dtype)
+        hipLaunchKernelGGL(unextend_kernel<half_t>, grid, dim3(256), 0, st, (const half_t *)ext, H,
+                           C, rate, frame_stream, M, dst);
+    else
+        hipLaunchKernelGGL(unextend_kernel<float>, grid, dim3(256), 0, st, (const float *)ext, H, C,
+                           rate, frame_stream, M, dst);
+    return hipGetLastError();
+}
+
+}  // namespace snrvq

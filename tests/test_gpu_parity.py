@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path, called through the C ABI, against the fp64 oracle.
+
+Bar: per stream, max|gpu - oracle| <= tol * max|oracle| with tol = 1e-5 for
+fp32 weights and 2e-3 for bf16 weights; codebook indexing bit-exact; the
+GPU's streamed and whole-utterance decodes within the same bound; repeated
+runs bitwise identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rvq_inputs as RI
+import streaming_neural_audio_rvq_amd as snr
+from _util import analytic_left_context, host_weights, rel_err, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def open_codec(cfg, w=None):
+    w = RI.make_weights(cfg) if w is None else w
+    return snr.Codec(cfg, host_weights(cfg, w))
+
+
+def run_lockstep(codec, ids, codes, plan):
+    """All streams decode chunk sizes plan[0], plan[1], ... in lockstep.
+    codes[b] is [T, K]; returns per-stream concatenated PCM (numpy f32)."""
+    hop = codec.hop
+    B = len(ids)
+    outs = [[] for _ in range(B)]
+    at = 0
+    for n in plan:
+        packed = np.concatenate([codes[b][at:at + n] for b in range(B)])
+        pcm = torch.empty(B * n * hop, dtype=torch.float32, device="cuda")
+        codec.decode_chunk(ids, [n] * B, packed, pcm)
+        host = pcm.cpu().numpy()
+        for b in range(B):
+            outs[b].append(host[b * n * hop:(b + 1) * n * hop])
+        at += n
+    return [np.concatenate(o) for o in outs]
+
+
+def decode_full_gpu(codec, codes_list):
+    """Whole-utterance decode of every stream in one call (fresh streams)."""
+    ids = [codec.stream_open() for _ in codes_list]
+    n = [c.shape[0] for c in codes_list]
+    pcm = torch.empty(sum(n) * codec.hop, dtype=torch.float32, device="cuda")
+    codec.decode_chunk(ids, n, np.concatenate(codes_list), pcm)
+    host = pcm.cpu().numpy()
+    out, at = [], 0
+    for k in n:
+        out.append(host[at * codec.hop:(at + k) * codec.hop])
+        at += k
+    for i in ids:
+        codec.stream_close(i)
+    return out
+
+
+# --------------------------------------------------------------------------
+def test_c1_fp32_streamed_and_full_vs_oracle():
+    cfg = RI.get_config("c1")
+    say("case c1 fp32: 1 stream x 50 frames, chunks", RI.C1_CHUNKS)
+    w = RI.make_weights(cfg)
+    codes = RI.stream_codes(cfg, 0, cfg["n_frames"])
+    ref = oracle.Model(cfg, w).decode_full(codes)
+    c = open_codec(cfg, w)
+    sid = c.stream_open()
+    streamed = run_lockstep(c, [sid], [codes], RI.C1_CHUNKS)[0]
+    full = decode_full_gpu(c, [codes])[0]
+    e_s, ac_s = rel_err(streamed, ref)
+    e_f, _ = rel_err(full, ref)
+    e_sf, _ = rel_err(streamed, full.astype(np.float64))
+    say(f"c1 err/peak streamed {e_s:.3e} (AC-rel {ac_s:.3e}) full {e_f:.3e} streamed-vs-full {e_sf:.3e}")
+    assert e_s <= 1e-5 and e_f <= 1e-5 and e_sf <= 1e-5
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_index_probe_gather_bit_exact(name):
+    cfg = RI.get_config(name)
+    say("case index probe", name)
+    w = RI.index_probe_weights(cfg)
+    m = oracle.Model(cfg, w)
+    codes = np.concatenate([RI.stream_codes(cfg, b, 5 + 3 * b) for b in range(3)])
+    n = [5, 8, 11]
+    _, u_ref, _ = m.stream().decode(codes, capture=True)  # rows are independent per frame
+    c = open_codec(cfg, w)
+    ids = [c.stream_open() for _ in n]
+    pcm = torch.empty(sum(n) * c.hop, dtype=torch.float32, device="cuda")
+    c.decode_chunk(ids, n, codes, pcm)
+    cap = torch.empty(sum(n) * cfg["d_lat"], dtype=torch.float32, device="cuda")
+    c.debug_capture(snr.CAPTURE_LATENT, cap)
+    got = cap.cpu().numpy().reshape(sum(n), cfg["d_lat"]).astype(np.float64)
+    assert np.array_equal(got, u_ref)
+
+
+def test_c2_streamed_ramp_vs_oracle_and_full():
+    cfg = RI.get_config("c2")
+    plan = [1, 2, 4, 8, 8, 8]
+    B = 3
+    say("case c2 bf16:", B, "streams, lockstep chunks", plan)
+    w = RI.make_weights(cfg)
+    T = sum(plan)
+    codes = [RI.stream_codes(cfg, b, T) for b in range(B)]
+    m = oracle.Model(cfg, w)
+    refs = [m.decode_full(cd) for cd in codes]
+    c = open_codec(cfg, w)
+    ids = [c.stream_open() for _ in range(B)]
+    streamed = run_lockstep(c, ids, codes, plan)
+    full = decode_full_gpu(c, codes)
+    tol = tol_for(cfg)
+    for b in range(B):
+        e, ac = rel_err(streamed[b], refs[b])
+        ef, _ = rel_err(full[b], refs[b])
+        esf, _ = rel_err(streamed[b], full[b].astype(np.float64))
+        say(f"stream {b}: err/peak {e:.3e} (AC-rel {ac:.3e}) full {ef:.3e} "
+            f"streamed-vs-full {esf:.3e} bitwise={np.array_equal(streamed[b], full[b])}")
+        assert e <= tol and ef <= tol and esf <= tol
+
+
+def test_single_frame_utterance_decodes():
+    # a one-frame request whose final chunk is that one frame must decode
+    cfg = RI.get_config("c2")
+    say("case single-frame utterance")
+    w = RI.make_weights(cfg)
+    codes = RI.stream_codes(cfg, 7, 1)
+    ref = oracle.Model(cfg, w).decode_full(codes)
+    c = open_codec(cfg, w)
+    got = decode_full_gpu(c, [codes])[0]
+    torch.cuda.synchronize()
+    assert got.shape == ref.shape
+    assert rel_err(got, ref)[0] <= tol_for(cfg)
+
+
+def test_ragged_mixed_batch_and_prefill():
+    # streams at different positions with different chunk sizes in one call,
+    # after a prefill; compared with the oracle's whole-utterance decode.
+    cfg = RI.get_config("c2")
+    say("case ragged batch + prefill")
+    w = RI.make_weights(cfg)
+    m = oracle.Model(cfg, w)
+    c = open_codec(cfg, w)
+    pre = [0, 5, 13, 2]
+    steps = [[3, 1, 16, 2], [1, 7, 1, 9]]
+    tot = [pre[b] + sum(s[b] for s in steps) for b in range(4)]
+    codes = [RI.stream_codes(cfg, b, tot[b], part=9) for b in range(4)]
+    ids = [c.stream_open() for _ in range(4)]
+    for b in range(4):
+        if pre[b]:
+            c.stream_prefill(ids[b], codes[b][:pre[b]])
+    at = list(pre)
+    outs = [[] for _ in range(4)]
+    for st in steps:
+        packed = np.concatenate([codes[b][at[b]:at[b] + st[b]] for b in range(4)])
+        pcm = torch.empty(sum(st) * c.hop, dtype=torch.float32, device="cuda")
+        c.decode_chunk(ids, st, packed, pcm)
+        host = pcm.cpu().numpy()
+        o = 0
+        for b in range(4):
+            outs[b].append(host[o * c.hop:(o + st[b]) * c.hop])
+            o += st[b]
+            at[b] += st[b]
+    H = c.hop
+    for b in range(4):
+        ref = m.decode_full(codes[b])[pre[b] * H:]
+        got = np.concatenate(outs[b])
+        e, ac = rel_err(got, ref)
+        say(f"stream {b} pre={pre[b]}: err/peak {e:.3e} AC-rel {ac:.3e}")
+        assert e <= tol_for(cfg)
+
+
+def test_repeat_runs_bitwise_identical():
+    cfg = RI.get_config("c2")
+    say("case determinism")
+    w = RI.make_weights(cfg)
+    codes = [RI.stream_codes(cfg, b, 12) for b in range(5)]
+    c = open_codec(cfg, w)
+    a = decode_full_gpu(c, codes)
+    b = decode_full_gpu(c, codes)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_c4_full_scale_sampled_parity():
+    """The headline workload: 128 streams at staggered offsets (prefilled),
+    steps of mixed chunk sizes {1,2,4,8,16}; sampled streams' chunks are
+    checked against the oracle, which decodes each from its left-context
+    window (exact, since an output frame depends on at most L earlier frames)."""
+    cfg = RI.get_config("c4")
+    steps = 3
+    say("case c4: 128 streams, offsets 0..500, steps", steps)
+    w = RI.make_weights(cfg)
+    c = open_codec(cfg, w)
+    Bn = cfg["n_streams"]
+    off = RI.c4_offsets(cfg)
+    ids = [c.stream_open() for _ in range(Bn)]
+    hist = [RI.stream_codes(cfg, b, int(off[b]), part=0) for b in range(Bn)]
+    for b in range(Bn):
+        if off[b]:
+            c.stream_prefill(ids[b], hist[b])
+    last = None
+    for j in range(steps):
+        n = RI.c4_chunk_sizes(cfg, j)
+        step_codes = [RI.stream_codes(cfg, b, int(n[b]), part=1 + j) for b in range(Bn)]
+        pcm = torch.empty(int(n.sum()) * c.hop, dtype=torch.float32, device="cuda")
+        c.decode_chunk(ids, n, np.concatenate(step_codes), pcm)
+        for b in range(Bn):
+            hist[b] = np.concatenate([hist[b], step_codes[b]])
+        last = (n, pcm.cpu().numpy())
+    n, host = last
+    H = c.hop
+    L = analytic_left_context(cfg) + 1
+    cu = np.concatenate([[0], np.cumsum(n)])
+    sample = sorted({int(np.argmin(off)), int(np.argmax(off))} |
+                    {int(b) for b in np.random.default_rng(3).choice(Bn, 6, replace=False)})
+    m = oracle.Model(cfg, w)
+    for b in sample:
+        T = hist[b].shape[0]
+        start = T - int(n[b])
+        w0 = max(0, start - L)
+        ref = m.stream(w0).decode(hist[b][w0:])[(start - w0) * H:]
+        got = host[cu[b] * H:cu[b + 1] * H]
+        e, ac = rel_err(got, ref)
+        say(f"c4 stream {b} offset {off[b]} pos {start} n {n[b]}: err/peak {e:.3e} AC-rel {ac:.3e}")
+        assert e <= tol_for(cfg)

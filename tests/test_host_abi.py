@@ -1,0 +1,123 @@
+"""CPU-only checks of the HIP library's host side: it loads, exports every
+function its header declares, and its host-only policy and argument checks
+behave as specified.  No kernel runs here."""
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import rvq_inputs as RI
+import streaming_neural_audio_rvq_amd as snr
+from oracle import policy
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLD = json.load(open(os.path.join(ROOT, "tests", "golden", "chunk_plan_qwen3_tts.json")))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "snrvq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    L = snr.lib()
+    declared = header_functions()
+    assert len(declared) >= 13
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(snr.EXPORTS) == declared
+
+
+def test_chunk_plan_printed_example():
+    plan = snr.chunk_plan(sum(GOLD["new_frames_per_decode"]), GOLD["ramp"], GOLD["steady"])
+    assert plan == GOLD["new_frames_per_decode"]
+    assert policy.decode_points(plan)[:6] == GOLD["decode_points_first_six"]
+
+
+def test_chunk_plan_matches_oracle_policy():
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        total = int(rng.integers(0, 120))
+        ramp = tuple(int(v) for v in rng.integers(1, 12, size=int(rng.integers(0, 5))))
+        steady = int(rng.integers(1, 17))
+        initial = int(rng.integers(0, 20)) if rng.random() < 0.3 else 0
+        if not ramp and initial == 0:
+            ramp = (steady,)
+        assert snr.chunk_plan(total, ramp, steady, initial) == \
+            policy.chunk_plan(total, ramp, steady, initial), (total, ramp, steady, initial)
+
+
+def test_resolve_initial_chunk_frames():
+    assert snr.resolve_initial_chunk_frames(None, 8) == 0
+    assert snr.resolve_initial_chunk_frames(None, 8, 3) == 3
+    assert snr.resolve_initial_chunk_frames("5", 8) == 5
+    assert snr.resolve_initial_chunk_frames(40, 8) == 8
+    with pytest.raises(ValueError):
+        snr.resolve_initial_chunk_frames(3, 0)
+    with pytest.raises(TypeError):
+        snr.resolve_initial_chunk_frames("abc", 8)
+    with pytest.raises(ValueError):
+        snr.resolve_initial_chunk_frames(-1, 8)
+
+
+def _bits(cfg, w):
+    return RI.weight_bits(w) if cfg["weight_dtype"] == "bf16" else w
+
+
+def open_err(cfg, weights):
+    with pytest.raises(snr.CodecError) as ei:
+        snr.Codec(cfg, weights)
+    return ei.value
+
+
+def test_open_rejects_bad_config_before_touching_a_device():
+    cfg = RI.get_config("c1")
+    w = RI.make_weights(cfg)
+    e = open_err(dict(cfg, K=0), w)
+    assert e.code == snr.CODEC_EINVAL and "K=0" in str(e)
+    e = open_err(dict(cfg, strides=[]), w)
+    assert e.code == snr.CODEC_EINVAL
+    e = open_err(dict(cfg, max_frames_per_call=0), w)
+    assert e.code == snr.CODEC_EINVAL
+    e = open_err(dict(cfg, d_lat=48), RI.make_weights(dict(cfg, d_lat=48)))
+    assert e.code == snr.CODEC_EINVAL and "multiple" in str(e)
+
+
+def test_open_rejects_bad_weight_manifest():
+    cfg = RI.get_config("c1")
+    w = dict(RI.make_weights(cfg))
+    missing = {k: v for k, v in w.items() if k != "dec.out.conv.bias"}
+    e = open_err(cfg, missing)
+    assert e.code == snr.CODEC_EINVAL and "dec.out.conv.bias" in str(e) and "missing" in str(e)
+    bad = dict(w)
+    bad["dec.stage.0.convT.weight"] = np.zeros((3, 3, 3), np.float32)
+    e = open_err(cfg, bad)
+    assert e.code == snr.CODEC_EINVAL and "shape" in str(e)
+    extra = dict(w)
+    extra["dec.bogus"] = np.zeros(3, np.float32)
+    e = open_err(cfg, extra)
+    assert e.code == snr.CODEC_EINVAL and "dec.bogus" in str(e)
+    # fp32 tensors for a configuration whose weights are bf16: dtype mismatch
+    import ctypes as C
+    cfg2 = RI.get_config("c2")
+    w2 = RI.make_weights(cfg2)
+    arr, keep = snr.make_tensors(w2, "fp32")
+    h = C.c_void_p()
+    rc = snr.lib().codec_open(arr, len(w2), C.byref(snr.make_cfg(cfg2)), C.byref(h))
+    assert rc == snr.CODEC_EINVAL and not h.value
+    assert b"dtype" in snr.lib().codec_last_error(None)
+    with pytest.raises(TypeError):
+        snr.make_tensors(w2, "bf16")  # the binding wants bit patterns for bf16
+
+
+def test_open_without_gpu_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    cfg = RI.get_config("c1")
+    e = open_err(cfg, RI.make_weights(cfg))
+    assert e.code == snr.CODEC_EHIP

@@ -17,6 +17,7 @@ import torch.nn.functional as F
 
 import oracle
 import rvq_inputs as RI
+from _util import analytic_first_frame, analytic_left_context
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 rng = np.random.default_rng(1234)
@@ -313,25 +314,6 @@ def test_decode_batch_equals_per_stream():
 # --------------------------------------------------------------------------
 # Receptive field: perturbation vs the analytic left context
 # --------------------------------------------------------------------------
-def analytic_first_frame(cfg, n):
-    """Earliest frame that output sample n depends on: walk back through the
-    layers (causal conv i -> i - (k-1) d; transposed conv i -> floor(i/s) - 1;
-    windowed attention i -> i - (window - 1) per layer)."""
-    i = n - 6                                   # output conv, k 7
-    for s in reversed(cfg["strides"]):
-        i -= 3 * 6                              # residual unit, dilation 3
-        i -= 6                                  # residual unit, dilation 1
-        i = i // s - 1                          # transposed conv, kernel 2 s
-    i -= 6                                      # input conv
-    i -= cfg["tf_layers"] * max(cfg["tf_window"] - 1, 0)
-    return i
-
-
-def analytic_left_context(cfg):
-    H = RI.hop(cfg)
-    return max(n // H - analytic_first_frame(cfg, n) for n in range(4 * H, 5 * H))
-
-
 @pytest.mark.parametrize("name,expect", [("c1", 16), ("c2", 11), ("c3", 135)])
 def test_left_context_frames(name, expect):
     assert analytic_left_context(RI.get_config(name)) == expect
