@@ -91,6 +91,15 @@ struct codec {
     float *out_w = nullptr;
     float out_b = 0.f;
 
+    // windowed transformer (tf_layers > 0)
+    int dm = 0;
+    Lin tf_in, tf_out, tf_qkv[16], tf_o[16], tf_fc1[16], tf_fc2[16];
+    float *ln1_g[16]{}, *ln1_b[16]{}, *ln2_g[16]{}, *ln2_b[16]{}, *lnf_g = nullptr,
+          *lnf_b = nullptr;
+    double *inv_freq = nullptr;
+    void *u16 = nullptr, *a16 = nullptr, *att16 = nullptr, *f16 = nullptr;
+    float *h32 = nullptr, *qkv32 = nullptr, *kring = nullptr, *vring = nullptr;
+
     void *z = nullptr, *u_ext = nullptr, *aT[CODEC_MAX_STAGES]{}, *a1[CODEC_MAX_STAGES]{},
          *a2[CODEC_MAX_STAGES]{}, *h = nullptr, *a_outb = nullptr;
     float *x = nullptr, *pcm_scratch = nullptr;
@@ -174,6 +183,30 @@ std::vector<ParamSpec> param_specs(const codec_cfg &g, const int *ch)
     }
     v.push_back({"rvq.proj.weight", {g.d_lat, g.d_cb}});
     v.push_back({"rvq.proj.bias", {g.d_lat}});
+    if (g.tf_layers > 0) {
+        int64_t dm = (int64_t)g.tf_heads * g.tf_head_dim, mlp = g.tf_mlp;
+        v.push_back({"tf.in_proj.weight", {dm, g.d_lat}});
+        v.push_back({"tf.in_proj.bias", {dm}});
+        for (int l = 0; l < g.tf_layers; l++) {
+            std::string p = "tf.layer." + std::to_string(l) + ".";
+            v.push_back({p + "ln1.weight", {dm}});
+            v.push_back({p + "ln1.bias", {dm}});
+            v.push_back({p + "attn.qkv.weight", {3 * dm, dm}});
+            v.push_back({p + "attn.qkv.bias", {3 * dm}});
+            v.push_back({p + "attn.out.weight", {dm, dm}});
+            v.push_back({p + "attn.out.bias", {dm}});
+            v.push_back({p + "ln2.weight", {dm}});
+            v.push_back({p + "ln2.bias", {dm}});
+            v.push_back({p + "mlp.fc1.weight", {mlp, dm}});
+            v.push_back({p + "mlp.fc1.bias", {mlp}});
+            v.push_back({p + "mlp.fc2.weight", {dm, mlp}});
+            v.push_back({p + "mlp.fc2.bias", {dm}});
+        }
+        v.push_back({"tf.ln_f.weight", {dm}});
+        v.push_back({"tf.ln_f.bias", {dm}});
+        v.push_back({"tf.out_proj.weight", {g.d_lat, dm}});
+        v.push_back({"tf.out_proj.bias", {g.d_lat}});
+    }
     v.push_back({"dec.in_conv.weight", {ch[0], g.d_lat, 7}});
     v.push_back({"dec.in_conv.bias", {ch[0]}});
     for (int i = 0; i < g.n_stages; i++) {
@@ -399,6 +432,84 @@ int run_conv(codec *c, const char *name, const ConvArgs &a, hipStream_t s)
 
 size_t round4(size_t n) { return (n + 3) & ~(size_t)3; }
 
+// Windowed causal transformer over the F new frames of this step (pre-norm
+// layers; the KV ring holds every stream's last W-1 frames per layer).
+int enqueue_transformer(codec *c, int B, int F, const StepMeta &m, hipStream_t s)
+{
+    const codec_cfg &g = c->cfg;
+    const int dm = c->dm;
+    ConvArgs a = conv_args(c, c->tf_in, c->u16, 0, 1, F, m);
+    a.out32 = c->h32;
+    int rc = run_conv(c, "tf.in_proj", a, s);
+    if (rc)
+        return rc;
+    AttnArgs at{};
+    at.qkv = c->qkv32;
+    at.att = c->att16;
+    at.kring = c->kring;
+    at.vring = c->vring;
+    at.frame_stream = m.frame_stream;
+    at.cu = m.cu;
+    at.slot = m.slot;
+    at.pos = m.pos;
+    at.F = F;
+    at.H = g.tf_heads;
+    at.hd = g.tf_head_dim;
+    at.W = g.tf_window;
+    at.n_layers = g.tf_layers;
+    at.dtype = c->dtype;
+    for (int l = 0; l < g.tf_layers; l++) {
+        at.layer = l;
+        if ((rc = timed(c, "tf.ln", F, s, [&] {
+                 return launch_layer_norm(c->h32, c->ln1_g[l], c->ln1_b[l], F, dm, c->a16,
+                                          c->dtype, s);
+             })))
+            return rc;
+        a = conv_args(c, c->tf_qkv[l], c->a16, 0, 1, F, m);
+        a.out32 = c->qkv32;
+        if ((rc = run_conv(c, "tf.qkv", a, s)))
+            return rc;
+        if ((rc = timed(c, "tf.rope", F, s, [&] {
+                 return launch_rope(c->qkv32, c->inv_freq, m.frame_stream, m.cu, m.pos, F,
+                                    g.tf_heads, g.tf_head_dim, s);
+             })))
+            return rc;
+        if ((rc = timed(c, "tf.attention", F, s, [&] { return launch_window_attention(at, s); })))
+            return rc;
+        if ((rc = timed(c, "tf.kv_append", B, s, [&] { return launch_kv_append(at, B, s); })))
+            return rc;
+        a = conv_args(c, c->tf_o[l], c->att16, 0, 1, F, m);
+        a.res = c->h32;
+        a.out32 = c->h32;
+        if ((rc = run_conv(c, "tf.o_proj", a, s)))
+            return rc;
+        if ((rc = timed(c, "tf.ln", F, s, [&] {
+                 return launch_layer_norm(c->h32, c->ln2_g[l], c->ln2_b[l], F, dm, c->a16,
+                                          c->dtype, s);
+             })))
+            return rc;
+        a = conv_args(c, c->tf_fc1[l], c->a16, 0, 1, F, m);
+        a.out16 = c->f16;
+        a.out_H = 0;
+        a.act = ACT_GELU;
+        if ((rc = run_conv(c, "tf.fc1", a, s)))
+            return rc;
+        a = conv_args(c, c->tf_fc2[l], c->f16, 0, 1, F, m);
+        a.res = c->h32;
+        a.out32 = c->h32;
+        if ((rc = run_conv(c, "tf.fc2", a, s)))
+            return rc;
+    }
+    if ((rc = timed(c, "tf.ln", F, s, [&] {
+             return launch_layer_norm(c->h32, c->lnf_g, c->lnf_b, F, dm, c->a16, c->dtype, s);
+         })))
+        return rc;
+    a = conv_args(c, c->tf_out, c->a16, 0, 1, F, m);
+    a.out16 = c->u_ext;
+    a.out_H = 6;
+    return run_conv(c, "tf.out_proj", a, s);
+}
+
 // One decode step over B streams (slots[] / n[] / codes[] already validated).
 int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int32_t *codes,
                  float *pcm, hipStream_t s)
@@ -450,9 +561,11 @@ int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int3
         return rc;
 
     ConvArgs a = conv_args(c, c->proj, c->z, 0, 1, F, m);
-    a.out16 = c->u_ext;
-    a.out_H = 6;
+    a.out16 = g.tf_layers ? c->u16 : c->u_ext;
+    a.out_H = g.tf_layers ? 0 : 6;
     if ((rc = run_conv(c, "proj", a, s)))
+        return rc;
+    if (g.tf_layers && (rc = enqueue_transformer(c, B, F, m, s)))
         return rc;
 
     a = conv_args(c, c->in_conv, c->u_ext, 6, 1, F, m);
@@ -541,11 +654,21 @@ int check_cfg(const codec_cfg *g, int *ch, int *hop)
     if (g->max_streams < 1 || g->max_frames_per_call < 1)
         return set_err(nullptr, CODEC_EINVAL, "cfg: max_streams=%d, max_frames_per_call=%d",
                        g->max_streams, g->max_frames_per_call);
-    if (g->tf_layers != 0)
-        return set_err(nullptr, CODEC_EINVAL,
-                       "cfg: tf_layers=%d: the windowed transformer is not in this build",
-                       g->tf_layers);
     int gran = g->weight_dtype == CODEC_DTYPE_BF16 ? 32 : 16;
+    if (g->tf_layers < 0 || g->tf_layers > 16)
+        return set_err(nullptr, CODEC_EINVAL, "cfg: tf_layers=%d (0..16)", g->tf_layers);
+    if (g->tf_layers > 0) {
+        if (g->tf_head_dim != 64 || g->tf_heads < 1 || g->tf_heads > 64)
+            return set_err(nullptr, CODEC_EINVAL,
+                           "cfg: tf_heads=%d tf_head_dim=%d (head_dim must be 64)", g->tf_heads,
+                           g->tf_head_dim);
+        if (g->tf_window < 1 || g->tf_window > SNRVQ_MAX_WINDOW)
+            return set_err(nullptr, CODEC_EINVAL, "cfg: tf_window=%d (1..%d)", g->tf_window,
+                           SNRVQ_MAX_WINDOW);
+        if (g->tf_mlp < gran || g->tf_mlp % gran)
+            return set_err(nullptr, CODEC_EINVAL, "cfg: tf_mlp=%d is not a multiple of %d",
+                           g->tf_mlp, gran);
+    }
     ch[0] = g->d_lat;
     *hop = 1;
     for (int i = 0; i < g->n_stages; i++) {
@@ -703,6 +826,40 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
     if ((rc = make_lin(c, W("rvq.proj.weight"), W("rvq.proj.bias"), g.d_lat, g.d_lat, g.d_cb, 1,
                        1, 1, &c->proj)))
         return cleanup_fail(rc);
+    if (g.tf_layers) {
+        const int dm = g.tf_heads * g.tf_head_dim, mlp = g.tf_mlp;
+        c->dm = dm;
+        if ((rc = make_lin(c, W("tf.in_proj.weight"), W("tf.in_proj.bias"), dm, dm, g.d_lat, 1,
+                           1, 1, &c->tf_in)))
+            return cleanup_fail(rc);
+        for (int l = 0; l < g.tf_layers; l++) {
+            std::string p = "tf.layer." + std::to_string(l) + ".";
+            if ((rc = upload_f32(c, W(p + "ln1.weight"), &c->ln1_g[l])) ||
+                (rc = upload_f32(c, W(p + "ln1.bias"), &c->ln1_b[l])) ||
+                (rc = upload_f32(c, W(p + "ln2.weight"), &c->ln2_g[l])) ||
+                (rc = upload_f32(c, W(p + "ln2.bias"), &c->ln2_b[l])) ||
+                (rc = make_lin(c, W(p + "attn.qkv.weight"), W(p + "attn.qkv.bias"), 3 * dm,
+                               3 * dm, dm, 1, 1, 1, &c->tf_qkv[l])) ||
+                (rc = make_lin(c, W(p + "attn.out.weight"), W(p + "attn.out.bias"), dm, dm, dm, 1,
+                               1, 1, &c->tf_o[l])) ||
+                (rc = make_lin(c, W(p + "mlp.fc1.weight"), W(p + "mlp.fc1.bias"), mlp, mlp, dm,
+                               1, 1, 1, &c->tf_fc1[l])) ||
+                (rc = make_lin(c, W(p + "mlp.fc2.weight"), W(p + "mlp.fc2.bias"), dm, dm, mlp, 1,
+                               1, 1, &c->tf_fc2[l])))
+                return cleanup_fail(rc);
+        }
+        if ((rc = upload_f32(c, W("tf.ln_f.weight"), &c->lnf_g)) ||
+            (rc = upload_f32(c, W("tf.ln_f.bias"), &c->lnf_b)) ||
+            (rc = make_lin(c, W("tf.out_proj.weight"), W("tf.out_proj.bias"), g.d_lat, g.d_lat,
+                           dm, 1, 1, 1, &c->tf_out)))
+            return cleanup_fail(rc);
+        std::vector<double> inv(g.tf_head_dim / 2);
+        for (size_t i = 0; i < inv.size(); i++)
+            inv[i] = std::pow(10000.0, -(2.0 * (double)i) / g.tf_head_dim);
+        if ((rc = dev_alloc(c, (void **)&c->inv_freq, inv.size() * 8, &c->weight_bytes)))
+            return cleanup_fail(rc);
+        HIPCHK(c, hipMemcpy(c->inv_freq, inv.data(), inv.size() * 8, hipMemcpyHostToDevice));
+    }
     if ((rc = make_lin(c, pack_conv(W("dec.in_conv.weight"), ch[0], g.d_lat, 7),
                        W("dec.in_conv.bias"), ch[0], ch[0], g.d_lat, 7, 1, 1, &c->in_conv)))
         return cleanup_fail(rc);
@@ -760,6 +917,18 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
         return cleanup_fail(rc);
     if ((rc = dev_alloc(c, &c->a_outb, (B * 6 + F * hop) * ch[c->S] * es, ws)))
         return cleanup_fail(rc);
+    if (g.tf_layers) {
+        const size_t dm = c->dm, W1 = g.tf_window - 1;
+        if ((rc = dev_alloc(c, &c->u16, F * g.d_lat * es, ws)) ||
+            (rc = dev_alloc(c, &c->a16, F * dm * es, ws)) ||
+            (rc = dev_alloc(c, &c->att16, F * dm * es, ws)) ||
+            (rc = dev_alloc(c, &c->f16, F * g.tf_mlp * es, ws)) ||
+            (rc = dev_alloc(c, (void **)&c->h32, F * dm * 4, ws)) ||
+            (rc = dev_alloc(c, (void **)&c->qkv32, F * 3 * dm * 4, ws)) ||
+            (rc = dev_alloc(c, (void **)&c->kring, B * g.tf_layers * (W1 ? W1 : 1) * dm * 4, ws)) ||
+            (rc = dev_alloc(c, (void **)&c->vring, B * g.tf_layers * (W1 ? W1 : 1) * dm * 4, ws)))
+            return cleanup_fail(rc);
+    }
     if ((rc = dev_alloc(c, (void **)&c->pcm_scratch, F * hop * 4, ws)))
         return cleanup_fail(rc);
 
@@ -851,7 +1020,9 @@ int codec_info(const codec_t *c, codec_info_t *o)
     o->max_frames_per_call = c->maxF;
     o->open_streams = (int32_t)c->id2slot.size();
     o->compute_dtype = c->dtype ? CODEC_DTYPE_F16 : CODEC_DTYPE_F32;
-    o->state_bytes_per_stream = c->slot_elems * c->esz;
+    o->state_bytes_per_stream =
+        c->slot_elems * c->esz +
+        (c->cfg.tf_layers ? (int64_t)2 * c->cfg.tf_layers * (c->cfg.tf_window - 1) * c->dm * 4 : 0);
     o->weight_bytes = c->weight_bytes;
     o->workspace_bytes = c->workspace_bytes;
     return CODEC_OK;
@@ -989,8 +1160,10 @@ int codec_debug_capture(codec_t *c, int32_t what, float *dst, int64_t capacity,
         return fail(c, CODEC_EINVAL, "codec_debug_capture: capacity %lld < %lld",
                     (long long)capacity, (long long)need);
     HIPCHK(c, hipSetDevice(c->dev));
-    HIPCHK(c, launch_unextend(c->u_ext, c->dtype, 6, c->cfg.d_lat, 1, c->last_meta.frame_stream,
-                              c->lastF, dst, (hipStream_t)stream));
+    const bool tf_latent = what == CODEC_CAPTURE_LATENT && c->cfg.tf_layers > 0;
+    HIPCHK(c, launch_unextend(tf_latent ? c->u16 : c->u_ext, c->dtype, tf_latent ? 0 : 6,
+                              c->cfg.d_lat, 1, c->last_meta.frame_stream, c->lastF, dst,
+                              (hipStream_t)stream));
     return CODEC_OK;
 }
 

@@ -92,4 +92,23 @@ hipError_t launch_final_conv(const void *A, int dtype, int A_H, int C, int rate,
 hipError_t launch_unextend(const void *ext, int dtype, int H, int C, int rate,
                            const int32_t *frame_stream, int M, float *dst, hipStream_t st);
 
+// ---- transformer ops (kernels_tf.hip) ----
+#define SNRVQ_MAX_WINDOW 32  // keys per query, including its own frame
+struct AttnArgs {
+    float *qkv;               // [F][3 dm] fp32, bias included; q, k rotated in place
+    void *att;                // [F][dm] compute type
+    float *kring, *vring;     // [slots][layers][W-1][dm] fp32
+    const int32_t *frame_stream, *cu, *slot, *pos;
+    int F, H, hd, W, layer, n_layers;
+    int dtype;
+};
+// y[f] = LN(x[f]) in the compute type (x fp32 [F][D], D % 64 == 0).
+hipError_t launch_layer_norm(const float *x, const float *g, const float *b, int F, int D,
+                             void *y, int dtype, hipStream_t st);
+hipError_t launch_rope(float *qkv, const double *inv_freq, const int32_t *frame_stream,
+                       const int32_t *cu, const int32_t *pos, int F, int H, int hd,
+                       hipStream_t st);
+hipError_t launch_window_attention(const AttnArgs &a, hipStream_t st);
+hipError_t launch_kv_append(const AttnArgs &a, int B, hipStream_t st);
+
 }  // namespace snrvq

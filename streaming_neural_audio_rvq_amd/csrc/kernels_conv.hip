@@ -255,9 +255,15 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
         if (p.out16) {
             int ch = n % p.Cout;
             f4 y;
+            if (p.act == ACT_SNAKE) {
 #pragma unroll
-            for (int e = 0; e < 4; e++)
-                y[e] = act_fn(v[e], p.act, p.alpha[ch + e], p.inv_alpha[ch + e]);
+                for (int e = 0; e < 4; e++)
+                    y[e] = act_fn(v[e], ACT_SNAKE, p.alpha[ch + e], p.inv_alpha[ch + e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    y[e] = act_fn(v[e], p.act, 0.f, 0.f);
+            }
             int b = p.frame_stream[m / p.rate_in];
             long base = ((long)(b + 1) * p.out_H + orow) * p.Cout + n;
             store4<T>((T *)p.out16 + base, y);

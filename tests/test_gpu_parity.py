@@ -226,3 +226,78 @@ def test_c4_full_scale_sampled_parity():
         e, ac = rel_err(got, ref)
         say(f"c4 stream {b} offset {off[b]} pos {start} n {n[b]}: err/peak {e:.3e} AC-rel {ac:.3e}")
         assert e <= tol_for(cfg)
+
+
+# --------------------------------------------------------------------------
+# Windowed causal transformer (Fish-DAC-shaped decoder)
+# --------------------------------------------------------------------------
+def test_c3_transformer_streamed_vs_oracle():
+    """Two streams, 8-frame chunks past the 32-frame window (ring wraps),
+    plus a third stream joining late in 1-frame and ramp chunks."""
+    cfg = RI.get_config("c3", max_streams=8, max_frames_per_call=64)
+    say("case c3: transformer + conv decoder, chunks of 8 past the window")
+    w = RI.make_weights(cfg)
+    m = oracle.Model(cfg, w)
+    c = open_codec(cfg, w)
+    plan = [8] * 5 + [3]
+    T = sum(plan)
+    codes = [RI.stream_codes(cfg, b, T) for b in range(2)]
+    ids = [c.stream_open() for _ in range(2)]
+    got = run_lockstep(c, ids, codes, plan)
+    # decoder input after the transformer for the last step, both streams
+    cap = torch.empty(2 * plan[-1] * cfg["d_lat"], dtype=torch.float32, device="cuda")
+    c.debug_capture(snr.CAPTURE_DEC_INPUT, cap)
+    cap = cap.cpu().numpy().reshape(2, plan[-1], cfg["d_lat"])
+    for b in range(2):
+        pcm_ref, _, x_ref = m.stream().decode(codes[b], capture=True)
+        e, ac = rel_err(got[b], pcm_ref)
+        ex, _ = rel_err(cap[b], x_ref[-plan[-1]:])
+        say(f"c3 stream {b}: err/peak {e:.3e} (AC-rel {ac:.3e}); transformer output err/peak {ex:.3e}")
+        assert e <= tol_for(cfg)
+        assert ex <= tol_for(cfg)
+    # a late stream with ramp chunks, decoded in the same calls as stream 0
+    c2 = open_codec(cfg, w)
+    late_codes = RI.stream_codes(cfg, 5, 15)
+    a, bb = c2.stream_open(), c2.stream_open()
+    outs = []
+    at = 0
+    for n in [1, 2, 4, 8]:
+        pcm = torch.empty((n + 8) * c2.hop, dtype=torch.float32, device="cuda")
+        c2.decode_chunk([a, bb], [n, 8], np.concatenate([late_codes[at:at + n], codes[0][:8]]), pcm)
+        outs.append(pcm.cpu().numpy()[: n * c2.hop])
+        at += n
+    e, _ = rel_err(np.concatenate(outs), m.decode_full(late_codes))
+    say(f"c3 late ramp stream: err/peak {e:.3e}")
+    assert e <= tol_for(cfg)
+
+
+def test_c3_full_scale_sampled_parity():
+    """64 streams x 300 frames in 8-frame chunks (F = 512 per step); sampled
+    chunks are checked against the oracle decoding the left-context window
+    (135 frames for this decoder) at the true absolute positions."""
+    cfg = RI.get_config("c3")
+    say("case c3 full scale: 64 streams x 300 frames, 8-frame chunks")
+    w = RI.make_weights(cfg)
+    c = open_codec(cfg, w)
+    Bn, T = cfg["n_streams"], cfg["n_frames"]
+    codes = [RI.stream_codes(cfg, b, T) for b in range(Bn)]
+    ids = [c.stream_open() for _ in range(Bn)]
+    H = c.hop
+    keep = {}
+    at = 0
+    for k, n in enumerate(RI.C3_CHUNKS):
+        pcm = torch.empty(Bn * n * H, dtype=torch.float32, device="cuda")
+        c.decode_chunk(ids, [n] * Bn, np.concatenate([cd[at:at + n] for cd in codes]), pcm)
+        if k in (2, 30):
+            keep[k] = (at, n, pcm.cpu().numpy())
+        at += n
+    m = oracle.Model(cfg, w)
+    L = analytic_left_context(cfg) + 1
+    for k, b in ((2, 17), (30, 3), (30, 62)):
+        start, n, host = keep[k]
+        w0 = max(0, start - L)
+        ref = m.stream(w0).decode(codes[b][w0:start + n])[(start - w0) * H:]
+        got = host[b * n * H:(b + 1) * n * H]
+        e, ac = rel_err(got, ref)
+        say(f"c3 chunk {k} stream {b} pos {start}: err/peak {e:.3e} AC-rel {ac:.3e}")
+        assert e <= tol_for(cfg)
