@@ -160,6 +160,21 @@ int decode_chunk(codec_t *codec, int32_t B, const int32_t *stream_ids, const int
                  const int32_t *codes, float *pcm, int64_t pcm_capacity,
                  codec_hip_stream stream);
 
+/* The same step with the codes already in device memory (as when stage 0
+ * samples them on this GPU): codes_dev is device int32 [sum n][K], read on
+ * the stream.  Host checks are those of decode_chunk except the code range,
+ * which is checked on the device: an out-of-range code is counted (see
+ * codec_device_status) and replaced by code 0, so no access leaves the
+ * codebook; the PCM of that step is then not meaningful. */
+int decode_chunk_device(codec_t *codec, int32_t B, const int32_t *stream_ids,
+                        const int32_t *n_frames, const int32_t *codes_dev, float *pcm,
+                        int64_t pcm_capacity, codec_hip_stream stream);
+
+/* Waits for the codec's device work and returns through *bad_codes the
+ * number of out-of-range codes seen by decode_chunk_device since the last
+ * call (then resets it).  CODEC_ERANGE when it is nonzero. */
+int codec_device_status(codec_t *codec, int64_t *bad_codes);
+
 /* ---- inspection (tests) -------------------------------------------------- */
 
 #define CODEC_CAPTURE_LATENT 0    /* projected RVQ sum, [sum n][d_lat] */

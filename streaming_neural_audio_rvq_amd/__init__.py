@@ -60,7 +60,8 @@ _I32P = C.POINTER(C.c_int32)
 _lib = None
 
 EXPORTS = ["codec_open", "codec_close", "codec_info", "codec_last_error", "stream_open",
-           "stream_close", "stream_prefill", "decode_chunk", "codec_debug_capture",
+           "stream_close", "stream_prefill", "decode_chunk", "decode_chunk_device",
+           "codec_device_status", "codec_debug_capture",
            "codec_profile_enable", "codec_profile_read", "codec_chunk_plan",
            "codec_resolve_initial_chunk_frames"]
 
@@ -85,6 +86,9 @@ def lib():
     L.stream_prefill.argtypes = [C.c_void_p, C.c_int32, _I32P, C.c_int32, C.c_void_p]
     L.decode_chunk.argtypes = [C.c_void_p, C.c_int32, _I32P, _I32P, _I32P, C.c_void_p,
                                C.c_int64, C.c_void_p]
+    L.decode_chunk_device.argtypes = [C.c_void_p, C.c_int32, _I32P, _I32P, C.c_void_p,
+                                      C.c_void_p, C.c_int64, C.c_void_p]
+    L.codec_device_status.argtypes = [C.c_void_p, C.POINTER(C.c_int64)]
     L.codec_debug_capture.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int64, C.c_void_p]
     L.codec_profile_enable.argtypes = [C.c_void_p, C.c_int32]
     L.codec_profile_read.argtypes = [C.c_void_p, C.c_int32, C.POINTER(C.c_char_p),
@@ -224,6 +228,22 @@ class Codec:
         _check(lib().decode_chunk(self._h, len(ids), _ptr(ids), _ptr(n), _ptr(codes),
                                   C.c_void_p(pcm.data_ptr()), pcm.numel(),
                                   _stream_handle(stream)), self._h)
+
+    def decode_chunk_device(self, stream_ids, n_frames, codes_dev, pcm, stream=None):
+        """codes_dev: an int32 CUDA tensor [sum n, K] already on the device."""
+        ids = _i32(stream_ids)
+        n = _i32(n_frames)
+        _check(lib().decode_chunk_device(self._h, len(ids), _ptr(ids), _ptr(n),
+                                         C.c_void_p(codes_dev.data_ptr()),
+                                         C.c_void_p(pcm.data_ptr()), pcm.numel(),
+                                         _stream_handle(stream)), self._h)
+
+    def device_status(self) -> int:
+        """Number of out-of-range device-resident codes since the last call
+        (raises CodecError ERANGE when nonzero)."""
+        bad = C.c_int64()
+        _check(lib().codec_device_status(self._h, C.byref(bad)), self._h)
+        return bad.value
 
     def debug_capture(self, what: int, dst, stream=None):
         _check(lib().codec_debug_capture(self._h, what, C.c_void_p(dst.data_ptr()), dst.numel(),

@@ -110,6 +110,7 @@ struct codec {
 
     void *meta_dev = nullptr;
     size_t meta_cap = 0;  // int32 elements
+    unsigned long long *bad_codes = nullptr;  // device counter (device-resident codes)
     void *pinned[2]{};
     hipEvent_t pin_ev[2]{};
     int pin_i = 0;
@@ -357,7 +358,7 @@ hipEvent_t get_ev(codec *c)
 {
     if (c->ev_pool.empty()) {
         hipEvent_t e;
-        hipEventCreate(&e);
+        (void)hipEventCreate(&e);
         return e;
     }
     hipEvent_t e = c->ev_pool.back();
@@ -384,11 +385,11 @@ int timed(codec *c, const char *name, int64_t units, hipStream_t s, Fn &&fn)
     if (c->prof) {
         a = get_ev(c);
         b = get_ev(c);
-        hipEventRecord(a, s);
+        (void)hipEventRecord(a, s);
     }
     hipError_t e = fn();
     if (c->prof) {
-        hipEventRecord(b, s);
+        (void)hipEventRecord(b, s);
         c->recs.push_back({cls_id(c, name), a, b, units});
     }
     if (e != hipSuccess)
@@ -511,8 +512,10 @@ int enqueue_transformer(codec *c, int B, int F, const StepMeta &m, hipStream_t s
 }
 
 // One decode step over B streams (slots[] / n[] / codes[] already validated).
+// codes: host array (copied with the metadata) or, when codes_on_device,
+// a device array read in place.
 int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int32_t *codes,
-                 float *pcm, hipStream_t s)
+                 float *pcm, hipStream_t s, bool codes_on_device = false)
 {
     const codec_cfg &g = c->cfg;
     int F = 0;
@@ -520,14 +523,16 @@ int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int3
         F += n[b];
 
     // ---- batch assembly into the pinned ring, one H2D copy ----
-    size_t o_codes = 0, o_fs = round4(o_codes + (size_t)F * g.K), o_cu = round4(o_fs + F),
+    size_t ncodes = codes_on_device ? 0 : (size_t)F * g.K;
+    size_t o_codes = 0, o_fs = round4(o_codes + ncodes), o_cu = round4(o_fs + F),
            o_slot = round4(o_cu + B + 1), o_fresh = round4(o_slot + B),
            o_pos = round4(o_fresh + B), total = round4(o_pos + B);
     int pi = c->pin_i;
     c->pin_i ^= 1;
     HIPCHK(c, hipEventSynchronize(c->pin_ev[pi]));  // the copy that last read this buffer is done
     int32_t *hp = (int32_t *)c->pinned[pi];
-    memcpy(hp + o_codes, codes, sizeof(int32_t) * (size_t)F * g.K);
+    if (!codes_on_device)
+        memcpy(hp + o_codes, codes, sizeof(int32_t) * (size_t)F * g.K);
     int acc = 0;
     hp[o_cu] = 0;
     for (int b = 0; b < B; b++) {
@@ -540,7 +545,8 @@ int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int3
         hp[o_pos + b] = (int32_t)c->slot_pos[slots[b]];
     }
     int32_t *dm = (int32_t *)c->meta_dev;
-    StepMeta m{dm + o_codes, dm + o_fs, dm + o_cu, dm + o_slot, dm + o_fresh, dm + o_pos};
+    StepMeta m{codes_on_device ? (int32_t *)codes : dm + o_codes, dm + o_fs, dm + o_cu,
+               dm + o_slot, dm + o_fresh, dm + o_pos};
     int rc = timed(c, "h2d_meta", (int64_t)total * 4, s, [&] {
         return hipMemcpyAsync(c->meta_dev, hp, total * 4, hipMemcpyHostToDevice, s);
     });
@@ -555,7 +561,7 @@ int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int3
         return rc;
     rc = timed(c, "rvq_gather", F, s, [&] {
         return launch_rvq_gather(c->cb, c->cb_dtype, m.codes, F, g.K, g.E, g.d_cb, c->z, c->dtype,
-                                 s);
+                                 c->bad_codes, s);
     });
     if (rc)
         return rc;
@@ -961,6 +967,9 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
     c->meta_cap = round4(F * g.K) + round4(F) + round4(B + 1) + 3 * round4(B) + 4;
     if ((rc = dev_alloc(c, &c->meta_dev, c->meta_cap * 4, ws)))
         return cleanup_fail(rc);
+    if ((rc = dev_alloc(c, (void **)&c->bad_codes, sizeof(unsigned long long), ws)))
+        return cleanup_fail(rc);
+    HIPCHK(c, hipMemset(c->bad_codes, 0, sizeof(unsigned long long)));
     for (int i = 0; i < 2; i++) {
         hipError_t e = hipHostMalloc(&c->pinned[i], c->meta_cap * 4, hipHostMallocDefault);
         if (e != hipSuccess) {
@@ -987,21 +996,21 @@ int codec_close(codec_t *c)
 {
     if (!c)
         return set_err(nullptr, CODEC_EINVAL, "codec_close: NULL codec");
-    hipDeviceSynchronize();
+    (void)hipDeviceSynchronize();
     for (auto &r : c->recs) {
-        hipEventDestroy(r.a);
-        hipEventDestroy(r.b);
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
     }
     for (auto e : c->ev_pool)
-        hipEventDestroy(e);
+        (void)hipEventDestroy(e);
     for (int i = 0; i < 2; i++) {
         if (c->pin_ev[i])
-            hipEventDestroy(c->pin_ev[i]);
+            (void)hipEventDestroy(c->pin_ev[i]);
         if (c->pinned[i])
-            hipHostFree(c->pinned[i]);
+            (void)hipHostFree(c->pinned[i]);
     }
     for (void *p : c->allocs)
-        hipFree(p);
+        (void)hipFree(p);
     delete c;
     return CODEC_OK;
 }
@@ -1079,11 +1088,10 @@ static int check_codes(codec *c, const int32_t *codes, int64_t F, const int32_t 
     return CODEC_OK;
 }
 
-int decode_chunk(codec_t *c, int32_t B, const int32_t *ids, const int32_t *n, const int32_t *codes,
-                 float *pcm, int64_t pcm_capacity, codec_hip_stream stream)
+static int check_step(codec_t *c, int32_t B, const int32_t *ids, const int32_t *n,
+                      const int32_t *codes, float *pcm, int64_t pcm_capacity, bool on_device,
+                      std::vector<int> &slots)
 {
-    if (!c)
-        return set_err(nullptr, CODEC_EINVAL, "decode_chunk: NULL codec");
     if (B < 1 || !ids || !n || !codes || !pcm)
         return fail(c, CODEC_EINVAL,
                     "decode_chunk: B=%d (must be >= 1) and ids, n_frames, codes, pcm non-NULL", B);
@@ -1095,7 +1103,7 @@ int decode_chunk(codec_t *c, int32_t B, const int32_t *ids, const int32_t *n, co
             return fail(c, CODEC_EINVAL, "decode_chunk: n_frames[%d]=%d (must be >= 1)", b, n[b]);
         F += n[b];
     }
-    std::vector<int> slots((size_t)B);
+    slots.assign((size_t)B, 0);
     std::unordered_set<int32_t> seen;
     for (int b = 0; b < B; b++) {
         auto it = c->id2slot.find(ids[b]);
@@ -1113,11 +1121,51 @@ int decode_chunk(codec_t *c, int32_t B, const int32_t *ids, const int32_t *n, co
     if (pcm_capacity < F * c->hop)
         return fail(c, CODEC_EINVAL, "decode_chunk: pcm capacity %lld < %lld samples",
                     (long long)pcm_capacity, (long long)(F * c->hop));
-    int rc = check_codes(c, codes, F, ids, n, B);
+    if (on_device)
+        return CODEC_OK;
+    return check_codes(c, codes, F, ids, n, B);
+}
+
+int decode_chunk(codec_t *c, int32_t B, const int32_t *ids, const int32_t *n, const int32_t *codes,
+                 float *pcm, int64_t pcm_capacity, codec_hip_stream stream)
+{
+    if (!c)
+        return set_err(nullptr, CODEC_EINVAL, "decode_chunk: NULL codec");
+    std::vector<int> slots;
+    int rc = check_step(c, B, ids, n, codes, pcm, pcm_capacity, false, slots);
     if (rc)
         return rc;
     HIPCHK(c, hipSetDevice(c->dev));
     return enqueue_step(c, B, slots.data(), n, codes, pcm, (hipStream_t)stream);
+}
+
+int decode_chunk_device(codec_t *c, int32_t B, const int32_t *ids, const int32_t *n,
+                        const int32_t *codes_dev, float *pcm, int64_t pcm_capacity,
+                        codec_hip_stream stream)
+{
+    if (!c)
+        return set_err(nullptr, CODEC_EINVAL, "decode_chunk_device: NULL codec");
+    std::vector<int> slots;
+    int rc = check_step(c, B, ids, n, codes_dev, pcm, pcm_capacity, true, slots);
+    if (rc)
+        return rc;
+    HIPCHK(c, hipSetDevice(c->dev));
+    return enqueue_step(c, B, slots.data(), n, codes_dev, pcm, (hipStream_t)stream, true);
+}
+
+int codec_device_status(codec_t *c, int64_t *bad)
+{
+    if (!c || !bad)
+        return set_err(c ? &c->err : nullptr, CODEC_EINVAL, "codec_device_status: NULL argument");
+    HIPCHK(c, hipSetDevice(c->dev));
+    HIPCHK(c, hipDeviceSynchronize());
+    unsigned long long v = 0;
+    HIPCHK(c, hipMemcpy(&v, c->bad_codes, sizeof v, hipMemcpyDeviceToHost));
+    HIPCHK(c, hipMemset(c->bad_codes, 0, sizeof v));
+    *bad = (int64_t)v;
+    if (v)
+        return fail(c, CODEC_ERANGE, "%llu out-of-range codes in device-resident steps", v);
+    return CODEC_OK;
 }
 
 int stream_prefill(codec_t *c, int32_t id, const int32_t *codes, int32_t n,

@@ -86,7 +86,8 @@ __device__ __forceinline__ void store8(float *p, const float *v)
 // contiguous [K][E][d_cb] array.
 template <typename CB, typename OUT>
 __global__ __launch_bounds__(256) void rvq_gather_kernel(const CB *cb, const int32_t *codes,
-                                                         int F, int K, int E, int d_cb, OUT *z)
+                                                         int F, int K, int E, int d_cb, OUT *z,
+                                                         unsigned long long *bad)
 {
     const int per_frame = d_cb / 8;
     long g = (long)blockIdx.x * 256 + threadIdx.x;
@@ -98,6 +99,11 @@ __global__ __launch_bounds__(256) void rvq_gather_kernel(const CB *cb, const int
     const int32_t *cf = codes + f * K;
     for (int k = 0; k < K; k++) {
         int e = cf[k];
+        if ((unsigned)e >= (unsigned)E) {  // only reachable with device-resident codes
+            if (d == 0)
+                atomicAdd(bad, 1ull);
+            e = 0;
+        }
         float v[8];
         load8(cb + ((long)k * E + e) * d_cb + d, v);
 #pragma unroll
@@ -199,7 +205,8 @@ hipError_t launch_halo_save(const HaloTable &t, void *state, const StepMeta &m, 
 }
 
 hipError_t launch_rvq_gather(const void *cb, int cb_dtype, const int32_t *codes, int F, int K,
-                             int E, int d_cb, void *z, int out_dtype, hipStream_t st)
+                             int E, int d_cb, void *z, int out_dtype, unsigned long long *bad,
+                             hipStream_t st)
 {
     if (F <= 0)
         return hipSuccess;
@@ -207,16 +214,16 @@ hipError_t launch_rvq_gather(const void *cb, int cb_dtype, const int32_t *codes,
     dim3 grid((unsigned)((threads + 255) / 256));
     if (cb_dtype == 1 && out_dtype == 1)
         hipLaunchKernelGGL((rvq_gather_kernel<uint16_t, half_t>), grid, dim3(256), 0, st,
-                           (const uint16_t *)cb, codes, F, K, E, d_cb, (half_t *)z);
+                           (const uint16_t *)cb, codes, F, K, E, d_cb, (half_t *)z, bad);
     else if (cb_dtype == 0 && out_dtype == 0)
         hipLaunchKernelGGL((rvq_gather_kernel<float, float>), grid, dim3(256), 0, st,
-                           (const float *)cb, codes, F, K, E, d_cb, (float *)z);
+                           (const float *)cb, codes, F, K, E, d_cb, (float *)z, bad);
     else if (cb_dtype == 1 && out_dtype == 0)
         hipLaunchKernelGGL((rvq_gather_kernel<uint16_t, float>), grid, dim3(256), 0, st,
-                           (const uint16_t *)cb, codes, F, K, E, d_cb, (float *)z);
+                           (const uint16_t *)cb, codes, F, K, E, d_cb, (float *)z, bad);
     else
         hipLaunchKernelGGL((rvq_gather_kernel<float, half_t>), grid, dim3(256), 0, st,
-                           (const float *)cb, codes, F, K, E, d_cb, (half_t *)z);
+                           (const float *)cb, codes, F, K, E, d_cb, (half_t *)z, bad);
     return hipGetLastError();
 }
 

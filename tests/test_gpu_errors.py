@@ -88,3 +88,25 @@ def test_slots_exhaust_and_close_then_reopen(small_codec):
     assert np.array_equal(x, y)
     for i in (new, ids[1], ids[2]):
         c.stream_close(i)
+
+
+def test_device_resident_codes_match_host_codes_and_count_bad_codes(small_codec):
+    cfg, c = small_codec
+    print("case device-resident codes", flush=True)
+    a = c.stream_open()
+    b = c.stream_open()
+    codes = RI.stream_codes(cfg, 4, 7)
+    x = decode(c, [a], [7], codes)
+    pcm = torch.empty(7 * c.hop, dtype=torch.float32, device="cuda")
+    c.decode_chunk_device([b], [7], torch.from_numpy(codes).cuda(), pcm)
+    assert np.array_equal(x, pcm.cpu().numpy())
+    assert c.device_status() == 0
+    bad = codes.copy()
+    bad[2, 1] = 2150
+    bad[5, 0] = -3
+    c.decode_chunk_device([b], [7], torch.from_numpy(bad).cuda(), pcm)
+    e = err_of(c.device_status)
+    assert e.code == snr.CODEC_ERANGE and "2 out-of-range" in str(e)
+    assert c.device_status() == 0  # the count resets
+    c.stream_close(a)
+    c.stream_close(b)
