@@ -91,7 +91,14 @@ typedef struct {
     int32_t weight_dtype; /* CODEC_DTYPE_F32 or CODEC_DTYPE_BF16 */
     int32_t max_streams;
     int32_t max_frames_per_call;
+    int32_t flags; /* CODEC_FLAG_* */
 } codec_cfg;
+
+/* Run every layer as its own launch instead of the fused per-stage kernels
+ * (same arithmetic, bit-identical output; for testing and comparison), for
+ * all stages or for upsample stage i only. */
+#define CODEC_FLAG_PER_LAYER 1
+#define CODEC_FLAG_PER_LAYER_STAGE(i) (1 << (8 + (i)))
 
 typedef struct {
     int32_t hop;                 /* PCM samples per frame */
@@ -184,6 +191,13 @@ int codec_device_status(codec_t *codec, int64_t *bad_codes);
  * the codes: [sum n][d_lat].  dst is device memory with capacity elements. */
 int codec_debug_capture(codec_t *codec, int32_t what, float *dst, int64_t capacity,
                         codec_hip_stream stream);
+
+/* Copies the state slot of an open stream to host memory after waiting for
+ * the codec's device work: the conv left contexts ([H][C] per layer, in the
+ * compute type, in layer order) followed by nothing else.  *bytes_out
+ * receives the slot size; dst may be NULL to query it. */
+int codec_debug_read_state(codec_t *codec, int32_t stream_id, void *dst, int64_t capacity,
+                           int64_t *bytes_out);
 
 /* Per-kernel-class device time of the decode steps since the last reset,
  * measured with HIP events on the decode stream while profiling is on.

@@ -21,6 +21,7 @@ CODEC_ENOSLOT, CODEC_ETOOBIG, CODEC_ENOMEM, CODEC_EHIP = 5, 6, 7, 8
 DTYPE_F32, DTYPE_BF16, DTYPE_F16 = 0, 1, 2
 ACT = {"snake": 0, "elu": 1}
 CAPTURE_LATENT, CAPTURE_DEC_INPUT = 0, 1
+FLAG_PER_LAYER = 1
 MAX_STAGES = 8
 
 ERROR_NAMES = {1: "EINVAL", 2: "ESTREAM", 3: "EDUP", 4: "ERANGE", 5: "ENOSLOT", 6: "ETOOBIG",
@@ -44,7 +45,8 @@ class codec_cfg(C.Structure):
                 ("sample_rate", C.c_int32), ("act", C.c_int32), ("final_tanh", C.c_int32),
                 ("tf_layers", C.c_int32), ("tf_heads", C.c_int32), ("tf_head_dim", C.c_int32),
                 ("tf_window", C.c_int32), ("tf_mlp", C.c_int32), ("weight_dtype", C.c_int32),
-                ("max_streams", C.c_int32), ("max_frames_per_call", C.c_int32)]
+                ("max_streams", C.c_int32), ("max_frames_per_call", C.c_int32),
+                ("flags", C.c_int32)]
 
 
 class codec_info_t(C.Structure):
@@ -61,7 +63,7 @@ _lib = None
 
 EXPORTS = ["codec_open", "codec_close", "codec_info", "codec_last_error", "stream_open",
            "stream_close", "stream_prefill", "decode_chunk", "decode_chunk_device",
-           "codec_device_status", "codec_debug_capture",
+           "codec_device_status", "codec_debug_capture", "codec_debug_read_state",
            "codec_profile_enable", "codec_profile_read", "codec_chunk_plan",
            "codec_resolve_initial_chunk_frames"]
 
@@ -90,6 +92,8 @@ def lib():
                                       C.c_void_p, C.c_int64, C.c_void_p]
     L.codec_device_status.argtypes = [C.c_void_p, C.POINTER(C.c_int64)]
     L.codec_debug_capture.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int64, C.c_void_p]
+    L.codec_debug_read_state.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int64,
+                                         C.POINTER(C.c_int64)]
     L.codec_profile_enable.argtypes = [C.c_void_p, C.c_int32]
     L.codec_profile_read.argtypes = [C.c_void_p, C.c_int32, C.POINTER(C.c_char_p),
                                      C.POINTER(C.c_double), C.POINTER(C.c_int64),
@@ -142,6 +146,8 @@ def make_cfg(cfg: dict) -> codec_cfg:
     c.weight_dtype = DTYPE_BF16 if cfg["weight_dtype"] == "bf16" else DTYPE_F32
     c.max_streams = cfg["max_streams"]
     c.max_frames_per_call = cfg["max_frames_per_call"]
+    c.flags = (FLAG_PER_LAYER if cfg.get("per_layer", False) else 0) | \
+        sum(1 << (8 + i) for i in cfg.get("per_layer_stages", ()))
     return c
 
 
@@ -248,6 +254,15 @@ class Codec:
     def debug_capture(self, what: int, dst, stream=None):
         _check(lib().codec_debug_capture(self._h, what, C.c_void_p(dst.data_ptr()), dst.numel(),
                                          _stream_handle(stream)), self._h)
+
+    def read_state(self, sid: int) -> np.ndarray:
+        """The stream's state slot (conv left contexts) as raw bytes."""
+        n = C.c_int64()
+        _check(lib().codec_debug_read_state(self._h, int(sid), None, 0, C.byref(n)), self._h)
+        buf = np.empty(n.value, np.uint8)
+        _check(lib().codec_debug_read_state(self._h, int(sid), buf.ctypes.data, buf.size,
+                                            C.byref(n)), self._h)
+        return buf
 
     def profile_enable(self, on: bool = True):
         _check(lib().codec_profile_enable(self._h, int(on)), self._h)

@@ -18,7 +18,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsnrvq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "kernels_conv.hip", "kernels_misc.hip", "kernels_tf.hip"]
+SOURCES = ["api.cpp", "kernels_conv.hip", "kernels_misc.hip", "kernels_tf.hip",
+           "kernels_stage.hip"]
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Wno-unused-function", "-I" + INCLUDE, "-I" + CSRC,
           # no packed-fp32 instructions anywhere in device code

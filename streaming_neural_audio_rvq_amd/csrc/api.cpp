@@ -81,6 +81,7 @@ struct codec {
     int rate[CODEC_MAX_STAGES + 1]{};
     int left_ctx = 0;
     int maxF = 0, maxB = 0;
+    int n_cu = 256;  // compute units of the device
 
     std::vector<void *> allocs;
     void *cb = nullptr;
@@ -106,7 +107,10 @@ struct codec {
 
     void *state = nullptr;
     int64_t slot_elems = 0;
-    HaloTable halo{};
+    HaloTable halo{};       // filled before every step
+    HaloTable halo_save{};  // saved after it (fused stages write their own)
+    int fuse_T[CODEC_MAX_STAGES]{};  // output rows per tile of a fused stage, 0 = per-layer
+    int64_t off_a1[CODEC_MAX_STAGES]{}, off_a2[CODEC_MAX_STAGES]{}, off_ao = 0;
 
     void *meta_dev = nullptr;
     size_t meta_cap = 0;  // int32 elements
@@ -278,12 +282,16 @@ int upload_f32(codec *c, const std::vector<float> &v, float **dst)
     return CODEC_OK;
 }
 
+// Snake parameters as the kernels use them: alpha / 2pi (the hardware sine
+// takes revolutions) and 1 / alpha, both rounded once from fp64.
 int upload_act(codec *c, const std::vector<float> &alpha, ActP *a)
 {
-    std::vector<float> inv(alpha.size());
-    for (size_t i = 0; i < alpha.size(); i++)
-        inv[i] = 1.0f / alpha[i];
-    int rc = upload_f32(c, alpha, &a->alpha);
+    std::vector<float> rev(alpha.size()), inv(alpha.size());
+    for (size_t i = 0; i < alpha.size(); i++) {
+        rev[i] = (float)((double)alpha[i] / (2.0 * M_PI));
+        inv[i] = (float)(1.0 / (double)alpha[i]);
+    }
+    int rc = upload_f32(c, rev, &a->alpha);
     if (rc)
         return rc;
     return upload_f32(c, inv, &a->ialpha);
@@ -432,6 +440,54 @@ int run_conv(codec *c, const char *name, const ConvArgs &a, hipStream_t s)
 }
 
 size_t round4(size_t n) { return (n + 3) & ~(size_t)3; }
+
+// Stage i as one fused kernel (ConvT + both residual units [+ final conv]).
+int enqueue_fused_stage(codec *c, int i, int F, const StepMeta &m, float *pcm, hipStream_t s)
+{
+    const bool fin = i == c->S - 1;
+    StageArgs a{};
+    a.aT = (const half_t *)c->aT[i];
+    a.WT = (const half_t *)c->convT[i].Wt;
+    a.bT = c->convT[i].bias;
+    for (int j = 0; j < 2; j++) {
+        a.W7[j] = (const half_t *)c->conv7[i][j].Wt;
+        a.b7[j] = c->conv7[i][j].bias;
+        a.W1[j] = (const half_t *)c->conv1[i][j].Wt;
+        a.b1[j] = c->conv1[i][j].bias;
+        a.al1[j] = c->a_ru1[i][j].alpha;
+        a.ial1[j] = c->a_ru1[i][j].ialpha;
+        a.al2[j] = c->a_ru2[i][j].alpha;
+        a.ial2[j] = c->a_ru2[i][j].ialpha;
+    }
+    const ActP &nx = fin ? c->a_out : c->a_stage[i + 1];
+    a.al_next = nx.alpha;
+    a.ial_next = nx.ialpha;
+    a.a1_ext = (const half_t *)c->a1[i];
+    a.a2_ext = (const half_t *)c->a2[i];
+    a.ao_ext = (const half_t *)c->a_outb;
+    a.next = fin ? nullptr : (half_t *)c->aT[i + 1];
+    a.pcm = pcm;
+    a.w_out = c->out_w;
+    a.b_out = c->out_b;
+    a.final_tanh = c->cfg.final_tanh;
+    a.state = (half_t *)c->state;
+    a.slot_elems = c->slot_elems;
+    a.off_a1 = c->off_a1[i];
+    a.off_a2 = c->off_a2[i];
+    a.off_ao = c->off_ao;
+    a.frame_stream = m.frame_stream;
+    a.cu = m.cu;
+    a.slot = m.slot;
+    a.r_in = c->rate[i];
+    a.r_out = c->rate[i + 1];
+    a.act = c->cfg.act == CODEC_ACT_ELU ? ACT_ELU : ACT_SNAKE;
+    a.n_cu = c->n_cu;
+    char nm[32];
+    snprintf(nm, sizeof nm, "s%d.fused", i);
+    return timed(c, nm, (int64_t)F * c->rate[i + 1], s, [&] {
+        return launch_stage_fused(a, c->ch[i + 1], c->cfg.strides[i], c->fuse_T[i], fin, F, s);
+    });
+}
 
 // Windowed causal transformer over the F new frames of this step (pre-norm
 // layers; the KV ring holds every stream's last W-1 frames per layer).
@@ -584,6 +640,11 @@ int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int3
     char nm[64];
     for (int i = 0; i < c->S; i++) {
         int ri = c->rate[i], ro = c->rate[i + 1];
+        if (c->fuse_T[i]) {
+            if ((rc = enqueue_fused_stage(c, i, F, m, pcm, s)))
+                return rc;
+            continue;
+        }
         a = conv_args(c, c->convT[i], c->aT[i], 1, ri, F * ri, m);
         a.out32 = c->x;
         a.out16 = c->a1[i];
@@ -623,14 +684,16 @@ int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int3
                 return rc;
         }
     }
-    rc = timed(c, "final_conv", (int64_t)F * c->hop, s, [&] {
-        return launch_final_conv(c->a_outb, c->dtype, 6, c->ch[c->S], c->hop, c->out_w, c->out_b,
-                                 g.final_tanh, m.frame_stream, F * c->hop, pcm, s);
-    });
-    if (rc)
-        return rc;
+    if (!c->fuse_T[c->S - 1]) {
+        rc = timed(c, "final_conv", (int64_t)F * c->hop, s, [&] {
+            return launch_final_conv(c->a_outb, c->dtype, 6, c->ch[c->S], c->hop, c->out_w,
+                                     c->out_b, g.final_tanh, m.frame_stream, F * c->hop, pcm, s);
+        });
+        if (rc)
+            return rc;
+    }
     rc = timed(c, "halo_save", B, s,
-               [&] { return launch_halo_save(c->halo, c->state, m, B, s); });
+               [&] { return launch_halo_save(c->halo_save, c->state, m, B, s); });
     if (rc)
         return rc;
 
@@ -782,6 +845,12 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
     codec *c = new codec();
     c->cfg = *cfg;
     c->dev = dev;
+    {
+        int ncu = 0;
+        if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            ncu > 0)
+            c->n_cu = ncu;
+    }
     c->dtype = cfg->weight_dtype == CODEC_DTYPE_BF16 ? 1 : 0;
     c->esz = c->dtype ? 2 : 4;
     c->S = cfg->n_stages;
@@ -954,12 +1023,35 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
     add(c->u_ext, 6, g.d_lat, 1);
     for (int i = 0; i < c->S; i++) {
         add(c->aT[i], 1, ch[i], c->rate[i]);
+        c->off_a1[i] = off;
         add(c->a1[i], 6, ch[i + 1], c->rate[i + 1]);
+        c->off_a2[i] = off;
         add(c->a2[i], 18, ch[i + 1], c->rate[i + 1]);
     }
+    c->off_ao = off;
     add(c->a_outb, 6, ch[c->S], hop);
     c->slot_elems = off;
     t.slot_elems = off;
+    // fused stages (fp16 path): their residual-unit and final-conv left
+    // contexts are written by the stage kernel itself, not by the halo save
+    for (int i = 0; i < c->S; i++)
+        c->fuse_T[i] = (c->dtype && g.act == CODEC_ACT_SNAKE && !(g.flags & CODEC_FLAG_PER_LAYER) &&
+                        !(g.flags & CODEC_FLAG_PER_LAYER_STAGE(i)))
+                           ? stage_fused_tile(ch[i + 1], g.strides[i], c->rate[i + 1], i == c->S - 1)
+                           : 0;
+    HaloTable &sv = c->halo_save;
+    sv.elem_bytes = t.elem_bytes;
+    sv.slot_elems = t.slot_elems;
+    for (int k = 0; k < t.n; k++) {
+        const void *e = t.l[k].ext;
+        bool skip = false;
+        for (int i = 0; i < c->S; i++)
+            if (c->fuse_T[i] && (e == c->a1[i] || e == c->a2[i] ||
+                                 (i == c->S - 1 && e == c->a_outb)))
+                skip = true;
+        if (!skip)
+            sv.l[sv.n++] = t.l[k];
+    }
     if ((rc = dev_alloc(c, &c->state, (size_t)c->maxB * off * es, ws)))
         return cleanup_fail(rc);
 
@@ -1212,6 +1304,28 @@ int codec_debug_capture(codec_t *c, int32_t what, float *dst, int64_t capacity,
     HIPCHK(c, launch_unextend(tf_latent ? c->u16 : c->u_ext, c->dtype, tf_latent ? 0 : 6,
                               c->cfg.d_lat, 1, c->last_meta.frame_stream, c->lastF, dst,
                               (hipStream_t)stream));
+    return CODEC_OK;
+}
+
+int codec_debug_read_state(codec_t *c, int32_t id, void *dst, int64_t capacity,
+                           int64_t *bytes_out)
+{
+    if (!c || !bytes_out)
+        return set_err(c ? &c->err : nullptr, CODEC_EINVAL, "codec_debug_read_state: NULL argument");
+    auto it = c->id2slot.find(id);
+    if (it == c->id2slot.end())
+        return fail(c, CODEC_ESTREAM, "codec_debug_read_state: stream %d is not open", id);
+    const int64_t bytes = c->slot_elems * c->esz;
+    *bytes_out = bytes;
+    if (!dst)
+        return CODEC_OK;
+    if (capacity < bytes)
+        return fail(c, CODEC_EINVAL, "codec_debug_read_state: capacity %lld < %lld",
+                    (long long)capacity, (long long)bytes);
+    HIPCHK(c, hipSetDevice(c->dev));
+    HIPCHK(c, hipDeviceSynchronize());
+    HIPCHK(c, hipMemcpy(dst, (char *)c->state + (size_t)it->second * bytes, (size_t)bytes,
+                        hipMemcpyDeviceToHost));
     return CODEC_OK;
 }
 

@@ -20,6 +20,35 @@ typedef _Float16 half_t;
 
 enum Act : int { ACT_NONE = 0, ACT_SNAKE = 1, ACT_ELU = 2, ACT_GELU = 3 };
 
+// Snake, applied once per element in fp32: v + sin^2(alpha v) / alpha.
+// alpha_rev = alpha / 2pi (precomputed per channel), so alpha v in
+// revolutions is one multiply; it is reduced to [-0.5, 0.5] and fed to the
+// hardware sine, which takes revolutions.  Every Snake evaluation of the
+// library goes through this one function, so fused and per-layer paths
+// round identically.
+// The rounding steps are spelled out (no contraction) so that every caller
+// gets the same bits whatever the compiler does around it.
+__device__ __forceinline__ float snrvq_snake(float v, float alpha_rev, float inv_alpha)
+{
+#pragma clang fp contract(off)
+    float r = alpha_rev * v;
+    r = r - __builtin_rintf(r);
+    const float s = __builtin_amdgcn_sinf(r);
+    const float s2 = s * s;
+    return __builtin_fmaf(s2, inv_alpha, v);
+}
+__device__ __forceinline__ float snrvq_elu(float v) { return v > 0.f ? v : __expf(v) - 1.f; }
+
+// fp32 -> fp16 (round to nearest even) of a materialized fp32 value.  The
+// empty asm keeps the compiler from folding the conversion into the FMA that
+// produced x (v_fma_mixlo_f16 rounds once, straight to fp16), so every
+// kernel rounds the same way: to fp32 first, then to fp16.
+__device__ __forceinline__ half_t snrvq_f16(float x)
+{
+    __asm__ volatile("" : "+v"(x));
+    return (half_t)x;
+}
+
 // One implicit-GEMM convolution (also transposed conv in polyphase form,
 // and plain GEMMs as k = 1 convs).
 //   out[m, n] = bias[n % Cout] + sum_{tap, c} A_ext[row(m) - (taps-1-tap) dil, c] * Wt[n, tap Cin + c]
@@ -93,6 +122,34 @@ hipError_t launch_final_conv(const void *A, int dtype, int A_H, int C, int rate,
 // Copies packed rows out of an extended buffer as fp32 [M][C].
 hipError_t launch_unextend(const void *ext, int dtype, int H, int C, int rate,
                            const int32_t *frame_stream, int M, float *dst, hipStream_t st);
+
+// ---- fused upsample stage (kernels_stage.hip), fp16 operands only ----
+struct StageArgs {
+    const half_t *aT;                 // ConvT input, extended with 1 halo row, width 2C
+    const half_t *WT;                 // polyphase ConvT weights [S C][2 * 2C]
+    const float *bT;                  // [C]
+    const half_t *W7[2], *W1[2];      // residual units: [C][7C], [C][C]
+    const float *b7[2], *b1[2];
+    const float *al1[2], *ial1[2];    // activation of each residual unit's input
+    const float *al2[2], *ial2[2];    // activation inside each residual unit
+    const float *al_next, *ial_next;  // activation of the stage output
+    const half_t *a1_ext, *a2_ext, *ao_ext;  // halo sources (extended, H = 6, 18, 6)
+    half_t *next;                     // next stage's ConvT input (extended, 1 halo row)
+    float *pcm;                       // final stage: PCM [F hop]
+    const float *w_out;               // final conv [C][7]
+    float b_out;
+    int final_tanh;
+    half_t *state;                    // slot array, slot_elems per slot
+    long slot_elems, off_a1, off_a2, off_ao;
+    const int32_t *frame_stream, *cu, *slot;
+    int r_in, r_out, act, tiles_per_frame, n_tiles;
+    int n_cu;                         // compute units of the device
+};
+// Output rows per tile of an instantiated fused stage, or 0 when the shape
+// has none (then the per-layer path runs).
+int stage_fused_tile(int C, int S, int r_out, bool final_stage);
+hipError_t launch_stage_fused(const StageArgs &a, int C, int S, int T, bool final_stage, int F,
+                              hipStream_t st);
 
 // ---- transformer ops (kernels_tf.hip) ----
 #define SNRVQ_MAX_WINDOW 32  // keys per query, including its own frame

@@ -46,12 +46,10 @@ struct Traits<float> {
 
 __device__ __forceinline__ float act_fn(float v, int act, float a, float ia)
 {
-    if (act == ACT_SNAKE) {
-        float s = sinf(a * v);
-        return v + s * s * ia;
-    }
+    if (act == ACT_SNAKE)
+        return snrvq_snake(v, a, ia);
     if (act == ACT_ELU)
-        return v > 0.f ? v : expm1f(v);
+        return snrvq_elu(v);
     if (act == ACT_GELU)
         return 0.5f * v * (1.f + erff(v * 0.7071067811865475f));
     return v;
@@ -62,7 +60,7 @@ __device__ __forceinline__ void store4(T *dst, f4 v);
 template <>
 __device__ __forceinline__ void store4<half_t>(half_t *dst, f4 v)
 {
-    h4 h = {(half_t)v[0], (half_t)v[1], (half_t)v[2], (half_t)v[3]};
+    h4 h = {snrvq_f16(v[0]), snrvq_f16(v[1]), snrvq_f16(v[2]), snrvq_f16(v[3])};
     *(h4 *)dst = h;
 }
 template <>

@@ -72,7 +72,7 @@ __device__ __forceinline__ void store8(half_t *p, const float *v)
     h8 h;
 #pragma unroll
     for (int i = 0; i < 8; i++)
-        h[i] = (half_t)v[i];
+        h[i] = snrvq_f16(v[i]);
     *(h8 *)p = h;
 }
 __device__ __forceinline__ void store8(float *p, const float *v)

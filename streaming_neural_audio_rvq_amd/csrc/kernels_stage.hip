@@ -1,0 +1,445 @@
+// kernels_stage.hip -- one kernel per late upsample stage of the conv
+// decoder: ConvTranspose1d -> residual unit (dilation 1) -> residual unit
+// (dilation 3) [-> final conv to PCM, for the last stage], over time tiles
+// of one stream.  Snake activations only (ELU decoders take the per-layer
+// path).
+//
+// The per-layer path moves every intermediate through HBM (at the last stage
+// of the Qwen-shaped decoder about 1.1 KB per output row).  Here a tile of T
+// output rows recomputes the left halo its residual units need (6 rows for
+// the dilation-1 conv, 18 for the dilation-3 conv, 6 more when the final
+// conv is fused) and keeps the fp32 residual stream x, the activated conv
+// inputs and the residual-unit intermediate in LDS.  HBM sees the stage's
+// fp16 input rows and its fp16 output rows (or the PCM) only.
+//
+// Arithmetic is the per-layer path's, operation for operation: the same
+// fp16 operands (each activation applied once, then rounded), the same K
+// order (tap-major, channel-minor in steps of 32) on v_mfma_f32_16x16x32_f16,
+// the same fp32 epilogues, so both paths give bit-identical PCM.
+//
+// Left context: at a stream's first tile the rows before the chunk come
+// from the halo rows that the step's halo fill wrote into the (otherwise
+// unused) extended buffers of the per-layer path; the stream's last tile
+// writes the new left contexts straight into its state slot.
+//
+// Work split (8 waves): ConvT work items of 16 input rows x up to 8 column
+// blocks; residual-unit row blocks of 16 output rows, RB blocks per wave in
+// flight so each weight fragment feeds RB MFMAs.  The dilated conv reads its
+// 7 taps as row shifts of the LDS tile.  Each lane owns the same NB = C/16
+// channels in every MFMA output block, so all per-channel parameters (biases,
+// Snake alpha/2pi and 1/alpha) live in registers for the whole kernel.  With
+// WL the stage's weights also sit in LDS and one persistent work-group per
+// CU walks the tiles.
+#include "internal.h"
+
+namespace snrvq {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ f4 mma(h8 a, h8 b, f4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Per-lane channel parameters: index [param][n] is channel n * 16 + lane % 16.
+enum Prm {
+    P_BT = 0,                                      // ConvT bias
+    P_A1R0, P_A1I0, P_B70, P_A2R0, P_A2I0, P_B10,  // residual unit 0
+    P_A1R1, P_A1I1, P_B71, P_A2R1, P_A2I1, P_B11,  // residual unit 1
+    P_ANR, P_ANI,                                  // activation of the stage output
+    P_COUNT
+};
+
+// One residual unit over output rows [lo, hi): conv7 (dilation D) of the
+// activated input in LDS (row of time t at in + (t - in_t0) * CP), Snake,
+// 1x1 conv, + bias + residual x (LDS fp32, row of t at xs + (t - x_t0) * C);
+// epi(t, c, n, v) receives every result (n = channel block of c).
+template <int C, int D, int RB, int U, class Epi>
+__device__ __forceinline__ void residual_unit(const half_t *in, int in_t0, int lo, int hi,
+                                              const half_t *W7, int ld7, const half_t *W1,
+                                              int ld1, const float (&pr)[P_COUNT][C / 16],
+                                              const float *xs, int x_t0, half_t *hsw, Epi epi)
+{
+    constexpr int CP = C + 8;
+    constexpr int NB = C / 16;
+    constexpr int K7 = 7 * C;
+    constexpr int NW = 8;
+    constexpr int PB7 = U ? P_B71 : P_B70, PA2R = U ? P_A2R1 : P_A2R0,
+                  PA2I = U ? P_A2I1 : P_A2I0, PB1 = U ? P_B11 : P_B10;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int nblk = (hi - lo + 15) / 16;
+    for (int rb0 = wave; rb0 < nblk; rb0 += NW * RB) {
+        f4 acc[RB][NB];
+#pragma unroll
+        for (int j = 0; j < RB; j++)
+#pragma unroll
+            for (int n = 0; n < NB; n++)
+                acc[j][n] = f4{0.f, 0.f, 0.f, 0.f};
+        int rowoff[RB];
+#pragma unroll
+        for (int j = 0; j < RB; j++) {
+            int t = lo + (rb0 + j * NW) * 16 + l16;
+            t = t < hi ? t : hi - 1;
+            rowoff[j] = (t - in_t0) * CP + lg * 8;
+        }
+#pragma unroll 2
+        for (int k0 = 0; k0 < K7; k0 += 32) {
+            const int tap = k0 / C, c0 = k0 - tap * C;
+            const int sh = (tap - 6) * D * CP + c0;
+            h8 bf[NB];
+#pragma unroll
+            for (int n = 0; n < NB; n++)
+                bf[n] = *(const h8 *)(W7 + (n * 16 + l16) * ld7 + k0 + lg * 8);
+#pragma unroll
+            for (int j = 0; j < RB; j++) {
+                if (rb0 + j * NW < nblk) {
+                    h8 af = *(const h8 *)(in + rowoff[j] + sh);
+#pragma unroll
+                    for (int n = 0; n < NB; n++)
+                        acc[j][n] = mma(af, bf[n], acc[j][n]);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < RB; j++) {
+            const int blk = rb0 + j * NW;
+            if (blk >= nblk)
+                continue;
+            // Snake(conv7 + b7) -> fp16 rows of this wave's scratch
+#pragma unroll
+            for (int n = 0; n < NB; n++) {
+                const int c = n * 16 + l16;
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    hsw[(lg * 4 + e) * CP + c] = snrvq_f16(snrvq_snake(
+                        acc[j][n][e] + pr[PB7][n], pr[PA2R][n], pr[PA2I][n]));
+            }
+            wave_lds_sync();
+            f4 a2c[NB];
+#pragma unroll
+            for (int n = 0; n < NB; n++)
+                a2c[n] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c0 = 0; c0 < C; c0 += 32) {
+                h8 af = *(const h8 *)(hsw + l16 * CP + c0 + lg * 8);
+#pragma unroll
+                for (int n = 0; n < NB; n++) {
+                    h8 bf = *(const h8 *)(W1 + (n * 16 + l16) * ld1 + c0 + lg * 8);
+                    a2c[n] = mma(af, bf, a2c[n]);
+                }
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int n = 0; n < NB; n++) {
+                const int c = n * 16 + l16;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int t = lo + blk * 16 + lg * 4 + e;
+                    if (t < hi)
+                        epi(t, c, n, a2c[n][e] + pr[PB1][n] + xs[(t - x_t0) * C + c]);
+                }
+            }
+        }
+    }
+}
+
+template <int C, int S, int T, bool FINAL, bool WL>
+__global__ __launch_bounds__(512) void stage_kernel(StageArgs p)
+{
+    constexpr int E = FINAL ? 6 : 0;
+    constexpr int HX = S * ((24 + E + S - 1) / S);  // ConvT rows recomputed before t0
+    constexpr int NX = T + HX;                      // a1 rows: [t0 - HX, t0 + T)
+    constexpr int NR = T + 18 + E;                  // x and a2 rows: [t0 - 18 - E, t0 + T)
+    constexpr int CP = C + 8;
+    constexpr int NW = 8;
+    constexpr int NB = C / 16;
+    constexpr int RB = C >= 128 ? 2 : 4;
+    constexpr int CIN = 2 * C;
+    constexpr int NT = S * C, KT = 2 * CIN, NBT = NT / 16;
+    // ConvT column blocks per work item: the largest divisor of NBT <= 8
+    constexpr int NG = NBT % 8 == 0 ? 8 : NBT % 6 == 0 ? 6 : NBT % 4 == 0 ? 4 : NBT % 2 == 0 ? 2 : 1;
+    constexpr int NGR = NBT / NG;
+    static_assert(T % S == 0 && NT % 16 == 0 && C % 32 == 0, "shape");
+
+    __shared__ __attribute__((aligned(16))) float xs[NR * C];
+    __shared__ __attribute__((aligned(16))) half_t a1s[NX * CP];  // a1, then a_out (FINAL)
+    __shared__ __attribute__((aligned(16))) half_t a2s[NR * CP];
+    __shared__ __attribute__((aligned(16))) half_t hs[NW * 16 * CP];
+    constexpr int LDT = KT + 8, LD7 = 7 * C + 8, LD1 = C + 8;
+    constexpr int WBYTES = WL ? 2 * (NT * LDT + 2 * C * LD7 + 2 * C * LD1) : 16;
+    __shared__ __attribute__((aligned(16))) char wsm[WBYTES];
+    __shared__ float wout_s[FINAL ? 7 * C : 1];  // final conv weights, [tap][channel]
+    half_t *const wTs = (half_t *)wsm;
+    half_t *const w7s = wTs + NT * LDT;
+    half_t *const w1s = w7s + 2 * C * LD7;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+
+    // ---- per-lane channel parameters, for the kernel's lifetime
+    float pr[P_COUNT][NB];
+    {
+        const float *src[P_COUNT] = {p.bT,      p.al1[0], p.ial1[0], p.b7[0], p.al2[0],
+                                     p.ial2[0], p.b1[0],  p.al1[1], p.ial1[1], p.b7[1],
+                                     p.al2[1],  p.ial2[1], p.b1[1],  p.al_next, p.ial_next};
+#pragma unroll
+        for (int k = 0; k < P_COUNT; k++)
+#pragma unroll
+            for (int n = 0; n < NB; n++)
+                pr[k][n] = src[k][n * 16 + l16];
+    }
+    if (WL) {
+        auto copy = [&](half_t *dst, int ld, const half_t *src, int rows, int cols) {
+            const int cpr = cols / 8;
+            for (int i = tid; i < rows * cpr; i += 512) {
+                const int r = i / cpr, c8 = (i - r * cpr) * 8;
+                *(h8 *)(dst + r * ld + c8) = *(const h8 *)(src + (long)r * cols + c8);
+            }
+        };
+        copy(wTs, LDT, p.WT, NT, KT);
+        for (int j = 0; j < 2; j++) {
+            copy(w7s + j * C * LD7, LD7, p.W7[j], C, 7 * C);
+            copy(w1s + j * C * LD1, LD1, p.W1[j], C, C);
+        }
+    }
+    if (FINAL) {
+        for (int i = tid; i < 7 * C; i += 512) {
+            const int c = i / 7, j = i - c * 7;  // input layout [C][7]
+            wout_s[j * C + c] = p.w_out[i];
+        }
+    }
+    const half_t *const WT = WL ? wTs : p.WT;
+    const int ldT = WL ? LDT : KT;
+    const half_t *const W7a = WL ? w7s : p.W7[0];
+    const half_t *const W7b = WL ? w7s + C * LD7 : p.W7[1];
+    const half_t *const W1a = WL ? w1s : p.W1[0];
+    const half_t *const W1b = WL ? w1s + C * LD1 : p.W1[1];
+    const int ld7 = WL ? LD7 : 7 * C, ld1 = WL ? LD1 : C;
+    __syncthreads();  // weights (WL) and final-conv weights are in LDS
+
+    for (int g = blockIdx.x; g < p.n_tiles; g += gridDim.x) {
+        if (g != (int)blockIdx.x)
+            __syncthreads();  // the previous tile's LDS reads are done
+        const int f = g / p.tiles_per_frame;
+        const int b = p.frame_stream[f];
+        const int cu0 = p.cu[b];
+        const int rows_b = (p.cu[b + 1] - cu0) * p.r_out;
+        const int t0 = (g - cu0 * p.tiles_per_frame) * T;
+        const bool first = t0 == 0, last = t0 + T == rows_b;
+        half_t *hsw = hs + wave * 16 * CP;
+        half_t *slot_state = p.state + (long)p.slot[b] * p.slot_elems;
+
+        // ---- left context of a stream's first tile (written by the halo fill)
+        if (first) {
+            const half_t *s1 = p.a1_ext + ((long)b * 6 + (long)cu0 * p.r_out) * C;
+            for (int i = tid; i < 6 * C / 8; i += 512) {
+                int r = i / (C / 8), c8 = (i - r * (C / 8)) * 8;
+                *(h8 *)(a1s + (HX - 6 + r) * CP + c8) = *(const h8 *)(s1 + r * C + c8);
+            }
+            const half_t *s2 = p.a2_ext + ((long)b * 18 + (long)cu0 * p.r_out) * C;
+            for (int i = tid; i < 18 * C / 8; i += 512) {
+                int r = i / (C / 8), c8 = (i - r * (C / 8)) * 8;
+                *(h8 *)(a2s + (E + r) * CP + c8) = *(const h8 *)(s2 + r * C + c8);
+            }
+        }
+
+        // ---- phase 1: transposed conv of input rows [qlo, qhi) -> x, a1
+        {
+            const int q0 = t0 / S;
+            const int qlo = first ? 0 : q0 - HX / S;
+            const int qhi = q0 + T / S;
+            const int nbt = (qhi - qlo + 15) / 16;
+            for (int item = wave; item < nbt * NGR; item += NW) {
+                const int rb = item / NGR, ng = item - rb * NGR;
+                f4 acc[NG];
+#pragma unroll
+                for (int n = 0; n < NG; n++)
+                    acc[n] = f4{0.f, 0.f, 0.f, 0.f};
+                int q = qlo + rb * 16 + l16;
+                q = q < qhi ? q : qhi - 1;
+                const half_t *x1 =
+                    p.aT + ((long)(b + 1) + (long)cu0 * p.r_in + q) * CIN + lg * 8;
+                const half_t *x0 = x1 - CIN;
+                const half_t *wt = WT + (ng * NG * 16 + l16) * ldT + lg * 8;
+#pragma unroll 2
+                for (int k0 = 0; k0 < KT; k0 += 32) {
+                    const int tap = k0 / CIN, c0 = k0 - tap * CIN;
+                    h8 af = *(const h8 *)((tap ? x1 : x0) + c0);
+#pragma unroll
+                    for (int n = 0; n < NG; n++) {
+                        h8 bf = *(const h8 *)(wt + n * 16 * ldT + k0);
+                        acc[n] = mma(af, bf, acc[n]);
+                    }
+                }
+#pragma unroll
+                for (int n = 0; n < NG; n++) {
+                    const int col = (ng * NG + n) * 16 + l16;
+                    const int r = col / C, c = col - r * C;
+                    // channel block of c: (ng NG + n) 16 mod C, over 16 (NG, NB powers
+                    // of two or NB | NG, so this is n % NB when ng NG is a multiple of NB)
+                    const int nb = (((ng * NG + n) * 16) % C) / 16;
+                    float bt = 0.f, ar = 0.f, ai = 0.f;
+#pragma unroll
+                    for (int k = 0; k < NB; k++)
+                        if (k == nb) {
+                            bt = pr[P_BT][k];
+                            ar = pr[P_A1R0][k];
+                            ai = pr[P_A1I0][k];
+                        }
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int qq = qlo + rb * 16 + lg * 4 + e;
+                        if (qq >= qhi)
+                            continue;
+                        const int t = qq * S + r;
+                        const float v = acc[n][e] + bt;
+                        if (t >= t0 - 18 - E)
+                            xs[(t - (t0 - 18 - E)) * C + c] = v;
+                        a1s[(t - (t0 - HX)) * CP + c] = snrvq_f16(snrvq_snake(v, ar, ai));
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- phase 2: residual unit, dilation 1, rows [lo2, t0 + T)
+        if (last) {  // new left context of the dilation-1 conv: last 6 rows of a1
+            half_t *d = slot_state + p.off_a1;
+            for (int i = tid; i < 6 * C / 8; i += 512) {
+                int r = i / (C / 8), c8 = (i - r * (C / 8)) * 8;
+                *(h8 *)(d + r * C + c8) = *(const h8 *)(a1s + (T + HX - 6 + r) * CP + c8);
+            }
+        }
+        {
+            const int lo2 = first ? 0 : t0 - 18 - E;
+            const int xt0 = t0 - 18 - E;
+            residual_unit<C, 1, RB, 0>(a1s, t0 - HX, lo2, t0 + T, W7a, ld7, W1a, ld1, pr, xs,
+                                       xt0, hsw, [&](int t, int c, int n, float v) {
+                                           xs[(t - xt0) * C + c] = v;
+                                           a2s[(t - xt0) * CP + c] = snrvq_f16(snrvq_snake(
+                                               v, pr[P_A1R1][n], pr[P_A1I1][n]));
+                                       });
+        }
+        __syncthreads();
+
+        // ---- phase 3: residual unit, dilation 3, rows [lo3, t0 + T)
+        if (last) {  // new left context of the dilation-3 conv: last 18 rows of a2
+            half_t *d = slot_state + p.off_a2;
+            for (int i = tid; i < 18 * C / 8; i += 512) {
+                int r = i / (C / 8), c8 = (i - r * (C / 8)) * 8;
+                *(h8 *)(d + r * C + c8) = *(const h8 *)(a2s + (T + E + r) * CP + c8);
+            }
+        }
+        if (FINAL && first) {  // left context of the final conv into a_out rows 0..5
+            const half_t *s3 = p.ao_ext + ((long)b * 6 + (long)cu0 * p.r_out) * C;
+            for (int i = tid; i < 6 * C / 8; i += 512) {
+                int r = i / (C / 8), c8 = (i - r * (C / 8)) * 8;
+                *(h8 *)(a1s + r * CP + c8) = *(const h8 *)(s3 + r * C + c8);
+            }
+        }
+        {
+            const int lo3 = first ? 0 : t0 - E;
+            const int xt0 = t0 - 18 - E;
+            const long next_base = ((long)(b + 1) + (long)cu0 * p.r_out) * C;
+            residual_unit<C, 3, RB, 1>(a2s, xt0, lo3, t0 + T, W7b, ld7, W1b, ld1, pr, xs, xt0,
+                                       hsw, [&](int t, int c, int n, float v) {
+                                           const half_t y = snrvq_f16(snrvq_snake(
+                                               v, pr[P_ANR][n], pr[P_ANI][n]));
+                                           if (FINAL)
+                                               a1s[(t - (t0 - 6)) * CP + c] = y;
+                                           else
+                                               p.next[next_base + (long)t * C + c] = y;
+                                       });
+        }
+
+        if (FINAL) {
+            __syncthreads();
+            if (last) {  // new left context of the final conv: last 6 rows of a_out
+                half_t *d = slot_state + p.off_ao;
+                for (int i = tid; i < 6 * C / 8; i += 512) {
+                    int r = i / (C / 8), c8 = (i - r * (C / 8)) * 8;
+                    *(h8 *)(d + r * C + c8) = *(const h8 *)(a1s + (T + r) * CP + c8);
+                }
+            }
+            // ---- phase 4: final conv, one output sample per thread
+            for (int t = t0 + tid; t < t0 + T; t += 512) {
+                float acc = p.b_out;
+#pragma unroll 1
+                for (int j = 0; j < 7; j++) {
+                    const half_t *row = a1s + (t - t0 + j) * CP;
+                    const float *wj = wout_s + j * C;
+#pragma unroll
+                    for (int c0 = 0; c0 < C; c0 += 8) {
+                        h8 v = *(const h8 *)(row + c0);
+#pragma unroll
+                        for (int e = 0; e < 8; e++)
+                            acc += wj[c0 + e] * (float)v[e];
+                    }
+                }
+                p.pcm[(long)cu0 * p.r_out + t] = p.final_tanh ? tanhf(acc) : acc;
+            }
+        }
+    }  // tile loop
+}
+
+template <int C, int S, int T, bool FINAL, bool WL>
+hipError_t launch_stage_t(const StageArgs &a, int F, hipStream_t st)
+{
+    StageArgs b = a;
+    b.tiles_per_frame = a.r_out / T;
+    b.n_tiles = F * b.tiles_per_frame;
+    // weights resident in LDS: one persistent work-group per CU walks the tiles
+    int grid = WL ? (b.n_tiles < a.n_cu ? b.n_tiles : a.n_cu) : b.n_tiles;
+    hipLaunchKernelGGL((stage_kernel<C, S, T, FINAL, WL>), dim3(grid), dim3(512), 0, st, b);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// (C, stride, rows per frame at the output, final) -> an instantiated tile
+int stage_fused_tile(int C, int S, int r_out, bool final_stage)
+{
+    if (final_stage) {
+        if (C == 32 && S == 4 && r_out % 240 == 0)
+            return 240;
+        if (C == 32 && S == 2 && r_out % 256 == 0)
+            return 256;
+    } else {
+        if (C == 64 && S == 3 && r_out % 240 == 0)
+            return 240;
+        if (C == 64 && S == 4 && r_out % 128 == 0)
+            return 128;
+    }
+    return 0;
+}
+
+hipError_t launch_stage_fused(const StageArgs &a, int C, int S, int T, bool final_stage, int F,
+                              hipStream_t st)
+{
+    if (F <= 0)
+        return hipSuccess;
+    if (final_stage) {
+        if (C == 32 && S == 4 && T == 240)
+            return launch_stage_t<32, 4, 240, true, true>(a, F, st);
+        if (C == 32 && S == 2 && T == 256)
+            return launch_stage_t<32, 2, 256, true, true>(a, F, st);
+    } else {
+        if (C == 64 && S == 3 && T == 240)
+            return launch_stage_t<64, 3, 240, false, false>(a, F, st);
+        if (C == 64 && S == 4 && T == 128)
+            return launch_stage_t<64, 4, 128, false, false>(a, F, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace snrvq

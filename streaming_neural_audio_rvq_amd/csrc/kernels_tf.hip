@@ -25,7 +25,7 @@ __device__ __forceinline__ float wave_sum(float v)
 template <typename T>
 __device__ __forceinline__ void st(T *p, float v);
 template <>
-__device__ __forceinline__ void st<half_t>(half_t *p, float v) { *p = (half_t)v; }
+__device__ __forceinline__ void st<half_t>(half_t *p, float v) { *p = snrvq_f16(v); }
 template <>
 __device__ __forceinline__ void st<float>(float *p, float v) { *p = v; }
 

@@ -301,3 +301,40 @@ def test_c3_full_scale_sampled_parity():
         e, ac = rel_err(got, ref)
         say(f"c3 chunk {k} stream {b} pos {start}: err/peak {e:.3e} AC-rel {ac:.3e}")
         assert e <= tol_for(cfg)
+
+
+# --------------------------------------------------------------------------
+# Fused per-stage kernels vs the per-layer launch sequence: same arithmetic
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_fused_stages_bitwise_equal_per_layer(name):
+    cfg = RI.get_config(name, max_streams=8, max_frames_per_call=128)
+    say("case fused vs per-layer", name)
+    w = RI.make_weights(cfg)
+    fused = open_codec(cfg, w)
+    layer = open_codec(dict(cfg, per_layer=True), w)
+    steps = [[1, 3, 16, 2, 1], [8, 1, 1, 5, 2], [2, 16, 4, 1, 7]]
+    codes = [RI.stream_codes(cfg, b, sum(s[b] for s in steps), part=3) for b in range(5)]
+    outs = {}
+    for tag, c in (("fused", fused), ("layer", layer)):
+        ids = [c.stream_open() for _ in range(5)]
+        at = [0] * 5
+        res = []
+        for st in steps:
+            packed = np.concatenate([codes[b][at[b]:at[b] + st[b]] for b in range(5)])
+            pcm = torch.empty(sum(st) * c.hop, dtype=torch.float32, device="cuda")
+            c.decode_chunk(ids, st, packed, pcm)
+            res.append(pcm.cpu().numpy())
+            for b in range(5):
+                at[b] += st[b]
+        outs[tag] = np.concatenate(res)
+    d = np.abs(outs["fused"] - outs["layer"])
+    say(f"{name}: max |fused - per-layer| = {d.max():.3e}")
+    if d.max() > 0:
+        hop = fused.hop
+        bad = np.nonzero(d)[0]
+        say(f"  {len(bad)} of {d.size} samples differ; first at sample {bad[0]} "
+            f"(frame {bad[0] // hop}, offset {bad[0] % hop}); last {bad[-1]}")
+        off = np.bincount(bad % hop, minlength=hop)
+        say(f"  per-offset counts (first 64): {off[:64].tolist()}")
+    assert np.array_equal(outs["fused"], outs["layer"])
