@@ -22,8 +22,8 @@ enum Act : int { ACT_NONE = 0, ACT_SNAKE = 1, ACT_ELU = 2, ACT_GELU = 3 };
 
 // Snake, applied once per element in fp32: v + sin^2(alpha v) / alpha.
 // alpha_rev = alpha / 2pi (precomputed per channel), so alpha v in
-// revolutions is one multiply; it is reduced to [-0.5, 0.5] and fed to the
-// hardware sine, which takes revolutions.  Every Snake evaluation of the
+// revolutions is one multiply; its fractional part is fed to the hardware
+// sine, which takes revolutions.  Every Snake evaluation of the
 // library goes through this one function, so fused and per-layer paths
 // round identically.
 // The rounding steps are spelled out (no contraction) so that every caller
@@ -31,8 +31,7 @@ enum Act : int { ACT_NONE = 0, ACT_SNAKE = 1, ACT_ELU = 2, ACT_GELU = 3 };
 __device__ __forceinline__ float snrvq_snake(float v, float alpha_rev, float inv_alpha)
 {
 #pragma clang fp contract(off)
-    float r = alpha_rev * v;
-    r = r - __builtin_rintf(r);
+    const float r = __builtin_amdgcn_fractf(alpha_rev * v);  // exact reduction to [0, 1)
     const float s = __builtin_amdgcn_sinf(r);
     const float s2 = s * s;
     return __builtin_fmaf(s2, inv_alpha, v);

@@ -17,25 +17,30 @@
 // order (tap-major, channel-minor in steps of 32) on v_mfma_f32_16x16x32_f16,
 // the same fp32 epilogues, so both paths give bit-identical PCM.
 //
+// Orientation: weights are the MFMA's A operand (16 output channels per
+// block) and activations the B operand (16 time rows per block), so each
+// lane's accumulator holds 4 consecutive channels of one time row.  Every
+// epilogue then works on 4 channels at once: one 16-byte read and write of
+// the fp32 residual, one 8-byte fp16 store, one address per 4 values.
+//
 // Left context: at a stream's first tile the rows before the chunk come
 // from the halo rows that the step's halo fill wrote into the (otherwise
 // unused) extended buffers of the per-layer path; the stream's last tile
 // writes the new left contexts straight into its state slot.
 //
-// Work split (8 waves): ConvT work items of 16 input rows x up to 8 column
+// Work split (NW waves): ConvT work items of 16 input rows x up to 8 column
 // blocks; residual-unit row blocks of 16 output rows, RB blocks per wave in
 // flight so each weight fragment feeds RB MFMAs.  The dilated conv reads its
-// 7 taps as row shifts of the LDS tile.  Each lane owns the same NB = C/16
-// channels in every MFMA output block, so all per-channel parameters (biases,
-// Snake alpha/2pi and 1/alpha) live in registers for the whole kernel.  With
-// WL the stage's weights also sit in LDS and one persistent work-group per
-// CU walks the tiles.
+// 7 taps as row shifts of the LDS tile.  Per-channel parameters (biases,
+// Snake alpha/2pi and 1/alpha) sit in LDS.  With WL the stage's weights also
+// sit in LDS and one persistent work-group per CU walks the tiles.
 #include "internal.h"
 
 namespace snrvq {
 namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void wave_lds_sync()
@@ -50,7 +55,24 @@ __device__ __forceinline__ f4 mma(h8 a, h8 b, f4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Per-lane channel parameters: index [param][n] is channel n * 16 + lane % 16.
+__device__ __forceinline__ h4 snake4(f4 v, f4 ar, f4 ai)
+{
+    return h4{snrvq_f16(snrvq_snake(v[0], ar[0], ai[0])),
+              snrvq_f16(snrvq_snake(v[1], ar[1], ai[1])),
+              snrvq_f16(snrvq_snake(v[2], ar[2], ai[2])),
+              snrvq_f16(snrvq_snake(v[3], ar[3], ai[3]))};
+}
+
+// fp32 residual rows in LDS: C floats per row, the 4-float slots of row r
+// permuted by r mod (C/4), so 16 lanes reading 16 consecutive rows at one
+// channel group hit 16 different bank groups.
+template <int C>
+__device__ __forceinline__ int xoff(int r, int c)
+{
+    return r * C + (c ^ ((r & (C / 4 - 1)) << 2));
+}
+
+// Per-channel parameter rows in LDS ([P_COUNT][C] fp32).
 enum Prm {
     P_BT = 0,                                      // ConvT bias
     P_A1R0, P_A1I0, P_B70, P_A2R0, P_A2I0, P_B10,  // residual unit 0
@@ -61,18 +83,17 @@ enum Prm {
 
 // One residual unit over output rows [lo, hi): conv7 (dilation D) of the
 // activated input in LDS (row of time t at in + (t - in_t0) * CP), Snake,
-// 1x1 conv, + bias + residual x (LDS fp32, row of t at xs + (t - x_t0) * C);
-// epi(t, c, n, v) receives every result (n = channel block of c).
-template <int C, int D, int RB, int U, class Epi>
+// 1x1 conv, + bias + residual x (LDS fp32, row t - x_t0 of xs, see xoff);
+// epi(t, c, v) receives channels c..c+3 of row t.
+template <int C, int D, int RB, int NW, int U, class Epi>
 __device__ __forceinline__ void residual_unit(const half_t *in, int in_t0, int lo, int hi,
                                               const half_t *W7, int ld7, const half_t *W1,
-                                              int ld1, const float (&pr)[P_COUNT][C / 16],
-                                              const float *xs, int x_t0, half_t *hsw, Epi epi)
+                                              int ld1, const float *prm, const float *xs,
+                                              int x_t0, half_t *hsw, Epi epi)
 {
     constexpr int CP = C + 8;
     constexpr int NB = C / 16;
     constexpr int K7 = 7 * C;
-    constexpr int NW = 8;
     constexpr int PB7 = U ? P_B71 : P_B70, PA2R = U ? P_A2R1 : P_A2R0,
                   PA2I = U ? P_A2I1 : P_A2I0, PB1 = U ? P_B11 : P_B10;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -96,17 +117,17 @@ __device__ __forceinline__ void residual_unit(const half_t *in, int in_t0, int l
         for (int k0 = 0; k0 < K7; k0 += 32) {
             const int tap = k0 / C, c0 = k0 - tap * C;
             const int sh = (tap - 6) * D * CP + c0;
-            h8 bf[NB];
+            h8 wf[NB];
 #pragma unroll
             for (int n = 0; n < NB; n++)
-                bf[n] = *(const h8 *)(W7 + (n * 16 + l16) * ld7 + k0 + lg * 8);
+                wf[n] = *(const h8 *)(W7 + (n * 16 + l16) * ld7 + k0 + lg * 8);
 #pragma unroll
             for (int j = 0; j < RB; j++) {
                 if (rb0 + j * NW < nblk) {
-                    h8 af = *(const h8 *)(in + rowoff[j] + sh);
+                    h8 xf = *(const h8 *)(in + rowoff[j] + sh);
 #pragma unroll
                     for (int n = 0; n < NB; n++)
-                        acc[j][n] = mma(af, bf[n], acc[j][n]);
+                        acc[j][n] = mma(wf[n], xf, acc[j][n]);
                 }
             }
         }
@@ -115,14 +136,14 @@ __device__ __forceinline__ void residual_unit(const half_t *in, int in_t0, int l
             const int blk = rb0 + j * NW;
             if (blk >= nblk)
                 continue;
-            // Snake(conv7 + b7) -> fp16 rows of this wave's scratch
+            // Snake(conv7 + b7) -> this wave's scratch, row l16, 4 channels per lane
 #pragma unroll
             for (int n = 0; n < NB; n++) {
-                const int c = n * 16 + l16;
-#pragma unroll
-                for (int e = 0; e < 4; e++)
-                    hsw[(lg * 4 + e) * CP + c] = snrvq_f16(snrvq_snake(
-                        acc[j][n][e] + pr[PB7][n], pr[PA2R][n], pr[PA2I][n]));
+                const int c = n * 16 + lg * 4;
+                const f4 b7 = *(const f4 *)(prm + PB7 * C + c);
+                const f4 ar = *(const f4 *)(prm + PA2R * C + c);
+                const f4 ai = *(const f4 *)(prm + PA2I * C + c);
+                *(h4 *)(hsw + l16 * CP + c) = snake4(acc[j][n] + b7, ar, ai);
             }
             wave_lds_sync();
             f4 a2c[NB];
@@ -131,39 +152,38 @@ __device__ __forceinline__ void residual_unit(const half_t *in, int in_t0, int l
                 a2c[n] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c0 = 0; c0 < C; c0 += 32) {
-                h8 af = *(const h8 *)(hsw + l16 * CP + c0 + lg * 8);
+                const h8 hf = *(const h8 *)(hsw + l16 * CP + c0 + lg * 8);
 #pragma unroll
                 for (int n = 0; n < NB; n++) {
-                    h8 bf = *(const h8 *)(W1 + (n * 16 + l16) * ld1 + c0 + lg * 8);
-                    a2c[n] = mma(af, bf, a2c[n]);
+                    const h8 wf = *(const h8 *)(W1 + (n * 16 + l16) * ld1 + c0 + lg * 8);
+                    a2c[n] = mma(wf, hf, a2c[n]);
                 }
             }
             wave_lds_sync();
+            const int t = lo + blk * 16 + l16;
+            if (t < hi) {
 #pragma unroll
-            for (int n = 0; n < NB; n++) {
-                const int c = n * 16 + l16;
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int t = lo + blk * 16 + lg * 4 + e;
-                    if (t < hi)
-                        epi(t, c, n, a2c[n][e] + pr[PB1][n] + xs[(t - x_t0) * C + c]);
+                for (int n = 0; n < NB; n++) {
+                    const int c = n * 16 + lg * 4;
+                    const f4 b1 = *(const f4 *)(prm + PB1 * C + c);
+                    const f4 xr = *(const f4 *)(xs + xoff<C>(t - x_t0, c));
+                    epi(t, c, (a2c[n] + b1) + xr);
                 }
             }
         }
     }
 }
 
-template <int C, int S, int T, bool FINAL, bool WL>
-__global__ __launch_bounds__(512) void stage_kernel(StageArgs p)
+template <int C, int S, int T, bool FINAL, bool WL, int NW>
+__global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
 {
+    constexpr int NT_ = NW * 64;
     constexpr int E = FINAL ? 6 : 0;
     constexpr int HX = S * ((24 + E + S - 1) / S);  // ConvT rows recomputed before t0
     constexpr int NX = T + HX;                      // a1 rows: [t0 - HX, t0 + T)
     constexpr int NR = T + 18 + E;                  // x and a2 rows: [t0 - 18 - E, t0 + T)
     constexpr int CP = C + 8;
-    constexpr int NW = 8;
-    constexpr int NB = C / 16;
-    constexpr int RB = C >= 128 ? 2 : 4;
+    constexpr int RB = NW >= 16 && C >= 64 ? 2 : 4;
     constexpr int CIN = 2 * C;
     constexpr int NT = S * C, KT = 2 * CIN, NBT = NT / 16;
     // ConvT column blocks per work item: the largest divisor of NBT <= 8
@@ -175,6 +195,7 @@ __global__ __launch_bounds__(512) void stage_kernel(StageArgs p)
     __shared__ __attribute__((aligned(16))) half_t a1s[NX * CP];  // a1, then a_out (FINAL)
     __shared__ __attribute__((aligned(16))) half_t a2s[NR * CP];
     __shared__ __attribute__((aligned(16))) half_t hs[NW * 16 * CP];
+    __shared__ __attribute__((aligned(16))) float prm[P_COUNT * C];
     constexpr int LDT = KT + 8, LD7 = 7 * C + 8, LD1 = C + 8;
     constexpr int WBYTES = WL ? 2 * (NT * LDT + 2 * C * LD7 + 2 * C * LD1) : 16;
     __shared__ __attribute__((aligned(16))) char wsm[WBYTES];
@@ -186,22 +207,17 @@ __global__ __launch_bounds__(512) void stage_kernel(StageArgs p)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
 
-    // ---- per-lane channel parameters, for the kernel's lifetime
-    float pr[P_COUNT][NB];
     {
         const float *src[P_COUNT] = {p.bT,      p.al1[0], p.ial1[0], p.b7[0], p.al2[0],
                                      p.ial2[0], p.b1[0],  p.al1[1], p.ial1[1], p.b7[1],
                                      p.al2[1],  p.ial2[1], p.b1[1],  p.al_next, p.ial_next};
-#pragma unroll
-        for (int k = 0; k < P_COUNT; k++)
-#pragma unroll
-            for (int n = 0; n < NB; n++)
-                pr[k][n] = src[k][n * 16 + l16];
+        for (int i = tid; i < P_COUNT * C; i += NT_)
+            prm[i] = src[i / C][i % C];
     }
     if (WL) {
         auto copy = [&](half_t *dst, int ld, const half_t *src, int rows, int cols) {
             const int cpr = cols / 8;
-            for (int i = tid; i < rows * cpr; i += 512) {
+            for (int i = tid; i < rows * cpr; i += NT_) {
                 const int r = i / cpr, c8 = (i - r * cpr) * 8;
                 *(h8 *)(dst + r * ld + c8) = *(const h8 *)(src + (long)r * cols + c8);
             }
@@ -213,7 +229,7 @@ __global__ __launch_bounds__(512) void stage_kernel(StageArgs p)
         }
     }
     if (FINAL) {
-        for (int i = tid; i < 7 * C; i += 512) {
+        for (int i = tid; i < 7 * C; i += NT_) {
             const int c = i / 7, j = i - c * 7;  // input layout [C][7]
             wout_s[j * C + c] = p.w_out[i];
         }
@@ -225,7 +241,7 @@ __global__ __launch_bounds__(512) void stage_kernel(StageArgs p)
     const half_t *const W1a = WL ? w1s : p.W1[0];
     const half_t *const W1b = WL ? w1s + C * LD1 : p.W1[1];
     const int ld7 = WL ? LD7 : 7 * C, ld1 = WL ? LD1 : C;
-    __syncthreads();  // weights (WL) and final-conv weights are in LDS
+    __syncthreads();  // parameters and weights are in LDS
 
     for (int g = blockIdx.x; g < p.n_tiles; g += gridDim.x) {
         if (g != (int)blockIdx.x)
@@ -242,12 +258,12 @@ __global__ __launch_bounds__(512) void stage_kernel(StageArgs p)
         // ---- left context of a stream's first tile (written by the halo fill)
         if (first) {
             const half_t *s1 = p.a1_ext + ((long)b * 6 + (long)cu0 * p.r_out) * C;
-            for (int i = tid; i < 6 * C / 8; i += 512) {
+            for (int i = tid; i < 6 * C / 8; i += NT_) {
                 int r = i / (C / 8), c8 = (i - r * (C / 8)) * 8;
                 *(h8 *)(a1s + (HX - 6 + r) * CP + c8) = *(const h8 *)(s1 + r * C + c8);
             }
             const half_t *s2 = p.a2_ext + ((long)b * 18 + (long)cu0 * p.r_out) * C;
-            for (int i = tid; i < 18 * C / 8; i += 512) {
+            for (int i = tid; i < 18 * C / 8; i += NT_) {
                 int r = i / (C / 8), c8 = (i - r * (C / 8)) * 8;
                 *(h8 *)(a2s + (E + r) * CP + c8) = *(const h8 *)(s2 + r * C + c8);
             }
@@ -266,7 +282,8 @@ __global__ __launch_bounds__(512) void stage_kernel(StageArgs p)
                 for (int n = 0; n < NG; n++)
                     acc[n] = f4{0.f, 0.f, 0.f, 0.f};
                 int q = qlo + rb * 16 + l16;
-                q = q < qhi ? q : qhi - 1;
+                const bool qok = q < qhi;
+                q = qok ? q : qhi - 1;
                 const half_t *x1 =
                     p.aT + ((long)(b + 1) + (long)cu0 * p.r_in + q) * CIN + lg * 8;
                 const half_t *x0 = x1 - CIN;
@@ -274,38 +291,25 @@ __global__ __launch_bounds__(512) void stage_kernel(StageArgs p)
 #pragma unroll 2
                 for (int k0 = 0; k0 < KT; k0 += 32) {
                     const int tap = k0 / CIN, c0 = k0 - tap * CIN;
-                    h8 af = *(const h8 *)((tap ? x1 : x0) + c0);
+                    const h8 xf = *(const h8 *)((tap ? x1 : x0) + c0);
 #pragma unroll
                     for (int n = 0; n < NG; n++) {
-                        h8 bf = *(const h8 *)(wt + n * 16 * ldT + k0);
-                        acc[n] = mma(af, bf, acc[n]);
+                        const h8 wf = *(const h8 *)(wt + n * 16 * ldT + k0);
+                        acc[n] = mma(wf, xf, acc[n]);
                     }
                 }
+                if (qok) {
 #pragma unroll
-                for (int n = 0; n < NG; n++) {
-                    const int col = (ng * NG + n) * 16 + l16;
-                    const int r = col / C, c = col - r * C;
-                    // channel block of c: (ng NG + n) 16 mod C, over 16 (NG, NB powers
-                    // of two or NB | NG, so this is n % NB when ng NG is a multiple of NB)
-                    const int nb = (((ng * NG + n) * 16) % C) / 16;
-                    float bt = 0.f, ar = 0.f, ai = 0.f;
-#pragma unroll
-                    for (int k = 0; k < NB; k++)
-                        if (k == nb) {
-                            bt = pr[P_BT][k];
-                            ar = pr[P_A1R0][k];
-                            ai = pr[P_A1I0][k];
-                        }
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const int qq = qlo + rb * 16 + lg * 4 + e;
-                        if (qq >= qhi)
-                            continue;
-                        const int t = qq * S + r;
-                        const float v = acc[n][e] + bt;
+                    for (int n = 0; n < NG; n++) {
+                        const int col = (ng * NG + n) * 16 + lg * 4;
+                        const int r = col / C, c = col - r * C;
+                        const int t = q * S + r;
+                        const f4 v = acc[n] + *(const f4 *)(prm + P_BT * C + c);
                         if (t >= t0 - 18 - E)
-                            xs[(t - (t0 - 18 - E)) * C + c] = v;
-                        a1s[(t - (t0 - HX)) * CP + c] = snrvq_f16(snrvq_snake(v, ar, ai));
+                            *(f4 *)(xs + xoff<C>(t - (t0 - 18 - E), c)) = v;
+                        *(h4 *)(a1s + (t - (t0 - HX)) * CP + c) =
+                            snake4(v, *(const f4 *)(prm + P_A1R0 * C + c),
+                                   *(const f4 *)(prm + P_A1I0 * C + c));
                     }
                 }
             }
@@ -315,7 +319,7 @@ __global__ __launch_bounds__(512) void stage_kernel(StageArgs p)
         // ---- phase 2: residual unit, dilation 1, rows [lo2, t0 + T)
         if (last) {  // new left context of the dilation-1 conv: last 6 rows of a1
             half_t *d = slot_state + p.off_a1;
-            for (int i = tid; i < 6 * C / 8; i += 512) {
+            for (int i = tid; i < 6 * C / 8; i += NT_) {
                 int r = i / (C / 8), c8 = (i - r * (C / 8)) * 8;
                 *(h8 *)(d + r * C + c8) = *(const h8 *)(a1s + (T + HX - 6 + r) * CP + c8);
             }
@@ -323,26 +327,27 @@ __global__ __launch_bounds__(512) void stage_kernel(StageArgs p)
         {
             const int lo2 = first ? 0 : t0 - 18 - E;
             const int xt0 = t0 - 18 - E;
-            residual_unit<C, 1, RB, 0>(a1s, t0 - HX, lo2, t0 + T, W7a, ld7, W1a, ld1, pr, xs,
-                                       xt0, hsw, [&](int t, int c, int n, float v) {
-                                           xs[(t - xt0) * C + c] = v;
-                                           a2s[(t - xt0) * CP + c] = snrvq_f16(snrvq_snake(
-                                               v, pr[P_A1R1][n], pr[P_A1I1][n]));
-                                       });
+            residual_unit<C, 1, RB, NW, 0>(a1s, t0 - HX, lo2, t0 + T, W7a, ld7, W1a, ld1, prm, xs,
+                                           xt0, hsw, [&](int t, int c, f4 v) {
+                                               *(f4 *)(xs + xoff<C>(t - xt0, c)) = v;
+                                               *(h4 *)(a2s + (t - xt0) * CP + c) = snake4(
+                                                   v, *(const f4 *)(prm + P_A1R1 * C + c),
+                                                   *(const f4 *)(prm + P_A1I1 * C + c));
+                                           });
         }
         __syncthreads();
 
         // ---- phase 3: residual unit, dilation 3, rows [lo3, t0 + T)
         if (last) {  // new left context of the dilation-3 conv: last 18 rows of a2
             half_t *d = slot_state + p.off_a2;
-            for (int i = tid; i < 18 * C / 8; i += 512) {
+            for (int i = tid; i < 18 * C / 8; i += NT_) {
                 int r = i / (C / 8), c8 = (i - r * (C / 8)) * 8;
                 *(h8 *)(d + r * C + c8) = *(const h8 *)(a2s + (T + E + r) * CP + c8);
             }
         }
         if (FINAL && first) {  // left context of the final conv into a_out rows 0..5
             const half_t *s3 = p.ao_ext + ((long)b * 6 + (long)cu0 * p.r_out) * C;
-            for (int i = tid; i < 6 * C / 8; i += 512) {
+            for (int i = tid; i < 6 * C / 8; i += NT_) {
                 int r = i / (C / 8), c8 = (i - r * (C / 8)) * 8;
                 *(h8 *)(a1s + r * CP + c8) = *(const h8 *)(s3 + r * C + c8);
             }
@@ -351,28 +356,30 @@ __global__ __launch_bounds__(512) void stage_kernel(StageArgs p)
             const int lo3 = first ? 0 : t0 - E;
             const int xt0 = t0 - 18 - E;
             const long next_base = ((long)(b + 1) + (long)cu0 * p.r_out) * C;
-            residual_unit<C, 3, RB, 1>(a2s, xt0, lo3, t0 + T, W7b, ld7, W1b, ld1, pr, xs, xt0,
-                                       hsw, [&](int t, int c, int n, float v) {
-                                           const half_t y = snrvq_f16(snrvq_snake(
-                                               v, pr[P_ANR][n], pr[P_ANI][n]));
-                                           if (FINAL)
-                                               a1s[(t - (t0 - 6)) * CP + c] = y;
-                                           else
-                                               p.next[next_base + (long)t * C + c] = y;
-                                       });
+            residual_unit<C, 3, RB, NW, 1>(a2s, xt0, lo3, t0 + T, W7b, ld7, W1b, ld1, prm, xs,
+                                           xt0, hsw, [&](int t, int c, f4 v) {
+                                               const h4 y = snake4(
+                                                   v, *(const f4 *)(prm + P_ANR * C + c),
+                                                   *(const f4 *)(prm + P_ANI * C + c));
+                                               if (FINAL)
+                                                   *(h4 *)(a1s + (t - (t0 - 6)) * CP + c) = y;
+                                               else
+                                                   *(h4 *)(p.next + next_base + (long)t * C + c) =
+                                                       y;
+                                           });
         }
 
         if (FINAL) {
             __syncthreads();
             if (last) {  // new left context of the final conv: last 6 rows of a_out
                 half_t *d = slot_state + p.off_ao;
-                for (int i = tid; i < 6 * C / 8; i += 512) {
+                for (int i = tid; i < 6 * C / 8; i += NT_) {
                     int r = i / (C / 8), c8 = (i - r * (C / 8)) * 8;
                     *(h8 *)(d + r * C + c8) = *(const h8 *)(a1s + (T + r) * CP + c8);
                 }
             }
             // ---- phase 4: final conv, one output sample per thread
-            for (int t = t0 + tid; t < t0 + T; t += 512) {
+            for (int t = t0 + tid; t < t0 + T; t += NT_) {
                 float acc = p.b_out;
 #pragma unroll 1
                 for (int j = 0; j < 7; j++) {
@@ -392,7 +399,7 @@ __global__ __launch_bounds__(512) void stage_kernel(StageArgs p)
     }  // tile loop
 }
 
-template <int C, int S, int T, bool FINAL, bool WL>
+template <int C, int S, int T, bool FINAL, bool WL, int NW>
 hipError_t launch_stage_t(const StageArgs &a, int F, hipStream_t st)
 {
     StageArgs b = a;
@@ -400,7 +407,8 @@ hipError_t launch_stage_t(const StageArgs &a, int F, hipStream_t st)
     b.n_tiles = F * b.tiles_per_frame;
     // weights resident in LDS: one persistent work-group per CU walks the tiles
     int grid = WL ? (b.n_tiles < a.n_cu ? b.n_tiles : a.n_cu) : b.n_tiles;
-    hipLaunchKernelGGL((stage_kernel<C, S, T, FINAL, WL>), dim3(grid), dim3(512), 0, st, b);
+    hipLaunchKernelGGL((stage_kernel<C, S, T, FINAL, WL, NW>), dim3(grid), dim3(NW * 64), 0, st,
+                       b);
     return hipGetLastError();
 }
 
@@ -410,8 +418,8 @@ hipError_t launch_stage_t(const StageArgs &a, int F, hipStream_t st)
 int stage_fused_tile(int C, int S, int r_out, bool final_stage)
 {
     if (final_stage) {
-        if (C == 32 && S == 4 && r_out % 240 == 0)
-            return 240;
+        if (C == 32 && S == 4 && r_out % 192 == 0)
+            return 192;
         if (C == 32 && S == 2 && r_out % 256 == 0)
             return 256;
     } else {
@@ -429,15 +437,15 @@ hipError_t launch_stage_fused(const StageArgs &a, int C, int S, int T, bool fina
     if (F <= 0)
         return hipSuccess;
     if (final_stage) {
-        if (C == 32 && S == 4 && T == 240)
-            return launch_stage_t<32, 4, 240, true, true>(a, F, st);
+        if (C == 32 && S == 4 && T == 192)
+            return launch_stage_t<32, 4, 192, true, true, 16>(a, F, st);
         if (C == 32 && S == 2 && T == 256)
-            return launch_stage_t<32, 2, 256, true, true>(a, F, st);
+            return launch_stage_t<32, 2, 256, true, true, 16>(a, F, st);
     } else {
         if (C == 64 && S == 3 && T == 240)
-            return launch_stage_t<64, 3, 240, false, false>(a, F, st);
+            return launch_stage_t<64, 3, 240, false, false, 8>(a, F, st);
         if (C == 64 && S == 4 && T == 128)
-            return launch_stage_t<64, 4, 128, false, false>(a, F, st);
+            return launch_stage_t<64, 4, 128, false, false, 16>(a, F, st);
     }
     return hipErrorInvalidValue;
 }
