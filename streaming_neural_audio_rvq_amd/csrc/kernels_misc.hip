@@ -133,7 +133,10 @@ __device__ __forceinline__ void unpack<float>(const float *p, int n, float *v)
 }
 
 // pcm[m] = b + sum_j sum_c w[j][c] A[row(m) - (6 - j)][c]; one thread per
-// output sample, fp32 accumulation, taps then channels ascending.
+// output sample, fp32 accumulation.  The channels are split in four
+// quarters, each summed taps-then-channels ascending, and combined as
+// b + ((q0 + q1) + (q2 + q3)) -- the order the fused last-stage kernel uses
+// with four threads per sample.
 template <typename T>
 __global__ __launch_bounds__(256) void final_conv_kernel(const T *A, int A_H, int C, int rate,
                                                          const float *w, float bias, int tanh_out,
@@ -152,18 +155,24 @@ __global__ __launch_bounds__(256) void final_conv_kernel(const T *A, int A_H, in
     int b = frame_stream[m / rate];
     long ext = (long)(b + 1) * A_H + m;
     constexpr int VEC = 16 / (int)sizeof(T);
-    float acc = bias;
-    for (int j = 0; j < 7; j++) {
-        const T *row = A + (ext - (6 - j)) * C;
-        const float *wj = wsh + j * C;
-        for (int c = 0; c < C; c += VEC) {
-            float v[8];
-            unpack<T>(row + c, VEC, v);
+    const int CQ = C / 4;
+    float q[4];
+    for (int qp = 0; qp < 4; qp++) {
+        float part = 0.f;
+        for (int j = 0; j < 7; j++) {
+            const T *row = A + (ext - (6 - j)) * C + qp * CQ;
+            const float *wj = wsh + j * C + qp * CQ;
+            for (int c = 0; c < CQ; c += VEC) {
+                float v[8];
+                unpack<T>(row + c, VEC, v);
 #pragma unroll
-            for (int e = 0; e < VEC; e++)
-                acc += wj[c + e] * v[e];
+                for (int e = 0; e < VEC; e++)
+                    part += wj[c + e] * v[e];
+            }
         }
+        q[qp] = part;
     }
+    const float acc = bias + ((q[0] + q[1]) + (q[2] + q[3]));
     pcm[m] = tanh_out ? tanhf(acc) : acc;
 }
 

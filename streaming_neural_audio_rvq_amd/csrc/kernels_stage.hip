@@ -186,9 +186,13 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
     constexpr int RB = NW >= 16 && C >= 64 ? 2 : 4;
     constexpr int CIN = 2 * C;
     constexpr int NT = S * C, KT = 2 * CIN, NBT = NT / 16;
-    // ConvT column blocks per work item: the largest divisor of NBT <= 8
-    constexpr int NG = NBT % 8 == 0 ? 8 : NBT % 6 == 0 ? 6 : NBT % 4 == 0 ? 4 : NBT % 2 == 0 ? 2 : 1;
+    // ConvT column blocks per work item: 2 with 16 waves (enough items for
+    // every wave), else the largest divisor of NBT <= 8 (fewer re-reads of
+    // the item's input rows, which are loaded once, up front)
+    constexpr int NG = NW >= 16 ? (NBT % 2 == 0 ? 2 : 1)
+                                : (NBT % 8 == 0 ? 8 : NBT % 6 == 0 ? 6 : NBT % 4 == 0 ? 4 : NBT % 2 == 0 ? 2 : 1);
     constexpr int NGR = NBT / NG;
+    constexpr int NKT = KT / 32;
     static_assert(T % S == 0 && NT % 16 == 0 && C % 32 == 0, "shape");
 
     __shared__ __attribute__((aligned(16))) float xs[NR * C];
@@ -288,14 +292,18 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
                     p.aT + ((long)(b + 1) + (long)cu0 * p.r_in + q) * CIN + lg * 8;
                 const half_t *x0 = x1 - CIN;
                 const half_t *wt = WT + (ng * NG * 16 + l16) * ldT + lg * 8;
-#pragma unroll 2
-                for (int k0 = 0; k0 < KT; k0 += 32) {
-                    const int tap = k0 / CIN, c0 = k0 - tap * CIN;
-                    const h8 xf = *(const h8 *)((tap ? x1 : x0) + c0);
+                h8 xf[NKT];
+#pragma unroll
+                for (int ks = 0; ks < NKT; ks++) {
+                    const int k0 = ks * 32, tap = k0 / CIN, c0 = k0 - tap * CIN;
+                    xf[ks] = *(const h8 *)((tap ? x1 : x0) + c0);
+                }
+#pragma unroll
+                for (int ks = 0; ks < NKT; ks++) {
 #pragma unroll
                     for (int n = 0; n < NG; n++) {
-                        const h8 wf = *(const h8 *)(wt + n * 16 * ldT + k0);
-                        acc[n] = mma(wf, xf, acc[n]);
+                        const h8 wf = *(const h8 *)(wt + n * 16 * ldT + ks * 32);
+                        acc[n] = mma(wf, xf[ks], acc[n]);
                     }
                 }
                 if (qok) {
@@ -378,22 +386,29 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
                     *(h8 *)(d + r * C + c8) = *(const h8 *)(a1s + (T + r) * CP + c8);
                 }
             }
-            // ---- phase 4: final conv, one output sample per thread
-            for (int t = t0 + tid; t < t0 + T; t += NT_) {
-                float acc = p.b_out;
-#pragma unroll 1
-                for (int j = 0; j < 7; j++) {
-                    const half_t *row = a1s + (t - t0 + j) * CP;
-                    const float *wj = wout_s + j * C;
+            // ---- phase 4: final conv, four threads per output sample, each
+            // over one quarter of the channels, combined as (q0+q1)+(q2+q3)
+            for (int i = tid; i < 4 * T; i += NT_) {
+                const int t = t0 + (i >> 2), qp = i & 3;
+                float part = 0.f;
 #pragma unroll
-                    for (int c0 = 0; c0 < C; c0 += 8) {
+                for (int j = 0; j < 7; j++) {
+                    const half_t *row = a1s + (t - t0 + j) * CP + qp * (C / 4);
+                    const float *wj = wout_s + j * C + qp * (C / 4);
+#pragma unroll
+                    for (int c0 = 0; c0 < C / 4; c0 += 8) {
                         h8 v = *(const h8 *)(row + c0);
 #pragma unroll
                         for (int e = 0; e < 8; e++)
-                            acc += wj[c0 + e] * (float)v[e];
+                            part += wj[c0 + e] * (float)v[e];
                     }
                 }
-                p.pcm[(long)cu0 * p.r_out + t] = p.final_tanh ? tanhf(acc) : acc;
+                part += __shfl_xor(part, 1, 64);
+                part += __shfl_xor(part, 2, 64);
+                if (qp == 0) {
+                    const float y = p.b_out + part;
+                    p.pcm[(long)cu0 * p.r_out + t] = p.final_tanh ? tanhf(y) : y;
+                }
             }
         }
     }  // tile loop
