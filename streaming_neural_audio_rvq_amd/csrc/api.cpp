@@ -104,12 +104,17 @@ struct codec {
     void *z = nullptr, *u_ext = nullptr, *aT[CODEC_MAX_STAGES]{}, *a1[CODEC_MAX_STAGES]{},
          *a2[CODEC_MAX_STAGES]{}, *h = nullptr, *a_outb = nullptr;
     float *x = nullptr, *pcm_scratch = nullptr;
+    float *splitk_ws = nullptr;  // split-K partial sums
+    long splitk_cap = 0;         // floats
 
     void *state = nullptr;
     int64_t slot_elems = 0;
     HaloTable halo{};       // filled before every step
     HaloTable halo_save{};  // saved after it (fused stages write their own)
     int fuse_T[CODEC_MAX_STAGES]{};  // output rows per tile of a fused stage, 0 = per-layer
+    // stages that have a fused kernel, whether or not it is used: their
+    // per-layer convs run K in one pass, the fused kernel's summation order
+    bool fusable[CODEC_MAX_STAGES]{};
     int64_t off_a1[CODEC_MAX_STAGES]{}, off_a2[CODEC_MAX_STAGES]{}, off_ao = 0;
 
     void *meta_dev = nullptr;
@@ -434,9 +439,14 @@ void set_act(codec *c, ConvArgs &a, const ActP &p)
     a.inv_alpha = p.ialpha;
 }
 
-int run_conv(codec *c, const char *name, const ConvArgs &a, hipStream_t s)
+int run_conv(codec *c, const char *name, const ConvArgs &a0, hipStream_t s, bool allow_split = true)
 {
-    return timed(c, name, (int64_t)a.M, s, [&] { return launch_conv_gemm(a, c->dtype, s, -1); });
+    ConvArgs a = a0;
+    a.splits_allowed = allow_split;
+    a.partial = c->splitk_ws;
+    const ConvPlan plan = conv_gemm_plan(a, c->dtype, c->n_cu, c->splitk_cap);
+    return timed(c, name, (int64_t)a.M, s,
+                 [&] { return launch_conv_gemm(a, c->dtype, s, plan); });
 }
 
 size_t round4(size_t n) { return (n + 3) & ~(size_t)3; }
@@ -651,7 +661,8 @@ int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int3
         a.out_H = 6;
         set_act(c, a, c->a_ru1[i][0]);
         snprintf(nm, sizeof nm, "s%d.convT", i);
-        if ((rc = run_conv(c, nm, a, s)))
+        const bool split = !c->fusable[i];
+        if ((rc = run_conv(c, nm, a, s, split)))
             return rc;
         for (int j = 0; j < 2; j++) {
             void *in = j == 0 ? c->a1[i] : c->a2[i];
@@ -661,7 +672,7 @@ int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int3
             a.out_H = 0;
             set_act(c, a, c->a_ru2[i][j]);
             snprintf(nm, sizeof nm, "s%d.ru%d.conv7", i, j);
-            if ((rc = run_conv(c, nm, a, s)))
+            if ((rc = run_conv(c, nm, a, s, split)))
                 return rc;
             a = conv_args(c, c->conv1[i][j], c->h, 0, ro, F * ro, m);
             a.res = c->x;
@@ -680,7 +691,7 @@ int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int3
                 set_act(c, a, c->a_out);
             }
             snprintf(nm, sizeof nm, "s%d.ru%d.conv1", i, j);
-            if ((rc = run_conv(c, nm, a, s)))
+            if ((rc = run_conv(c, nm, a, s, split)))
                 return rc;
         }
     }
@@ -1006,6 +1017,9 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
     }
     if ((rc = dev_alloc(c, (void **)&c->pcm_scratch, F * hop * 4, ws)))
         return cleanup_fail(rc);
+    c->splitk_cap = 16L << 20;  // 64 MiB of fp32 partials
+    if ((rc = dev_alloc(c, (void **)&c->splitk_ws, (size_t)c->splitk_cap * 4, ws)))
+        return cleanup_fail(rc);
 
     // ---- halo table and state slots ----
     HaloTable &t = c->halo;
@@ -1034,11 +1048,13 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
     t.slot_elems = off;
     // fused stages (fp16 path): their residual-unit and final-conv left
     // contexts are written by the stage kernel itself, not by the halo save
-    for (int i = 0; i < c->S; i++)
-        c->fuse_T[i] = (c->dtype && g.act == CODEC_ACT_SNAKE && !(g.flags & CODEC_FLAG_PER_LAYER) &&
-                        !(g.flags & CODEC_FLAG_PER_LAYER_STAGE(i)))
-                           ? stage_fused_tile(ch[i + 1], g.strides[i], c->rate[i + 1], i == c->S - 1)
-                           : 0;
+    for (int i = 0; i < c->S; i++) {
+        const int T = (c->dtype && g.act == CODEC_ACT_SNAKE)
+                          ? stage_fused_tile(ch[i + 1], g.strides[i], c->rate[i + 1], i == c->S - 1)
+                          : 0;
+        c->fusable[i] = T != 0;
+        c->fuse_T[i] = (g.flags & CODEC_FLAG_PER_LAYER) || (g.flags & CODEC_FLAG_PER_LAYER_STAGE(i)) ? 0 : T;
+    }
     HaloTable &sv = c->halo_save;
     sv.elem_bytes = t.elem_bytes;
     sv.slot_elems = t.slot_elems;

@@ -68,6 +68,14 @@ struct ConvArgs {
     int N, Cout, s;
     int out_H, act;
     int out_ld;             // row width of out16 / out32 (== Cout)
+    int splits;             // split-K count (set by the launcher)
+    int splits_allowed;     // 1: the planner may split K
+    float *partial;         // split-K partials [splits][M][N] fp32
+};
+
+// Tile choice and split-K count of one conv launch.
+struct ConvPlan {
+    int tile, splits;
 };
 
 // Halo layers: fill before a step, save after it.
@@ -96,8 +104,8 @@ struct StepMeta {
 
 // ---- launchers (kernels_*.hip) ----
 // dtype: 0 = fp32 operands, 1 = fp16 operands
-hipError_t launch_conv_gemm(const ConvArgs &a, int dtype, hipStream_t st, int tile_hint);
-int conv_gemm_tile_choice(const ConvArgs &a, int dtype);
+hipError_t launch_conv_gemm(const ConvArgs &a, int dtype, hipStream_t st, ConvPlan plan);
+ConvPlan conv_gemm_plan(const ConvArgs &a, int dtype, int n_cu, long partial_cap);
 const char *conv_gemm_tile_name(int dtype, int tile);
 
 hipError_t launch_halo_fill(const HaloTable &t, void *state, const StepMeta &m, int B,

@@ -1,6 +1,6 @@
 // kernels_conv.hip -- implicit-GEMM causal convolutions on CDNA4 MFMA.
 //
-// One kernel template serves every dense contraction of the decoder:
+// One kernel template serves every dense contraction of the per-layer path:
 //   * causal dilated Conv1d (k = 7, dilation 1 or 3): taps are row shifts of
 //     the channels-last extended input, so the GEMM's K dimension is
 //     (tap, channel) and the A operand rows are gathered per output row;
@@ -15,13 +15,20 @@
 // buffer.  So every activation is computed once per element, and every conv
 // reads operands that are ready for the matrix cores.
 //
-// Tiles: 256 threads (4 waves of 64), BM x BN output tile, BK = 32 (fp16,
-// v_mfma_f32_16x16x32_f16) or 16 (fp32, v_mfma_f32_16x16x4_f32).  Global
-// loads are 16-byte chunks staged through double-buffered LDS; the epilogue
-// goes through LDS so that every global store is a 16-byte chunk of a row.
-// Work-groups are remapped so that each XCD (dispatch round-robin over 8)
-// owns a contiguous range of tiles, N-tiles of one M-row block adjacent, so
-// the A rows (re-read by every tap and every N-tile) stay in one L2.
+// Tiles: 256 threads (4 waves of 64), BM x BN output tile, K staged in steps
+// of BK = 32 KSUB (fp16, v_mfma_f32_16x16x32_f16) or 16 (fp32,
+// v_mfma_f32_16x16x4_f32).  Global loads are 16-byte chunks double-buffered
+// through LDS; the epilogue goes through LDS so that every global store is a
+// 16-byte chunk of a row.  Work-groups are remapped so that each XCD
+// (dispatch round-robin over 8) owns a contiguous range of tiles, N-tiles of
+// one M-row block adjacent, so the A rows (re-read by every tap and every
+// N-tile) stay in one L2.
+//
+// Split-K (layers whose M x N has fewer tiles than the GPU has CUs, e.g. the
+// frame-rate layers at a few hundred frames): blockIdx.y selects a
+// contiguous K range; each split writes its fp32 partial tile and a reduce
+// kernel sums the splits in split order, then applies the same epilogue.
+// No atomics: the result depends only on the shapes, never on timing.
 #include "internal.h"
 
 namespace snrvq {
@@ -69,6 +76,36 @@ __device__ __forceinline__ void store4<float>(float *dst, f4 v)
     *(f4 *)dst = v;
 }
 
+// Output of 4 consecutive columns n..n+3 of packed input row m, bias added:
+// + residual, fp32 store, activation and compute-type store.
+template <typename T>
+__device__ __forceinline__ void epilogue4(const ConvArgs &p, int m, int n, f4 v)
+{
+    if (p.res) {
+        f4 rr = *(const f4 *)(p.res + (long)m * p.Cout + n);
+        v = v + rr;
+    }
+    long orow = (long)m * p.s;
+    if (p.out32)
+        *(f4 *)(p.out32 + orow * p.Cout + n) = v;
+    if (p.out16) {
+        int ch = n % p.Cout;
+        f4 y;
+        if (p.act == ACT_SNAKE) {
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                y[e] = act_fn(v[e], ACT_SNAKE, p.alpha[ch + e], p.inv_alpha[ch + e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                y[e] = act_fn(v[e], p.act, 0.f, 0.f);
+        }
+        int b = p.frame_stream[m / p.rate_in];
+        long base = ((long)(b + 1) * p.out_H + orow) * p.Cout + n;
+        store4<T>((T *)p.out16 + base, y);
+    }
+}
+
 // Contiguous tile range per XCD: bid % 8 is the XCD a work-group lands on.
 __device__ __forceinline__ int xcd_remap(int bid, int total)
 {
@@ -78,12 +115,13 @@ __device__ __forceinline__ int xcd_remap(int bid, int total)
     return x * q + (x < r ? x : r) + i;
 }
 
-template <typename T, int BM, int BN, int WM, int WN>
+template <typename T, int BM, int BN, int WM, int WN, int KSUB>
 __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
 {
-    constexpr int BK = Traits<T>::BK;
+    constexpr int BK0 = Traits<T>::BK;
+    constexpr int BK = BK0 * KSUB;
     constexpr int VEC = 16 / (int)sizeof(T);
-    constexpr int CPR = BK / VEC;  // 16-byte chunks per tile row (4)
+    constexpr int CPR = BK / VEC;  // 16-byte chunks per tile row
     constexpr int LD = BK + VEC;   // padded LDS row, elements
     constexpr int A_CH = BM * CPR, B_CH = BN * CPR;
     constexpr int A_PT = (A_CH + 255) / 256, B_PT = (B_CH + 255) / 256;
@@ -107,6 +145,12 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
     const int Ktot = p.taps * p.Cin;
     const T *A = (const T *)p.A;
     const T *W = (const T *)p.Wt;
+
+    // K range of this split (whole K without split-K)
+    const int nk_all = Ktot / BK;
+    const int per = (nk_all + p.splits - 1) / p.splits;
+    const int ks0 = blockIdx.y * per;
+    const int ks1 = ks0 + per < nk_all ? ks0 + per : nk_all;
 
     const T *a_ptr[A_PT];
     int a_lds[A_PT];
@@ -136,6 +180,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
     }
 
     Chunk ra[A_PT], rb[B_PT];
+    // a K stage of BK never straddles two taps (C_in is a multiple of BK)
     auto gload = [&](int ks) {
         int k0 = ks * BK;
         int tap = k0 / p.Cin;
@@ -174,64 +219,69 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
     const int rbase = wm * TM, cbase = wn * TN;
     const int lrow = lane & 15, lk = lane >> 4;
 
-    const int nk = Ktot / BK;
-    gload(0);
-    sstore(0);
+    if (ks0 < ks1) {
+        gload(ks0);
+        sstore(0);
+    }
     __syncthreads();
-    for (int ks = 0; ks < nk; ks++) {
-        const int buf = ks & 1;
-        if (ks + 1 < nk)
+    for (int ks = ks0; ks < ks1; ks++) {
+        const int buf = (ks - ks0) & 1;
+        if (ks + 1 < ks1)
             gload(ks + 1);
         const T *Ab = As + buf * BM * LD;
         const T *Bb = Bs + buf * BN * LD;
-        if constexpr (sizeof(T) == 2) {
-            h8 af[FM], bf[FN];
 #pragma unroll
-            for (int i = 0; i < FM; i++)
-                af[i] = *(const h8 *)(Ab + (rbase + i * 16 + lrow) * LD + lk * 8);
+        for (int sub = 0; sub < KSUB; sub++) {
+            if constexpr (sizeof(T) == 2) {
+                h8 af[FM], bf[FN];
 #pragma unroll
-            for (int j = 0; j < FN; j++)
-                bf[j] = *(const h8 *)(Bb + (cbase + j * 16 + lrow) * LD + lk * 8);
-#pragma unroll
-            for (int i = 0; i < FM; i++)
+                for (int i = 0; i < FM; i++)
+                    af[i] = *(const h8 *)(Ab + (rbase + i * 16 + lrow) * LD + sub * 32 + lk * 8);
 #pragma unroll
                 for (int j = 0; j < FN; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0,
-                                                                       0, 0);
-        } else {
-            f4 af[FM], bf[FN];
-#pragma unroll
-            for (int i = 0; i < FM; i++)
-                af[i] = *(const f4 *)(Ab + (rbase + i * 16 + lrow) * LD + lk * 4);
-#pragma unroll
-            for (int j = 0; j < FN; j++)
-                bf[j] = *(const f4 *)(Bb + (cbase + j * 16 + lrow) * LD + lk * 4);
-#pragma unroll
-            for (int kk = 0; kk < 4; kk++)
+                    bf[j] = *(const h8 *)(Bb + (cbase + j * 16 + lrow) * LD + sub * 32 + lk * 8);
 #pragma unroll
                 for (int i = 0; i < FM; i++)
 #pragma unroll
                     for (int j = 0; j < FN; j++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][kk], bf[j][kk],
-                                                                         acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j],
+                                                                           acc[i][j], 0, 0, 0);
+            } else {
+                f4 af[FM], bf[FN];
+#pragma unroll
+                for (int i = 0; i < FM; i++)
+                    af[i] = *(const f4 *)(Ab + (rbase + i * 16 + lrow) * LD + sub * 16 + lk * 4);
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+                    bf[j] = *(const f4 *)(Bb + (cbase + j * 16 + lrow) * LD + sub * 16 + lk * 4);
+#pragma unroll
+                for (int kk = 0; kk < 4; kk++)
+#pragma unroll
+                    for (int i = 0; i < FM; i++)
+#pragma unroll
+                        for (int j = 0; j < FN; j++)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                af[i][kk], bf[j][kk], acc[i][j], 0, 0, 0);
+            }
         }
-        if (ks + 1 < nk)
+        if (ks + 1 < ks1)
             sstore(buf ^ 1);
         __syncthreads();
     }
 
-    // ---- epilogue: bias into an LDS tile, then row-contiguous 16-byte stores
+    // ---- epilogue: through an LDS tile, then row-contiguous 16-byte stores
+    const bool split = p.splits > 1;
     float *epi = (float *)smem;
 #pragma unroll
     for (int i = 0; i < FM; i++)
 #pragma unroll
         for (int j = 0; j < FN; j++) {
             int c = cbase + j * 16 + lrow;
-            float bv = p.bias[(n0 + c) % p.Cout];
+            float bv = split ? 0.f : p.bias[(n0 + c) % p.Cout];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 int r = rbase + i * 16 + lk * 4 + e;
-                epi[r * ELD + c] = acc[i][j][e] + bv;
+                epi[r * ELD + c] = split ? acc[i][j][e] : acc[i][j][e] + bv;
             }
         }
     __syncthreads();
@@ -243,74 +293,93 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
             continue;
         int n = n0 + cq;
         f4 v = *(const f4 *)(epi + r * ELD + cq);
-        if (p.res) {
-            f4 rr = *(const f4 *)(p.res + (long)m * p.Cout + n);
-            v = v + rr;
-        }
-        long orow = (long)m * p.s;
-        if (p.out32)
-            *(f4 *)(p.out32 + orow * p.Cout + n) = v;
-        if (p.out16) {
-            int ch = n % p.Cout;
-            f4 y;
-            if (p.act == ACT_SNAKE) {
-#pragma unroll
-                for (int e = 0; e < 4; e++)
-                    y[e] = act_fn(v[e], ACT_SNAKE, p.alpha[ch + e], p.inv_alpha[ch + e]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; e++)
-                    y[e] = act_fn(v[e], p.act, 0.f, 0.f);
-            }
-            int b = p.frame_stream[m / p.rate_in];
-            long base = ((long)(b + 1) * p.out_H + orow) * p.Cout + n;
-            store4<T>((T *)p.out16 + base, y);
-        }
+        if (split)
+            *(f4 *)(p.partial + ((long)blockIdx.y * p.M + m) * p.N + n) = v;
+        else
+            epilogue4<T>(p, m, n, v);
     }
 }
 
+// Sum of the split-K partials in split order, + bias, then the epilogue.
+template <typename T>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(ConvArgs p)
+{
+    const long q = (long)blockIdx.x * 256 + threadIdx.x;
+    const long nq = (long)p.M * (p.N / 4);
+    if (q >= nq)
+        return;
+    const int m = (int)(q / (p.N / 4));
+    const int n = (int)(q - (long)m * (p.N / 4)) * 4;
+    const long stride = (long)p.M * p.N;
+    f4 v = *(const f4 *)(p.partial + (long)m * p.N + n);
+    for (int s = 1; s < p.splits; s++)
+        v = v + *(const f4 *)(p.partial + s * stride + (long)m * p.N + n);
+    const int ch = n % p.Cout;
+    v = v + f4{p.bias[ch], p.bias[ch + 1], p.bias[ch + 2], p.bias[ch + 3]};
+    epilogue4<T>(p, m, n, v);
+}
+
 struct TileDesc {
-    int BM, BN;
+    int BM, BN, BK;
     const char *name;
 };
 
 // fp16 operand tiles, in order of preference
 const TileDesc H_TILES[] = {
-    {128, 128, "h128x128"}, {256, 64, "h256x64"}, {128, 64, "h128x64"}, {256, 32, "h256x32"},
-    {64, 64, "h64x64"},     {128, 32, "h128x32"}, {32, 64, "h32x64"},   {64, 32, "h64x32"},
+    {128, 128, 64, "h128x128k64"}, {128, 64, 64, "h128x64k64"}, {64, 128, 64, "h64x128k64"},
+    {64, 64, 64, "h64x64k64"},     {256, 32, 32, "h256x32"},    {128, 32, 32, "h128x32"},
+    {32, 64, 32, "h32x64"},        {64, 32, 32, "h64x32"},
 };
 const TileDesc F_TILES[] = {
-    {64, 64, "f64x64"}, {128, 32, "f128x32"}, {64, 32, "f64x32"}, {64, 16, "f64x16"},
+    {64, 64, 16, "f64x64"}, {128, 32, 16, "f128x32"}, {64, 32, 16, "f64x32"}, {64, 16, 16, "f64x16"},
 };
 constexpr int NH = sizeof(H_TILES) / sizeof(H_TILES[0]);
 constexpr int NF = sizeof(F_TILES) / sizeof(F_TILES[0]);
 
-template <typename T, int BM, int BN, int WM, int WN>
+template <typename T, int BM, int BN, int WM, int WN, int KSUB>
 hipError_t launch_t(const ConvArgs &a, hipStream_t st)
 {
     int ntm = (a.M + BM - 1) / BM, ntn = a.N / BN;
-    hipLaunchKernelGGL((conv_gemm_kernel<T, BM, BN, WM, WN>), dim3(ntm * ntn), dim3(256), 0, st,
-                       a);
+    hipLaunchKernelGGL((conv_gemm_kernel<T, BM, BN, WM, WN, KSUB>), dim3(ntm * ntn, a.splits),
+                       dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int conv_gemm_tile_choice(const ConvArgs &a, int dtype)
+// Tile and split count for a launch: the preferred tile that gives at least
+// two work-groups per CU; failing that, split K (at least 8 K stages per
+// split, partials within the workspace) until the CUs are covered.
+ConvPlan conv_gemm_plan(const ConvArgs &a, int dtype, int n_cu, long partial_cap)
 {
     const TileDesc *t = dtype ? H_TILES : F_TILES;
-    int n = dtype ? NH : NF;
-    int best = -1;
-    long best_tiles = -1;
+    const int n = dtype ? NH : NF;
+    const int Ktot = a.taps * a.Cin;  // a K stage must not straddle two taps
+    ConvPlan best{-1, 1};
+    long best_work = -1;
     for (int i = 0; i < n; i++) {
-        if (a.N % t[i].BN != 0)
+        if (a.N % t[i].BN != 0 || a.Cin % t[i].BK != 0)
             continue;
         long tiles = (long)((a.M + t[i].BM - 1) / t[i].BM) * (a.N / t[i].BN);
-        if (tiles >= 512)
-            return i;
-        if (tiles > best_tiles) {
-            best_tiles = tiles;
-            best = i;
+        if (tiles >= 2L * n_cu)
+            return ConvPlan{i, 1};
+        if (tiles > best_work) {
+            best_work = tiles;
+            best = ConvPlan{i, 1};
+        }
+    }
+    if (a.splits_allowed && partial_cap > 0) {
+        for (int i = 0; i < n; i++) {
+            if (a.N % t[i].BN != 0 || a.Cin % t[i].BK != 0)
+                continue;
+            long tiles = (long)((a.M + t[i].BM - 1) / t[i].BM) * (a.N / t[i].BN);
+            int nk = Ktot / t[i].BK;
+            for (int sp = 2; sp <= 8; sp++) {
+                if (nk / sp < 8 || (long)sp * a.M * a.N > partial_cap)
+                    break;
+                if (tiles * sp >= (long)n_cu)
+                    return ConvPlan{i, sp};
+            }
         }
     }
     return best;
@@ -323,34 +392,43 @@ const char *conv_gemm_tile_name(int dtype, int tile)
     return dtype ? H_TILES[tile].name : F_TILES[tile].name;
 }
 
-hipError_t launch_conv_gemm(const ConvArgs &a, int dtype, hipStream_t st, int tile)
+hipError_t launch_conv_gemm(const ConvArgs &a0, int dtype, hipStream_t st, ConvPlan plan)
 {
-    if (a.M <= 0)
+    if (a0.M <= 0)
         return hipSuccess;
-    if (tile < 0)
-        tile = conv_gemm_tile_choice(a, dtype);
-    if (tile < 0)
+    if (plan.tile < 0)
         return hipErrorInvalidValue;
+    ConvArgs a = a0;
+    a.splits = plan.splits > 1 ? plan.splits : 1;
+    hipError_t e = hipErrorInvalidValue;
     if (dtype) {
-        switch (tile) {
-        case 0: return launch_t<half_t, 128, 128, 2, 2>(a, st);
-        case 1: return launch_t<half_t, 256, 64, 4, 1>(a, st);
-        case 2: return launch_t<half_t, 128, 64, 2, 2>(a, st);
-        case 3: return launch_t<half_t, 256, 32, 4, 1>(a, st);
-        case 4: return launch_t<half_t, 64, 64, 2, 2>(a, st);
-        case 5: return launch_t<half_t, 128, 32, 4, 1>(a, st);
-        case 6: return launch_t<half_t, 32, 64, 2, 2>(a, st);
-        case 7: return launch_t<half_t, 64, 32, 4, 1>(a, st);
+        switch (plan.tile) {
+        case 0: e = launch_t<half_t, 128, 128, 2, 2, 2>(a, st); break;
+        case 1: e = launch_t<half_t, 128, 64, 2, 2, 2>(a, st); break;
+        case 2: e = launch_t<half_t, 64, 128, 2, 2, 2>(a, st); break;
+        case 3: e = launch_t<half_t, 64, 64, 2, 2, 2>(a, st); break;
+        case 4: e = launch_t<half_t, 256, 32, 4, 1, 1>(a, st); break;
+        case 5: e = launch_t<half_t, 128, 32, 4, 1, 1>(a, st); break;
+        case 6: e = launch_t<half_t, 32, 64, 2, 2, 1>(a, st); break;
+        case 7: e = launch_t<half_t, 64, 32, 4, 1, 1>(a, st); break;
         }
     } else {
-        switch (tile) {
-        case 0: return launch_t<float, 64, 64, 2, 2>(a, st);
-        case 1: return launch_t<float, 128, 32, 4, 1>(a, st);
-        case 2: return launch_t<float, 64, 32, 4, 1>(a, st);
-        case 3: return launch_t<float, 64, 16, 4, 1>(a, st);
+        switch (plan.tile) {
+        case 0: e = launch_t<float, 64, 64, 2, 2, 1>(a, st); break;
+        case 1: e = launch_t<float, 128, 32, 4, 1, 1>(a, st); break;
+        case 2: e = launch_t<float, 64, 32, 4, 1, 1>(a, st); break;
+        case 3: e = launch_t<float, 64, 16, 4, 1, 1>(a, st); break;
         }
     }
-    return hipErrorInvalidValue;
+    if (e != hipSuccess || a.splits == 1)
+        return e;
+    long nq = (long)a.M * (a.N / 4);
+    dim3 grid((unsigned)((nq + 255) / 256));
+    if (dtype)
+        hipLaunchKernelGGL(splitk_reduce_kernel<half_t>, grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(splitk_reduce_kernel<float>, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
 }
 
 }  // namespace snrvq
