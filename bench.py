@@ -57,6 +57,23 @@ def layer_model(cfg: dict) -> dict:
             m[f"s{i}.ru{j}.conv1"] = dict(fpr=2 * co * co, bpr=es * co + 4 * co + out,
                                           wpl=es * co * co)
     m["final_conv"] = dict(fpr=2 * 7 * ch[-1], bpr=es * ch[-1] + 4, wpl=0)
+    # a fused stage counts its output rows: the ConvT's input row is shared by
+    # s output rows; only the stage input and output cross HBM (the last
+    # stage writes PCM instead of the next stage's operand)
+    S = len(cfg["strides"])
+    for i, s in enumerate(cfg["strides"]):
+        ci, co = ch[i], ch[i + 1]
+        t = m[f"s{i}.convT"]
+        fpr = t["fpr"] / s + sum(m[f"s{i}.ru{j}.conv7"]["fpr"] + m[f"s{i}.ru{j}.conv1"]["fpr"]
+                                 for j in range(2))
+        wpl = t["wpl"] + sum(m[f"s{i}.ru{j}.conv7"]["wpl"] + m[f"s{i}.ru{j}.conv1"]["wpl"]
+                             for j in range(2))
+        if i == S - 1:
+            fpr += m["final_conv"]["fpr"]
+            bpr = es * ci / s + 4
+        else:
+            bpr = es * ci / s + es * co
+        m[f"s{i}.fused"] = dict(fpr=fpr, bpr=bpr, wpl=wpl)
     return m
 
 
@@ -104,6 +121,193 @@ def cpu_baseline(cfg: dict, weights: dict, budget_s: float) -> dict:
             "audio_sec_per_s": frames / dt / fr}
 
 
+def step_indices(warmup: int, steps: int, profiled: bool) -> list:
+    """Chunk-schedule indices of the decode steps a run dispatches, in order:
+    warmup, timed (codes in HBM), profiled (unless skipped), host codes."""
+    idx = list(range(warmup + steps))
+    if profiled:
+        idx += list(range(warmup + steps, warmup + 2 * steps))
+    return idx + list(range(warmup + 2 * steps, warmup + 3 * steps))
+
+
+def kernel_class(name: str, cfg: dict) -> str:
+    """Library launch class of a dispatched kernel name, as the library's own
+    profiler names it, where the name alone decides it."""
+    import re
+    import rvq_inputs as RI
+    mm = re.search(r"stage_kernel<(\d+), (\d+), (\d+), (true|false)", name)
+    if mm:
+        C, S = int(mm.group(1)), int(mm.group(2))
+        ch = RI.channels(cfg)
+        for i, st in enumerate(cfg["strides"]):
+            if ch[i + 1] == C and st == S:
+                return f"s{i}.fused"
+    for key, cls in (("halo_save", "halo_save"), ("halo_fill", "halo_fill"),
+                     ("rvq_gather", "rvq_gather"), ("final_conv", "final_conv")):
+        if key in name:
+            return cls
+    return ""
+
+
+def _steady(rows: list, n_steps: int) -> list:
+    """Dispatches of the decode steps: everything after the last prefill
+    call, whose end is marked by its state save (one per decode call)."""
+    saves = sorted(int(r["Dispatch_Id"]) for r in rows if "halo_save" in r["Kernel_Name"])
+    if len(saves) < n_steps:
+        raise SystemExit("trace holds fewer decode calls than the run's steps")
+    first = saves[len(saves) - n_steps - 1] if len(saves) > n_steps else 0
+    return [r for r in rows if int(r["Dispatch_Id"]) > first]
+
+
+def rocprof_summary(args) -> int:
+    """Text summary of a rocprofv3 kernel trace of this benchmark, and of two
+    counter runs (FETCH_SIZE, WRITE_SIZE) scaled by the same counters of a
+    plain negation kernel of known size."""
+    import csv
+    import hashlib
+    import rvq_inputs as RI
+    cfg = RI.get_config(args.config)
+    lm = layer_model(cfg)
+    rate = [1]
+    for st in cfg["strides"]:
+        rate.append(rate[-1] * st)
+    out = []
+    res = {"config": args.config}
+    if args.kt:
+        rows = list(csv.DictReader(open(os.path.join(args.kt, "kt_kernel_trace.csv"))))
+        idx = step_indices(args.kt_warmup, args.kt_steps, True)
+        st = _steady(rows, len(idx))
+        agg = {}
+        for r in st:
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            a = agg.setdefault(r["Kernel_Name"], [0, 0.0])
+            a[0] += 1
+            a[1] += d
+        tot = sum(v[1] for v in agg.values())
+        out.append(f"## Kernel time over the {len(idx)} decode steps "
+                   f"({len(st)} dispatches; setup and prefill excluded)\n")
+        out.append("| kernel | class | calls | avg us | total ms | % |")
+        out.append("|---|---|---:|---:|---:|---:|")
+        res["kernels"] = {}
+        for k, (n, t) in sorted(agg.items(), key=lambda kv: -kv[1][1])[:args.top]:
+            cls = kernel_class(k, cfg)
+            short = k if len(k) < 90 else k[:87] + "..."
+            out.append(f"| `{short}` | {cls} | {n} | {t / n:.1f} | {t / 1e3:.3f} | "
+                       f"{100 * t / tot:.1f} |")
+            if cls:
+                res["kernels"][cls] = {"calls": n, "avg_us": round(t / n, 2)}
+        out.append(f"\nSum over the steps: {tot / 1e3:.3f} ms, {tot / len(idx):.1f} us per step.\n")
+        logs = [os.path.join(args.kt, "..", f) for f in ("kt_bench.log",)]
+        if args.kt_json or os.path.exists(logs[0]):
+            lines = open(args.kt_json or logs[0]).read().splitlines()
+            rec = json.loads([ln for ln in lines if ln.startswith("{")][-1])
+            ks = rec.get("kernels", {})
+            out.append("The same run's own HIP-event timing (its profiled pass of "
+                       f"{args.kt_steps} steps), for the classes named above:\n")
+            out.append("| class | rocprofv3 avg us | HIP events avg us |")
+            out.append("|---|---:|---:|")
+            for cls, v in res["kernels"].items():
+                if cls in ks:
+                    out.append(f"| {cls} | {v['avg_us']:.1f} | {ks[cls]['avg_us']:.1f} |")
+            res["bench_value"] = rec.get("value")
+            out.append(f"\nThat run's throughput under the tracer: {rec.get('value')} frames/s.\n")
+        stats = os.path.join(args.kt, "kt_kernel_stats.csv")
+        if os.path.exists(stats):
+            srows = list(csv.DictReader(open(stats)))[:8]
+            out.append("`--stats` over the whole process (setup and prefill included):\n")
+            out.append("| kernel | calls | avg us | % |")
+            out.append("|---|---:|---:|---:|")
+            for r in srows:
+                k = r["Name"] if len(r["Name"]) < 90 else r["Name"][:87] + "..."
+                out.append(f"| `{k}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                           f"{r['Percentage']} |")
+            out.append("")
+    if args.pmc_fetch and args.pmc_write:
+        idx = step_indices(args.pmc_warmup, args.pmc_steps, False)
+        frames = [int(RI.c4_chunk_sizes(cfg, j).sum()) for j in idx]
+        res["copy_mib"] = args.copy_mib
+        per_cls = {}
+        for tag, path in (("FETCH_SIZE", args.pmc_fetch), ("WRITE_SIZE", args.pmc_write)):
+            fn = [f for f in os.listdir(path) if f.endswith("counter_collection.csv")][0]
+            rows = [r for r in csv.DictReader(open(os.path.join(path, fn)))
+                    if r["Counter_Name"] == tag]
+            neg = [r for r in rows if "neg_kernel" in r["Kernel_Name"]]
+            if len(neg) != 1:
+                raise SystemExit(f"{tag}: expected one negation dispatch, found {len(neg)}")
+            factor = args.copy_mib * 1024.0 / float(neg[0]["Counter_Value"])
+            res[f"{tag}_factor"] = round(factor, 4)
+            st = _steady(rows, len(idx))
+            seen = {}
+            for r in st:
+                cls = kernel_class(r["Kernel_Name"], cfg)
+                if not cls.endswith(".fused"):
+                    continue
+                j = seen.get(cls, 0)
+                seen[cls] = j + 1
+                i = int(cls[1:cls.index(".")])
+                units = frames[j] * rate[i + 1]
+                c = per_cls.setdefault(cls, {"units": 0, "FETCH_SIZE": 0.0, "WRITE_SIZE": 0.0,
+                                             "raw": {}})
+                if tag == "FETCH_SIZE":
+                    c["units"] += units
+                c[tag] += float(r["Counter_Value"]) * 1024.0 * factor
+                c["raw"].setdefault(tag, []).append(float(r["Counter_Value"]))
+        out.append("## HBM traffic of the fused stage kernels\n")
+        out.append(f"Calibration: for one negation kernel that reads and writes {args.copy_mib} "
+                   f"MiB, FETCH_SIZE times {res['FETCH_SIZE_factor']} and WRITE_SIZE times "
+                   f"{res['WRITE_SIZE_factor']} give the known size; the counters below are "
+                   "scaled by these factors.\n")
+        out.append("| class | dispatches | output rows | fetch B/row | write B/row | "
+                   "total B/row | algorithmic B/row |")
+        out.append("|---|---:|---:|---:|---:|---:|---:|")
+        res["traffic"] = {}
+        for cls, c in sorted(per_cls.items()):
+            f, w = c["FETCH_SIZE"] / c["units"], c["WRITE_SIZE"] / c["units"]
+            n = len(c["raw"]["FETCH_SIZE"])
+            alg = lm[cls]["bpr"] + lm[cls]["wpl"] * n / c["units"]
+            out.append(f"| {cls} | {n} | {c['units']} | {f:.1f} | {w:.1f} | {f + w:.1f} | "
+                       f"{alg:.1f} |")
+            res["traffic"][cls] = {"bytes_per_unit": round(f + w, 3)}
+        src = os.path.join(ROOT, "streaming_neural_audio_rvq_amd", "csrc")
+        h = hashlib.sha256()
+        for fn in ("kernels_stage.hip", "internal.h"):
+            h.update(open(os.path.join(src, fn), "rb").read())
+        res["stage_source_sha256"] = h.hexdigest()
+        out.append("\nThe traffic holds for the kernel source whose SHA-256 (kernels_stage.hip "
+                   "then internal.h) is recorded below; bench.py reports it only while the "
+                   "source matches.\n")
+    out.append("```json\n" + json.dumps(res, indent=1) + "\n```")
+    text = "\n".join(out) + "\n"
+    if args.rocprof_summary == "-":
+        print(text)
+    else:
+        with open(args.rocprof_summary, "a") as fh:
+            fh.write(text)
+    return 0
+
+
+def stored_traffic(cls: str, units_per_launch: float):
+    """HBM bytes per launch of a fused stage class from the committed counter
+    summary, or None when absent or taken from other kernel source."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "stage_fused__qwen_128_streams__hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    mm = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not mm:
+        return None
+    rec = json.loads(mm.group(1))
+    src = os.path.join(ROOT, "streaming_neural_audio_rvq_amd", "csrc")
+    h = hashlib.sha256()
+    for fn in ("kernels_stage.hip", "internal.h"):
+        h.update(open(os.path.join(src, fn), "rb").read())
+    t = rec.get("traffic", {}).get(cls)
+    if rec.get("stage_source_sha256") != h.hexdigest() or not t:
+        return None
+    return t["bytes_per_unit"] * units_per_launch
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,7 +317,25 @@ def main() -> int:
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run one plain streaming kernel (negation) that reads and "
+                         "writes this many MiB: the known-size reference for HBM counters")
+    ap.add_argument("--rocprof-summary", metavar="OUT",
+                    help="summarise rocprofv3 output of earlier runs of this benchmark "
+                         "into OUT (appended; '-' prints) instead of running")
+    ap.add_argument("--kt", help="rocprofv3 --kernel-trace output directory")
+    ap.add_argument("--kt-steps", type=int, default=16)
+    ap.add_argument("--kt-json", help="the traced run's output (default: kt_bench.log "
+                                      "beside the trace directory)")
+    ap.add_argument("--kt-warmup", type=int, default=2)
+    ap.add_argument("--pmc-fetch", help="rocprofv3 --pmc FETCH_SIZE output directory")
+    ap.add_argument("--pmc-write", help="rocprofv3 --pmc WRITE_SIZE output directory")
+    ap.add_argument("--pmc-steps", type=int, default=2)
+    ap.add_argument("--pmc-warmup", type=int, default=1)
+    ap.add_argument("--top", type=int, default=30)
     args = ap.parse_args()
+    if args.rocprof_summary:
+        return rocprof_summary(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build decodes on one GPU only (asked for --gpus {args.gpus}, "
@@ -125,6 +347,14 @@ def main() -> int:
 
     import rvq_inputs as RI
     import streaming_neural_audio_rvq_amd as snr
+
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     cfg = RI.get_config(args.config)
     w = RI.make_weights(cfg)
@@ -219,6 +449,10 @@ def main() -> int:
             ach = d["flops_per_launch"] / sec / 1e12
             roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_f,
                     "unit": "TFLOP/s", "frac": round(ach / peak_f, 4), "traffic": None}
+        if dom.endswith(".fused"):
+            roof["traffic"] = stored_traffic(dom, d["units"] / d["launches"])
+            if roof["traffic"] is not None:
+                roof["traffic"] = int(roof["traffic"])
         roof["kernel"] = dom
         roof["avg_launch_us"] = round(d["avg_us"], 2)
         roof["alg_bytes_per_launch"] = int(d["bytes_per_launch"])
