@@ -91,33 +91,108 @@ def flops_per_frame(cfg: dict) -> float:
     return float(tot)
 
 
-def cpu_baseline(cfg: dict, weights: dict, budget_s: float) -> dict:
-    """The fp64 oracle on a bounded sample of the same workload: 8 streams
-    decoding their per-step chunks (drawn from the same buckets), in
-    parallel across streams, for about budget_s seconds of CPU time."""
+WORKLOADS = {
+    "c2": "8 streams in lockstep, 8 new frames each per step (F = 64), 16x2048 codebooks, "
+          "hop 1920 @ 24 kHz, bf16 random weights",
+    "c3": "64 streams in lockstep, 8 new frames each per step (F = 512), 10x1024 codebooks, "
+          "4-layer windowed transformer, hop 2048 @ 44.1 kHz, bf16 random weights",
+    "c4": "128 streams at offsets 0..500, chunks from {1,2,4,8,16} per stream per step, "
+          "16x2048 codebooks, hop 1920 @ 24 kHz, bf16 random weights",
+    "c5": "offline: 128 whole utterances of 50..500 frames (valid frames only, no padding), "
+          "calls grouping whole utterances up to 16,000 frames, fresh streams; "
+          "a step decodes all 128",
+}
+
+
+def make_workload(name: str, cfg: dict, codec, total_steps: int, stream) -> dict:
+    """Per step, the decode calls (stream ids or None for fresh streams, new
+    frames per stream, host codes, the same codes in HBM); streams opened and
+    prefilled here, untimed."""
+    import torch
+    import rvq_inputs as RI
+    dev = torch.device("cuda:0")
+    Bn = cfg["n_streams"]
+
+    def call(ids, n, codes):
+        n = np.asarray(n, np.int32)
+        return (ids, n, codes, torch.from_numpy(codes).to(dev))
+
+    steps = []
+    if name == "c4":
+        off = RI.c4_offsets(cfg)
+        ids = [codec.stream_open() for _ in range(Bn)]
+        for b in range(Bn):
+            if off[b]:
+                codec.stream_prefill(ids[b], RI.stream_codes(cfg, b, int(off[b]), part=0), stream)
+        for j in range(total_steps):
+            n = RI.c4_chunk_sizes(cfg, j)
+            codes = np.concatenate([RI.stream_codes(cfg, b, int(n[b]), part=1 + j)
+                                    for b in range(Bn)])
+            steps.append([call(ids, n, codes)])
+    elif name in ("c2", "c3"):
+        ids = [codec.stream_open() for _ in range(Bn)]
+        for j in range(total_steps):
+            codes = np.concatenate([RI.stream_codes(cfg, b, 8, part=1 + j) for b in range(Bn)])
+            steps.append([call(ids, [8] * Bn, codes)])
+    elif name == "c5":
+        lens = RI.c5_lengths(cfg)
+        maxF = cfg["max_frames_per_call"]
+        calls, b0 = [], 0
+        while b0 < Bn:
+            b1, tot = b0, 0
+            while b1 < Bn and tot + lens[b1] <= maxF:
+                tot += int(lens[b1])
+                b1 += 1
+            codes = np.concatenate([RI.stream_codes(cfg, b, int(lens[b]), part=0)
+                                    for b in range(b0, b1)])
+            calls.append(call(None, lens[b0:b1], codes))
+            b0 = b1
+        steps = [calls] * total_steps
+    else:
+        raise SystemExit(f"bench.py: no workload for config {name!r}")
+    return {"steps": steps, "desc": f"{name}: {WORKLOADS[name]}", "streams": Bn}
+
+
+def cpu_baseline(name: str, cfg: dict, weights: dict, budget_s: float) -> dict:
+    """The fp64 oracle on a bounded sample of the same workload, for about
+    budget_s seconds, parallel across streams: 8 streams decoding per-step
+    chunks drawn like the workload's (streamed workloads), or whole
+    utterances one after another (offline workload)."""
     import oracle
     import rvq_inputs as RI
     m = oracle.Model(cfg, weights)
-    nb = 8
-    streams = [m.stream() for _ in range(nb)]
     frames = 0
     t0 = time.perf_counter()
     step = 0
-    while True:
-        n = RI.c4_chunk_sizes(cfg, step)[:nb]
-        codes = np.concatenate([RI.stream_codes(cfg, b, int(n[b]), part=1 + step)
-                                for b in range(nb)])
-        m.decode_batch(streams, n, codes)
-        frames += int(n.sum())
-        step += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
+    if name == "c5":
+        lens = RI.c5_lengths(cfg)
+        while True:
+            b = step % len(lens)
+            m.stream().decode(RI.stream_codes(cfg, b, int(lens[b]), part=0))
+            frames += int(lens[b])
+            step += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        sample = f"{step} whole utterances ({frames} frames)"
+    else:
+        nb = 8
+        streams = [m.stream() for _ in range(nb)]
+        while True:
+            n = (RI.c4_chunk_sizes(cfg, step)[:nb] if name == "c4"
+                 else np.full(nb, 8, np.int32))
+            codes = np.concatenate([RI.stream_codes(cfg, b, int(n[b]), part=1 + step)
+                                    for b in range(nb)])
+            m.decode_batch(streams, n, codes)
+            frames += int(n.sum())
+            step += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        sample = f"{nb} streams x {step} steps of the workload's chunks ({frames} frames)"
     dt = time.perf_counter() - t0
-    fr = RI.get_config("c2")["sample_rate"] / RI.hop(cfg)
+    fr = cfg["sample_rate"] / RI.hop(cfg)
     return {"value": frames / dt, "unit": "frames/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{nb} streams x {step} steps of bucketed chunks ({frames} frames, "
-                      f"{dt:.1f} s), fp64, parallel across streams",
+            "sample": f"{sample}, {dt:.1f} s, fp64, parallel across streams and channels",
             "audio_sec_per_s": frames / dt / fr}
 
 
@@ -223,6 +298,8 @@ def rocprof_summary(args) -> int:
                            f"{r['Percentage']} |")
             out.append("")
     if args.pmc_fetch and args.pmc_write:
+        if args.config != "c4":
+            raise SystemExit("counter summaries are built for the 128-stream workload only")
         idx = step_indices(args.pmc_warmup, args.pmc_steps, False)
         frames = [int(RI.c4_chunk_sizes(cfg, j).sum()) for j in idx]
         res["copy_mib"] = args.copy_mib
@@ -360,41 +437,44 @@ def main() -> int:
     w = RI.make_weights(cfg)
     codec = snr.Codec(cfg, RI.weight_bits(w))
     hop = codec.hop
-    Bn = cfg["n_streams"]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
 
-    # ---- setup (untimed): open streams, prefill staggered offsets ----
-    off = RI.c4_offsets(cfg)
-    ids = [codec.stream_open() for _ in range(Bn)]
-    for b in range(Bn):
-        if off[b]:
-            codec.stream_prefill(ids[b], RI.stream_codes(cfg, b, int(off[b]), part=0), stream)
     # steps: warmup, timed (codes resident in HBM), profiled, host-codes
     total_steps = args.warmup + 3 * args.steps
-    sizes = [RI.c4_chunk_sizes(cfg, j) for j in range(total_steps)]
-    packed = [np.concatenate([RI.stream_codes(cfg, b, int(sizes[j][b]), part=1 + j)
-                              for b in range(Bn)]) for j in range(total_steps)]
-    packed_dev = [torch.from_numpy(p).to(dev) for p in packed]
+    wl = make_workload(args.config, cfg, codec, total_steps, stream)
     pcm = torch.empty(cfg["max_frames_per_call"] * hop, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
+    def run_step(j, host_codes=False):
+        for ids, n, codes, codes_dev in wl["steps"][j]:
+            fresh = ids is None
+            if fresh:
+                ids = [codec.stream_open() for _ in range(len(n))]
+            if host_codes:
+                codec.decode_chunk(ids, n, codes, pcm, stream)
+            else:
+                codec.decode_chunk_device(ids, n, codes_dev, pcm, stream)
+            if fresh:
+                for i in ids:
+                    codec.stream_close(i)
+
+    def step_frames(j):
+        return int(sum(int(np.sum(n)) for _, n, _, _ in wl["steps"][j]))
+
     for j in range(args.warmup):
-        codec.decode_chunk_device(ids, sizes[j], packed_dev[j], pcm, stream)
+        run_step(j)
     torch.cuda.synchronize()
 
     def timed_run(steps, host_codes: bool):
-        fr = int(sum(sizes[j].sum() for j in steps))
+        fr = sum(step_frames(j) for j in steps)
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         ev0.record(stream)
         for j in steps:
-            if host_codes:
-                codec.decode_chunk(ids, sizes[j], packed[j], pcm, stream)
-            else:
-                codec.decode_chunk_device(ids, sizes[j], packed_dev[j], pcm, stream)
+            run_step(j, host_codes)
         ev1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -419,7 +499,7 @@ def main() -> int:
         codec.profile_read()
         p_steps = range(args.warmup + args.steps, args.warmup + 2 * args.steps)
         for j in p_steps:
-            codec.decode_chunk_device(ids, sizes[j], packed_dev[j], pcm, stream)
+            run_step(j)
         torch.cuda.synchronize()
         prof = codec.profile_read()
         codec.profile_enable(False)
@@ -461,7 +541,7 @@ def main() -> int:
     fpf = flops_per_frame(cfg)
     peak_f = PEAK_F16_TFLOPS if cfg["weight_dtype"] == "bf16" else PEAK_F32_TFLOPS
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.config == "c4" else f"codec frames/s ({args.config})",
         "value": round(fps, 1),
         "unit": "frames/s",
         "n_gpus": 1,
@@ -473,17 +553,15 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f16" if cfg["weight_dtype"] == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": f"{args.config}: {Bn} streams at offsets 0..500, chunks from "
-                               "{1,2,4,8,16} per stream per step, 16x2048 codebooks, "
-                               "hop 1920 @ 24 kHz, bf16 random weights",
-                   "streams": Bn, "frames_timed": frames, "mean_frames_per_step": frames / args.steps},
+        "config": {"workload": wl["desc"], "streams": wl["streams"], "frames_timed": frames,
+                   "mean_frames_per_step": frames / args.steps},
         "audio_sec_per_s": round(fps / frame_rate, 1),
         "host_codes_frames_per_s": round(h_frames / h_elapsed, 1),
         "mfma_util_alg": round(fps * fpf / (peak_f * 1e12), 4),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, w, args.cpu_baseline_seconds)
+        out["cpu_baseline"] = cpu_baseline(args.config, cfg, w, args.cpu_baseline_seconds)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 2)
     if kernels:
         out["kernels"] = {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)

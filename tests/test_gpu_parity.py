@@ -201,31 +201,43 @@ def test_c4_full_scale_sampled_parity():
     for b in range(Bn):
         if off[b]:
             c.stream_prefill(ids[b], hist[b])
-    last = None
+    # sampled streams: the smallest and largest offsets, one stream per chunk
+    # bucket of the last step, the rest seeded; every step of each is checked
+    n_last = RI.c4_chunk_sizes(cfg, steps - 1)
+    sample = {int(np.argmin(off)), int(np.argmax(off))}
+    sample |= {int(np.flatnonzero(n_last == v)[0]) for v in cfg["buckets"]}
+    for b in np.random.default_rng(3).permutation(Bn):
+        if len(sample) >= 8:
+            break
+        sample.add(int(b))
+    sample = sorted(sample)
+    outs = []
     for j in range(steps):
         n = RI.c4_chunk_sizes(cfg, j)
         step_codes = [RI.stream_codes(cfg, b, int(n[b]), part=1 + j) for b in range(Bn)]
         pcm = torch.empty(int(n.sum()) * c.hop, dtype=torch.float32, device="cuda")
         c.decode_chunk(ids, n, np.concatenate(step_codes), pcm)
+        starts = [hist[b].shape[0] for b in range(Bn)]
         for b in range(Bn):
             hist[b] = np.concatenate([hist[b], step_codes[b]])
-        last = (n, pcm.cpu().numpy())
-    n, host = last
+        outs.append((n, starts, pcm.cpu().numpy()))
     H = c.hop
     L = analytic_left_context(cfg) + 1
-    cu = np.concatenate([[0], np.cumsum(n)])
-    sample = sorted({int(np.argmin(off)), int(np.argmax(off))} |
-                    {int(b) for b in np.random.default_rng(3).choice(Bn, 6, replace=False)})
     m = oracle.Model(cfg, w)
-    for b in sample:
-        T = hist[b].shape[0]
-        start = T - int(n[b])
-        w0 = max(0, start - L)
-        ref = m.stream(w0).decode(hist[b][w0:])[(start - w0) * H:]
-        got = host[cu[b] * H:cu[b + 1] * H]
-        e, ac = rel_err(got, ref)
-        say(f"c4 stream {b} offset {off[b]} pos {start} n {n[b]}: err/peak {e:.3e} AC-rel {ac:.3e}")
-        assert e <= tol_for(cfg)
+    buckets = set()
+    for j, (n, starts, host) in enumerate(outs):
+        cu = np.concatenate([[0], np.cumsum(n)])
+        for b in sample:
+            start = starts[b]
+            w0 = max(0, start - L)
+            ref = m.stream(w0).decode(hist[b][w0:start + int(n[b])])[(start - w0) * H:]
+            got = host[cu[b] * H:cu[b + 1] * H]
+            e, ac = rel_err(got, ref)
+            say(f"c4 step {j} stream {b} offset {off[b]} pos {start} n {n[b]}: "
+                f"err/peak {e:.3e} AC-rel {ac:.3e}")
+            assert e <= tol_for(cfg)
+            buckets.add(int(n[b]))
+    assert buckets == set(cfg["buckets"])
 
 
 # --------------------------------------------------------------------------
@@ -338,3 +350,109 @@ def test_fused_stages_bitwise_equal_per_layer(name):
         off = np.bincount(bad % hop, minlength=hop)
         say(f"  per-offset counts (first 64): {off[:64].tolist()}")
     assert np.array_equal(outs["fused"], outs["layer"])
+
+
+# --------------------------------------------------------------------------
+# Offline ceiling: whole-utterance decode of 128 ragged utterances
+# --------------------------------------------------------------------------
+def ramp_plan(T, ramp=(1, 2, 4), steady=8):
+    """Chunk sizes ramp[0], ramp[1], ..., then `steady`, the last chunk the
+    remainder (the streamed workload's schedule for an utterance of T frames)."""
+    plan, at = [], 0
+    for n in list(ramp) + [steady] * T:
+        if at >= T:
+            break
+        plan.append(min(n, T - at))
+        at += plan[-1]
+    return plan
+
+
+def test_c5_offline_whole_vs_streamed_vs_oracle():
+    """128 utterances of 50..500 frames. (1) Whole-utterance decode, calls
+    grouping whole utterances up to the per-call frame limit (valid frames
+    only: the ragged batch needs no padding). (2) The same codes streamed
+    with the ramp 1, 2, 4, 8, ... in lockstep, streams dropping out as they
+    end. (1) and (2) agree within the bf16 bound; (3) sampled windows of both
+    agree with the oracle; (4) a padded decode (pad code 0 up to 500 frames)
+    gives the same valid samples as the ragged one."""
+    cfg = RI.get_config("c5")
+    w = RI.make_weights(cfg)
+    c = open_codec(cfg, w)
+    H = c.hop
+    Bn = cfg["n_streams"]
+    lens = RI.c5_lengths(cfg)
+    codes = [RI.stream_codes(cfg, b, int(lens[b]), part=0) for b in range(Bn)]
+    say(f"case c5: {Bn} utterances, {int(lens.sum())} frames, lengths {lens.min()}..{lens.max()}")
+
+    # (1) whole-utterance decode, grouped by the per-call limit
+    maxF = cfg["max_frames_per_call"]
+    full = [None] * Bn
+    b0 = 0
+    while b0 < Bn:
+        b1, tot = b0, 0
+        while b1 < Bn and tot + lens[b1] <= maxF:
+            tot += int(lens[b1])
+            b1 += 1
+        outs = decode_full_gpu(c, codes[b0:b1])
+        for i, o in enumerate(outs):
+            full[b0 + i] = o
+        b0 = b1
+
+    # (2) streamed in lockstep with per-stream ramps
+    plans = [ramp_plan(int(t)) for t in lens]
+    ids = [c.stream_open() for _ in range(Bn)]
+    got = [[] for _ in range(Bn)]
+    at = [0] * Bn
+    for j in range(max(len(p) for p in plans)):
+        act = [b for b in range(Bn) if j < len(plans[b])]
+        n = [plans[b][j] for b in act]
+        packed = np.concatenate([codes[b][at[b]:at[b] + k] for b, k in zip(act, n)])
+        pcm = torch.empty(sum(n) * H, dtype=torch.float32, device="cuda")
+        c.decode_chunk([ids[b] for b in act], n, packed, pcm)
+        host = pcm.cpu().numpy()
+        o = 0
+        for b, k in zip(act, n):
+            got[b].append(host[o * H:(o + k) * H])
+            o += k
+            at[b] += k
+    for i in ids:
+        c.stream_close(i)
+    worst = 0.0
+    for b in range(Bn):
+        s = np.concatenate(got[b])
+        assert s.shape == full[b].shape
+        e, _ = rel_err(s, full[b])
+        worst = max(worst, e)
+        assert e <= tol_for(cfg), f"stream {b}: streamed vs full err/peak {e:.3e}"
+    say(f"c5 streamed vs full: worst err/peak {worst:.3e}")
+
+    # (3) sampled windows against the oracle
+    m = oracle.Model(cfg, w)
+    L = analytic_left_context(cfg) + 1
+    sample = sorted({int(np.argmin(lens)), int(np.argmax(lens))} |
+                    {int(b) for b in np.random.default_rng(5).choice(Bn, 2, replace=False)})
+    for b in sample:
+        T = int(lens[b])
+        for start in sorted({0, T // 2, T - 8}):
+            w0 = max(0, start - L)
+            ref = m.stream(w0).decode(codes[b][w0:start + 8])[(start - w0) * H:]
+            for tag, src in (("full", full[b]), ("streamed", np.concatenate(got[b]))):
+                e, ac = rel_err(src[start * H:(start + 8) * H], ref)
+                say(f"c5 stream {b} len {T} frames {start}..{start + 8} {tag}: "
+                    f"err/peak {e:.3e} AC-rel {ac:.3e}")
+                assert e <= tol_for(cfg)
+
+    # (4) padded decode: 32 streams padded with code 0 to the longest length
+    grp = list(range(32))
+    Tmax = cfg["max_len"]
+    pad = [np.concatenate([codes[b], np.zeros((Tmax - lens[b], cfg["K"]), np.int32)])
+           for b in grp]
+    outs = decode_full_gpu(c, pad)
+    same = 0
+    for b, o in zip(grp, outs):
+        v = o[:int(lens[b]) * H]
+        e, _ = rel_err(v, full[b])
+        assert e <= tol_for(cfg), f"stream {b}: padded vs ragged err/peak {e:.3e}"
+        same += int(np.array_equal(v, full[b]))
+    say(f"c5 padded vs ragged: {same} of {len(grp)} streams bitwise equal")
+    c.close()
