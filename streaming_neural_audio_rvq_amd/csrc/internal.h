@@ -68,6 +68,8 @@ struct ConvArgs {
     int N, Cout, s;
     int out_H, act;
     int out_ld;             // row width of out16 / out32 (== Cout)
+    uint32_t div_m;         // packed row -> frame: m / rate_in as a multiply-shift
+    int div_s1, div_s2;     //   (set by the launcher)
     int splits;             // split-K count (set by the launcher)
     int splits_allowed;     // 1: the planner may split K
     float *partial;         // split-K partials [splits][M][N] fp32

@@ -76,10 +76,20 @@ __device__ __forceinline__ void store4<float>(float *dst, f4 v)
     *(f4 *)dst = v;
 }
 
-// Output of 4 consecutive columns n..n+3 of packed input row m, bias added:
-// + residual, fp32 store, activation and compute-type store.
+// m / rate_in for any 32-bit m: round-up multiply-shift division with the
+// constants the launcher derives from the divisor.
+__device__ __forceinline__ int frame_of(const ConvArgs &p, int m)
+{
+    const uint32_t t = __umulhi(p.div_m, (uint32_t)m);
+    return (int)((t + (((uint32_t)m - t) >> p.div_s1)) >> p.div_s2);
+}
+
+// Output of 4 consecutive columns n..n+3 (channel ch..ch+3 of the output
+// row) of packed input row m, bias added: + residual, fp32 store, activation
+// and compute-type store.  al / ial: Snake parameters of channels ch..ch+3.
 template <typename T>
-__device__ __forceinline__ void epilogue4(const ConvArgs &p, int m, int n, f4 v)
+__device__ __forceinline__ void epilogue4(const ConvArgs &p, int m, int n, int ch, f4 v, f4 al,
+                                          f4 ial)
 {
     if (p.res) {
         f4 rr = *(const f4 *)(p.res + (long)m * p.Cout + n);
@@ -89,20 +99,29 @@ __device__ __forceinline__ void epilogue4(const ConvArgs &p, int m, int n, f4 v)
     if (p.out32)
         *(f4 *)(p.out32 + orow * p.Cout + n) = v;
     if (p.out16) {
-        int ch = n % p.Cout;
         f4 y;
         if (p.act == ACT_SNAKE) {
 #pragma unroll
             for (int e = 0; e < 4; e++)
-                y[e] = act_fn(v[e], ACT_SNAKE, p.alpha[ch + e], p.inv_alpha[ch + e]);
+                y[e] = act_fn(v[e], ACT_SNAKE, al[e], ial[e]);
         } else {
 #pragma unroll
             for (int e = 0; e < 4; e++)
                 y[e] = act_fn(v[e], p.act, 0.f, 0.f);
         }
-        int b = p.frame_stream[m / p.rate_in];
+        int b = p.frame_stream[frame_of(p, m)];
         long base = ((long)(b + 1) * p.out_H + orow) * p.Cout + n;
         store4<T>((T *)p.out16 + base, y);
+    }
+}
+
+__device__ __forceinline__ void snake_params(const ConvArgs &p, int ch, f4 &al, f4 &ial)
+{
+    al = f4{0.f, 0.f, 0.f, 0.f};
+    ial = al;
+    if (p.out16 && p.act == ACT_SNAKE) {
+        al = *(const f4 *)(p.alpha + ch);
+        ial = *(const f4 *)(p.inv_alpha + ch);
     }
 }
 
@@ -162,7 +181,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
             row = 0;
         int m = m0 + row;
         int mm = m < p.M ? m : p.M - 1;
-        int b = p.frame_stream[mm / p.rate_in];
+        int b = p.frame_stream[frame_of(p, mm)];
         long ext = (long)(b + 1) * p.A_H + mm;
         a_ptr[i] = A + ext * p.Cin + kc * VEC;
         a_lds[i] = row * LD + kc * VEC;
@@ -285,18 +304,24 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
             }
         }
     __syncthreads();
+    // each thread keeps one 4-column group and walks rows
     constexpr int QPR = BN / 4;
-    for (int q = tid; q < BM * QPR; q += 256) {
-        int r = q / QPR, cq = (q - r * QPR) * 4;
-        int m = m0 + r;
+    constexpr int RPI = 256 / QPR;
+    static_assert(256 % QPR == 0, "column groups");
+    const int cq = (tid % QPR) * 4;
+    const int n = n0 + cq;
+    const int ch = n % p.Cout;
+    f4 al, ial;
+    snake_params(p, ch, al, ial);
+    for (int r = tid / QPR; r < BM; r += RPI) {
+        const int m = m0 + r;
         if (m >= p.M)
-            continue;
-        int n = n0 + cq;
+            break;
         f4 v = *(const f4 *)(epi + r * ELD + cq);
         if (split)
             *(f4 *)(p.partial + ((long)blockIdx.y * p.M + m) * p.N + n) = v;
         else
-            epilogue4<T>(p, m, n, v);
+            epilogue4<T>(p, m, n, ch, v, al, ial);
     }
 }
 
@@ -315,8 +340,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ConvArgs p)
     for (int s = 1; s < p.splits; s++)
         v = v + *(const f4 *)(p.partial + s * stride + (long)m * p.N + n);
     const int ch = n % p.Cout;
-    v = v + f4{p.bias[ch], p.bias[ch + 1], p.bias[ch + 2], p.bias[ch + 3]};
-    epilogue4<T>(p, m, n, v);
+    v = v + *(const f4 *)(p.bias + ch);
+    f4 al, ial;
+    snake_params(p, ch, al, ial);
+    epilogue4<T>(p, m, n, ch, v, al, ial);
 }
 
 struct TileDesc {
@@ -400,6 +427,17 @@ hipError_t launch_conv_gemm(const ConvArgs &a0, int dtype, hipStream_t st, ConvP
         return hipErrorInvalidValue;
     ConvArgs a = a0;
     a.splits = plan.splits > 1 ? plan.splits : 1;
+    {
+        // m / d == (t + ((m - t) >> s1)) >> s2, t = umulhi(mult, m), for all
+        // 32-bit m (round-up reciprocal, l = ceil(log2 d))
+        const uint32_t d = (uint32_t)a.rate_in;
+        int l = 0;
+        while ((1ull << l) < d)
+            l++;
+        a.div_m = (uint32_t)((((1ull << 32) * ((1ull << l) - d)) / d) + 1);
+        a.div_s1 = l < 1 ? l : 1;
+        a.div_s2 = l > 1 ? l - 1 : 0;
+    }
     hipError_t e = hipErrorInvalidValue;
     if (dtype) {
         switch (plan.tile) {
