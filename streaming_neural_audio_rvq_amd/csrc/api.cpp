@@ -488,6 +488,9 @@ int enqueue_fused_stage(codec *c, int i, int F, const StepMeta &m, float *pcm, h
     a.frame_stream = m.frame_stream;
     a.cu = m.cu;
     a.slot = m.slot;
+    a.tile_cu = m.tile_cu[i];
+    a.n_streams = m.B;
+    a.n_tiles = m.n_tiles[i];
     a.r_in = c->rate[i];
     a.r_out = c->rate[i + 1];
     a.act = c->cfg.act == CODEC_ACT_ELU ? ACT_ELU : ACT_SNAKE;
@@ -495,7 +498,8 @@ int enqueue_fused_stage(codec *c, int i, int F, const StepMeta &m, float *pcm, h
     char nm[32];
     snprintf(nm, sizeof nm, "s%d.fused", i);
     return timed(c, nm, (int64_t)F * c->rate[i + 1], s, [&] {
-        return launch_stage_fused(a, c->ch[i + 1], c->cfg.strides[i], c->fuse_T[i], fin, F, s);
+        return F > 0 ? launch_stage_fused(a, c->ch[i + 1], c->cfg.strides[i], c->fuse_T[i], fin, s)
+                     : hipSuccess;
     });
 }
 
@@ -592,7 +596,14 @@ int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int3
     size_t ncodes = codes_on_device ? 0 : (size_t)F * g.K;
     size_t o_codes = 0, o_fs = round4(o_codes + ncodes), o_cu = round4(o_fs + F),
            o_slot = round4(o_cu + B + 1), o_fresh = round4(o_slot + B),
-           o_pos = round4(o_fresh + B), total = round4(o_pos + B);
+           o_pos = round4(o_fresh + B), o_tc = round4(o_pos + B);
+    size_t total = o_tc;
+    size_t o_tile[CODEC_MAX_STAGES]{};
+    for (int i = 0; i < c->S; i++)
+        if (c->fuse_T[i]) {
+            o_tile[i] = total;
+            total = round4(total + B + 1);
+        }
     int pi = c->pin_i;
     c->pin_i ^= 1;
     HIPCHK(c, hipEventSynchronize(c->pin_ev[pi]));  // the copy that last read this buffer is done
@@ -613,6 +624,20 @@ int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int3
     int32_t *dm = (int32_t *)c->meta_dev;
     StepMeta m{codes_on_device ? (int32_t *)codes : dm + o_codes, dm + o_fs, dm + o_cu,
                dm + o_slot, dm + o_fresh, dm + o_pos};
+    m.B = B;
+    // fused stages: each stream's output rows in tiles of fuse_T rows, the last shorter
+    for (int i = 0; i < c->S; i++) {
+        if (!c->fuse_T[i])
+            continue;
+        int32_t *tc = hp + o_tile[i];
+        tc[0] = 0;
+        for (int b = 0; b < B; b++) {
+            const int64_t rows = (int64_t)n[b] * c->rate[i + 1];
+            tc[b + 1] = tc[b] + (int32_t)((rows + c->fuse_T[i] - 1) / c->fuse_T[i]);
+        }
+        m.tile_cu[i] = dm + o_tile[i];
+        m.n_tiles[i] = tc[B];
+    }
     int rc = timed(c, "h2d_meta", (int64_t)total * 4, s, [&] {
         return hipMemcpyAsync(c->meta_dev, hp, total * 4, hipMemcpyHostToDevice, s);
     });
@@ -1050,7 +1075,7 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
     // contexts are written by the stage kernel itself, not by the halo save
     for (int i = 0; i < c->S; i++) {
         const int T = (c->dtype && g.act == CODEC_ACT_SNAKE)
-                          ? stage_fused_tile(ch[i + 1], g.strides[i], c->rate[i + 1], i == c->S - 1)
+                          ? stage_fused_tile(ch[i + 1], g.strides[i], i == c->S - 1)
                           : 0;
         c->fusable[i] = T != 0;
         c->fuse_T[i] = (g.flags & CODEC_FLAG_PER_LAYER) || (g.flags & CODEC_FLAG_PER_LAYER_STAGE(i)) ? 0 : T;
@@ -1072,7 +1097,8 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
         return cleanup_fail(rc);
 
     // ---- step metadata: device buffer + two pinned staging buffers ----
-    c->meta_cap = round4(F * g.K) + round4(F) + round4(B + 1) + 3 * round4(B) + 4;
+    c->meta_cap = round4(F * g.K) + round4(F) + round4(B + 1) + 3 * round4(B) +
+                  CODEC_MAX_STAGES * round4(B + 1) + 4;
     if ((rc = dev_alloc(c, &c->meta_dev, c->meta_cap * 4, ws)))
         return cleanup_fail(rc);
     if ((rc = dev_alloc(c, (void **)&c->bad_codes, sizeof(unsigned long long), ws)))

@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "snrvq.h"
+
 namespace snrvq {
 
 typedef _Float16 half_t;
@@ -102,6 +104,9 @@ struct StepMeta {
     int32_t *slot;         // [B]
     int32_t *fresh;        // [B]
     int32_t *pos;          // [B]
+    int32_t *tile_cu[CODEC_MAX_STAGES];  // fused stage i: first tile of each stream [B+1]
+    int B;                                // streams in the step
+    int n_tiles[CODEC_MAX_STAGES];        // fused stage i: tiles in the step
 };
 
 // ---- launchers (kernels_*.hip) ----
@@ -151,13 +156,16 @@ struct StageArgs {
     half_t *state;                    // slot array, slot_elems per slot
     long slot_elems, off_a1, off_a2, off_ao;
     const int32_t *frame_stream, *cu, *slot;
-    int r_in, r_out, act, tiles_per_frame, n_tiles;
+    const int32_t *tile_cu;           // [n_streams + 1]: stream b's tiles start at tile_cu[b]
+    int n_streams, n_tiles;
+    int r_in, r_out, act;
     int n_cu;                         // compute units of the device
 };
 // Output rows per tile of an instantiated fused stage, or 0 when the shape
-// has none (then the per-layer path runs).
-int stage_fused_tile(int C, int S, int r_out, bool final_stage);
-hipError_t launch_stage_fused(const StageArgs &a, int C, int S, int T, bool final_stage, int F,
+// has none (then the per-layer path runs).  A stream's rows are cut into
+// tiles of that many rows, the last one shorter.
+int stage_fused_tile(int C, int S, bool final_stage);
+hipError_t launch_stage_fused(const StageArgs &a, int C, int S, int T, bool final_stage,
                               hipStream_t st);
 
 // ---- transformer ops (kernels_tf.hip) ----
