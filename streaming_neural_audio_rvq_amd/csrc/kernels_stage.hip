@@ -24,9 +24,10 @@
 // leaves the wave's registers: the MFMA accumulator layout of a unit (lane =
 // row j and 4 consecutive channels) is the same in the transposed conv, both
 // residual units and the output epilogue.  Only the activated conv inputs
-// (the k = 7 convs read neighbouring rows) and the per-unit 1x1 inputs go
-// through LDS.  A tile spans 16 NW input rows, HQ of them recomputed halo,
-// so every wave has one q-block.
+// go through LDS (the k = 7 convs read neighbouring rows); each 1x1 conv
+// takes its operand straight from the k = 7 conv's accumulators, whose
+// output channels are ordered for it.  A tile spans 16 NW input rows, HQ of
+// them recomputed halo, so every wave has one q-block.
 //
 // Weights are the MFMA's A operand (16 output channels per block), the
 // activations its B operand (16 rows per block); a lane's accumulator holds
@@ -51,16 +52,17 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t Chunk __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 __device__ __forceinline__ f4 mma(h8 a, h8 b, f4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Output channel that A row `row` of channel block n of a k = 7 conv computes:
+// blocks 2k and 2k+1 hold channels 32k..32k+31, so that lane lg of both holds
+// channels 32k + 8 lg + 0..3 (block 2k) and + 4..7 (block 2k+1).
+__device__ __forceinline__ int ch7(int n, int row)
+{
+    return 32 * (n >> 1) + 8 * (row >> 2) + 4 * (n & 1) + (row & 3);
 }
 
 __device__ __forceinline__ h4 snake4(f4 v, f4 ar, f4 ai)
@@ -124,7 +126,6 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
 {
     using SH = StageShape<C, S, NW, FINAL>;
     using L = Rows<C, S>;
-    using LH = Rows<C, 1>;
     constexpr int NTH = NW * 64;
     constexpr int E = SH::E, HQ = SH::HQ, HX = SH::HX, T = SH::T;
     constexpr int CIN = 2 * C, NT = S * C, KT = 2 * CIN, NB = C / 16, NKT = KT / 32;
@@ -147,12 +148,10 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
     constexpr int A2_MIN = L::elems(SH::NA2);
     constexpr int A2_ELEMS =
         RES ? A2_MIN : (A2_MIN > A2_OFF_CT + 2 * CT_BUF ? A2_MIN : A2_OFF_CT + 2 * CT_BUF);
-    constexpr int HS_ELEMS = LH::elems(16);
     constexpr int W_ELEMS = RES ? RES_ELEMS : 2 * RU_BUF;
 
     __shared__ __attribute__((aligned(16))) half_t a1s[A1_ELEMS];  // a1, then a_out (FINAL)
     __shared__ __attribute__((aligned(16))) half_t a2s[A2_ELEMS];  // a2; ConvT chunks (streamed)
-    __shared__ __attribute__((aligned(16))) half_t hs[NW * HS_ELEMS];
     __shared__ __attribute__((aligned(16))) half_t wsm[W_ELEMS];
     __shared__ __attribute__((aligned(16))) float prm[P_COUNT * C];
     __shared__ float wout_s[FINAL ? 7 * C : 1];  // final conv weights, [tap][channel]
@@ -290,7 +289,6 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
         const int t0 = (g - p.tile_cu[b]) * T;
         const int tend = t0 + T < rows_b ? t0 + T : rows_b;  // rows [t0, tend)
         const bool first = t0 == 0, last = tend == rows_b;
-        half_t *hsw = hs + wave * HS_ELEMS;
         half_t *slot_state = p.state + (long)p.slot[b] * p.slot_elems;
         const int r1 = t0 - HX;      // stream row of a1s row 0
         const int r2 = t0 - 18 - E;  // stream row of a2s row 0
@@ -392,14 +390,15 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
 #pragma unroll
                 for (int n = 0; n < NB; n++)
                     acc[r][n] = f4{0.f, 0.f, 0.f, 0.f};
-            // one K step of 32 of the conv7 (dilation D) from weights wp (row pitch wld)
+            // one K step of 32 of the conv7 (dilation D) from weights wp (row pitch wld);
+            // block n, A row l16 computes output channel ch7(n, l16)
             auto step7 = [&](int k0, const half_t *wp, int wld) {
                 const int tap = k0 / C, c0 = k0 - tap * C;
                 const int sh = (tap - 6) * D;
                 h8 wf[NB];
 #pragma unroll
                 for (int n = 0; n < NB; n++)
-                    wf[n] = *(const h8 *)(wp + (n * 16 + l16) * wld + lg * 8);
+                    wf[n] = *(const h8 *)(wp + ch7(n, l16) * wld + lg * 8);
 #pragma unroll
                 for (int r = 0; r < S; r++) {
                     const h8 xf = *(const h8 *)(in + L::off(rowi[r] + sh, c0 + lg * 8));
@@ -422,7 +421,9 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
                     advance();
                 }
             }
-            // per unit: Snake(conv7 + b7) -> wave scratch -> 1x1 conv -> + b1 + x
+            // per unit: Snake(conv7 + b7) -> 1x1 conv -> + b1 + x.  The lane's conv7
+            // accumulators of blocks 2k, 2k+1 hold channels 32k + 8 lg + 0..7 of
+            // its row: exactly its B operand of the 1x1 conv's K step k.
             const half_t *w1p = RES ? w1s + u * C * LD1
                                     : wsm + ((NKT + u * (N7C + 1) + N7C) & 1) * RU_BUF;
             const int w1ld = RES ? LD1 : LDC;
@@ -430,29 +431,30 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
                       PA2I = u ? P_A2I1 : P_A2I0, PB1 = u ? P_B11 : P_B10;
 #pragma unroll
             for (int r = 0; r < S; r++) {
+                h8 hb[NB / 2];
 #pragma unroll
                 for (int n = 0; n < NB; n++) {
-                    const int c = n * 16 + lg * 4;
-                    *(h4 *)(hsw + LH::off(l16, c)) =
-                        snake4(acc[r][n] + *(const f4 *)(prm + PB7 * C + c),
-                               *(const f4 *)(prm + PA2R * C + c),
-                               *(const f4 *)(prm + PA2I * C + c));
+                    const int c = ch7(n, 4 * lg);
+                    const h4 hv = snake4(acc[r][n] + *(const f4 *)(prm + PB7 * C + c),
+                                         *(const f4 *)(prm + PA2R * C + c),
+                                         *(const f4 *)(prm + PA2I * C + c));
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        hb[n >> 1][(n & 1) * 4 + e] = hv[e];
                 }
-                wave_lds_sync();
                 f4 y[NB];
 #pragma unroll
                 for (int n = 0; n < NB; n++)
                     y[n] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int c0 = 0; c0 < C; c0 += 32) {
-                    const h8 hf = *(const h8 *)(hsw + LH::off(l16, c0 + lg * 8));
+                for (int kk = 0; kk < NB / 2; kk++) {
 #pragma unroll
                     for (int n = 0; n < NB; n++) {
-                        const h8 wf = *(const h8 *)(w1p + (n * 16 + l16) * w1ld + c0 + lg * 8);
-                        y[n] = mma(wf, hf, y[n]);
+                        const h8 wf =
+                            *(const h8 *)(w1p + (n * 16 + l16) * w1ld + kk * 32 + lg * 8);
+                        y[n] = mma(wf, hb[kk], y[n]);
                     }
                 }
-                wave_lds_sync();
                 const int t = q * S + r;
 #pragma unroll
                 for (int n = 0; n < NB; n++) {
