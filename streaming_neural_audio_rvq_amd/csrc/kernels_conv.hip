@@ -88,8 +88,8 @@ __device__ __forceinline__ int frame_of(const ConvArgs &p, int m)
 // row) of packed input row m, bias added: + residual, fp32 store, activation
 // and compute-type store.  al / ial: Snake parameters of channels ch..ch+3.
 template <typename T>
-__device__ __forceinline__ void epilogue4(const ConvArgs &p, int m, int n, int ch, f4 v, f4 al,
-                                          f4 ial)
+__device__ __forceinline__ void epilogue4(const ConvArgs &p, int m, int b, int n, int ch, f4 v,
+                                          f4 al, f4 ial)
 {
     if (p.res) {
         f4 rr = *(const f4 *)(p.res + (long)m * p.Cout + n);
@@ -109,7 +109,6 @@ __device__ __forceinline__ void epilogue4(const ConvArgs &p, int m, int n, int c
             for (int e = 0; e < 4; e++)
                 y[e] = act_fn(v[e], p.act, 0.f, 0.f);
         }
-        int b = p.frame_stream[frame_of(p, m)];
         long base = ((long)(b + 1) * p.out_H + orow) * p.Cout + n;
         store4<T>((T *)p.out16 + base, y);
     }
@@ -153,6 +152,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
     constexpr int EPI_BYTES = BM * ELD * 4;
     constexpr int SMEM = AB_BYTES > EPI_BYTES ? AB_BYTES : EPI_BYTES;
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
+    __shared__ int rowb[BM];  // stream of each tile row
     T *As = (T *)smem;
     T *Bs = As + 2 * BM * LD;
 
@@ -184,6 +184,8 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
         int b = p.frame_stream[frame_of(p, mm)];
         long ext = (long)(b + 1) * p.A_H + mm;
         a_ptr[i] = A + ext * p.Cin + kc * VEC;
+        if ((A_CH % 256 == 0 || c < A_CH) && kc == 0)
+            rowb[row] = b;
         a_lds[i] = row * LD + kc * VEC;
     }
     const T *b_ptr[B_PT];
@@ -291,16 +293,19 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
     // ---- epilogue: through an LDS tile, then row-contiguous 16-byte stores
     const bool split = p.splits > 1;
     float *epi = (float *)smem;
+    float bvj[FN];
+#pragma unroll
+    for (int j = 0; j < FN; j++)
+        bvj[j] = split ? 0.f : p.bias[(n0 + cbase + j * 16 + lrow) % p.Cout];
 #pragma unroll
     for (int i = 0; i < FM; i++)
 #pragma unroll
         for (int j = 0; j < FN; j++) {
-            int c = cbase + j * 16 + lrow;
-            float bv = split ? 0.f : p.bias[(n0 + c) % p.Cout];
+            const int c = cbase + j * 16 + lrow;
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 int r = rbase + i * 16 + lk * 4 + e;
-                epi[r * ELD + c] = split ? acc[i][j][e] : acc[i][j][e] + bv;
+                epi[r * ELD + c] = split ? acc[i][j][e] : acc[i][j][e] + bvj[j];
             }
         }
     __syncthreads();
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
         if (split)
             *(f4 *)(p.partial + ((long)blockIdx.y * p.M + m) * p.N + n) = v;
         else
-            epilogue4<T>(p, m, n, ch, v, al, ial);
+            epilogue4<T>(p, m, rowb[r], n, ch, v, al, ial);
     }
 }
 
@@ -343,7 +348,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ConvArgs p)
     v = v + *(const f4 *)(p.bias + ch);
     f4 al, ial;
     snake_params(p, ch, al, ial);
-    epilogue4<T>(p, m, n, ch, v, al, ial);
+    epilogue4<T>(p, m, p.out16 ? p.frame_stream[frame_of(p, m)] : 0, n, ch, v, al, ial);
 }
 
 struct TileDesc {
