@@ -18,8 +18,10 @@
 // Tiles: 256 threads (4 waves of 64), BM x BN output tile, K staged in steps
 // of BK = 32 KSUB (fp16, v_mfma_f32_16x16x32_f16) or 16 (fp32,
 // v_mfma_f32_16x16x4_f32).  Global loads are 16-byte chunks double-buffered
-// through LDS; the epilogue goes through LDS so that every global store is a
-// 16-byte chunk of a row.  Work-groups are remapped so that each XCD
+// through LDS.  The weights are the MFMA's A operand and the activation rows
+// its B operand, so each lane's accumulator holds 4 consecutive output
+// columns of one row and the epilogue stores straight from registers (4
+// channels per lane, 16 lanes per row segment).  Work-groups are remapped so that each XCD
 // (dispatch round-robin over 8) owns a contiguous range of tiles, N-tiles of
 // one M-row block adjacent, so the A rows (re-read by every tap and every
 // N-tile) stay in one L2.
@@ -147,10 +149,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
     constexpr int FM = TM / 16, FN = TN / 16;
     static_assert(WM * WN == 4, "4 waves");
     static_assert(FM >= 1 && FN >= 1 && TM % 16 == 0 && TN % 16 == 0, "wave tile");
-    constexpr int AB_BYTES = 2 * (BM + BN) * LD * (int)sizeof(T);
-    constexpr int ELD = BN + 4;
-    constexpr int EPI_BYTES = BM * ELD * 4;
-    constexpr int SMEM = AB_BYTES > EPI_BYTES ? AB_BYTES : EPI_BYTES;
+    constexpr int SMEM = 2 * (BM + BN) * LD * (int)sizeof(T);
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
     __shared__ int rowb[BM];  // stream of each tile row
     T *As = (T *)smem;
@@ -265,7 +264,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
                 for (int i = 0; i < FM; i++)
 #pragma unroll
                     for (int j = 0; j < FN; j++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j],
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[j], af[i],
                                                                            acc[i][j], 0, 0, 0);
             } else {
                 f4 af[FM], bf[FN];
@@ -282,7 +281,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
 #pragma unroll
                         for (int j = 0; j < FN; j++)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                af[i][kk], bf[j][kk], acc[i][j], 0, 0, 0);
+                                bf[j][kk], af[i][kk], acc[i][j], 0, 0, 0);
             }
         }
         if (ks + 1 < ks1)
@@ -290,43 +289,32 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
         __syncthreads();
     }
 
-    // ---- epilogue: through an LDS tile, then row-contiguous 16-byte stores
+    // ---- epilogue straight from the accumulators: weights are the MFMA's A
+    // operand, so acc[i][j] holds 4 consecutive output columns of one row
     const bool split = p.splits > 1;
-    float *epi = (float *)smem;
-    float bvj[FN];
+    f4 bias4[FN], al4[FN], ial4[FN];
+    int nj[FN], chj[FN];
 #pragma unroll
-    for (int j = 0; j < FN; j++)
-        bvj[j] = split ? 0.f : p.bias[(n0 + cbase + j * 16 + lrow) % p.Cout];
+    for (int j = 0; j < FN; j++) {
+        nj[j] = n0 + cbase + j * 16 + lk * 4;
+        chj[j] = nj[j] % p.Cout;
+        bias4[j] = split ? f4{0.f, 0.f, 0.f, 0.f} : *(const f4 *)(p.bias + chj[j]);
+        snake_params(p, chj[j], al4[j], ial4[j]);
+    }
 #pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++) {
-            const int c = cbase + j * 16 + lrow;
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                int r = rbase + i * 16 + lk * 4 + e;
-                epi[r * ELD + c] = split ? acc[i][j][e] : acc[i][j][e] + bvj[j];
-            }
-        }
-    __syncthreads();
-    // each thread keeps one 4-column group and walks rows
-    constexpr int QPR = BN / 4;
-    constexpr int RPI = 256 / QPR;
-    static_assert(256 % QPR == 0, "column groups");
-    const int cq = (tid % QPR) * 4;
-    const int n = n0 + cq;
-    const int ch = n % p.Cout;
-    f4 al, ial;
-    snake_params(p, ch, al, ial);
-    for (int r = tid / QPR; r < BM; r += RPI) {
+    for (int i = 0; i < FM; i++) {
+        const int r = rbase + i * 16 + lrow;
         const int m = m0 + r;
         if (m >= p.M)
-            break;
-        f4 v = *(const f4 *)(epi + r * ELD + cq);
-        if (split)
-            *(f4 *)(p.partial + ((long)blockIdx.y * p.M + m) * p.N + n) = v;
-        else
-            epilogue4<T>(p, m, rowb[r], n, ch, v, al, ial);
+            continue;
+        const int b = rowb[r];
+#pragma unroll
+        for (int j = 0; j < FN; j++) {
+            if (split)
+                *(f4 *)(p.partial + ((long)blockIdx.y * p.M + m) * p.N + nj[j]) = acc[i][j];
+            else
+                epilogue4<T>(p, m, b, nj[j], chj[j], acc[i][j] + bias4[j], al4[j], ial4[j]);
+        }
     }
 }
 
