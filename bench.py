@@ -57,6 +57,15 @@ def layer_model(cfg: dict) -> dict:
             m[f"s{i}.ru{j}.conv1"] = dict(fpr=2 * co * co, bpr=es * co + 4 * co + out,
                                           wpl=es * co * co)
     m["final_conv"] = dict(fpr=2 * 7 * ch[-1], bpr=es * ch[-1] + 4, wpl=0)
+    # a residual unit in one launch: the k = 7 conv's input, the residual in,
+    # its outputs (as the separate 1x1 conv writes them)
+    for i in range(len(cfg["strides"])):
+        co = ch[i + 1]
+        for j in range(2):
+            c7, c1 = m[f"s{i}.ru{j}.conv7"], m[f"s{i}.ru{j}.conv1"]
+            out = (4 + es) * co if j == 0 else es * co
+            m[f"s{i}.ru{j}"] = dict(fpr=c7["fpr"] + c1["fpr"], bpr=es * co + 4 * co + out,
+                                    wpl=c7["wpl"] + c1["wpl"])
     # a fused stage counts its output rows: the ConvT's input row is shared by
     # s output rows; only the stage input and output cross HBM (the last
     # stage writes PCM instead of the next stage's operand)

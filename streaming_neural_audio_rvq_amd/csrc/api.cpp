@@ -692,6 +692,35 @@ int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int3
         for (int j = 0; j < 2; j++) {
             void *in = j == 0 ? c->a1[i] : c->a2[i];
             int inH = 6 * RU_DIL[j];
+            if (!c->fusable[i] && ru_gemm_supported(c->ch[i + 1], c->dtype)) {
+                // the whole residual unit in one launch: h never leaves the chip
+                a = conv_args(c, c->conv7[i][j], in, inH, ro, F * ro, m);
+                a.W1 = c->conv1[i][j].Wt;
+                a.bias7 = c->conv7[i][j].bias;
+                a.act7 = c->cfg.act == CODEC_ACT_ELU ? ACT_ELU : ACT_SNAKE;
+                a.alpha7 = c->a_ru2[i][j].alpha;
+                a.inv_alpha7 = c->a_ru2[i][j].ialpha;
+                a.bias = c->conv1[i][j].bias;
+                a.res = c->x;
+                if (j == 0) {
+                    a.out32 = c->x;  // in place: each element is read then written by one thread
+                    a.out16 = c->a2[i];
+                    a.out_H = 18;
+                    set_act(c, a, c->a_ru1[i][1]);
+                } else if (i + 1 < c->S) {
+                    a.out16 = c->aT[i + 1];
+                    a.out_H = 1;
+                    set_act(c, a, c->a_stage[i + 1]);
+                } else {
+                    a.out16 = c->a_outb;
+                    a.out_H = 6;
+                    set_act(c, a, c->a_out);
+                }
+                snprintf(nm, sizeof nm, "s%d.ru%d", i, j);
+                if ((rc = timed(c, nm, (int64_t)a.M, s, [&] { return launch_ru_gemm(a, s); })))
+                    return rc;
+                continue;
+            }
             a = conv_args(c, c->conv7[i][j], in, inH, ro, F * ro, m);
             a.out16 = c->h;
             a.out_H = 0;

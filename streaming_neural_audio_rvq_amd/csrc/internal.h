@@ -75,6 +75,13 @@ struct ConvArgs {
     int splits;             // split-K count (set by the launcher)
     int splits_allowed;     // 1: the planner may split K
     float *partial;         // split-K partials [splits][M][N] fp32
+    // residual unit in one launch (k = 7 conv -> act7 -> 1x1 conv -> epilogue):
+    // A, Wt describe the k = 7 conv, bias and everything after it the 1x1
+    // conv's output side
+    const void *W1;         // [Cout][Cout] 1x1 weights
+    const float *bias7;     // [Cout] k = 7 conv bias
+    const float *alpha7, *inv_alpha7;  // [Cout] activation between the convs
+    int act7;
 };
 
 // Tile choice and split-K count of one conv launch.
@@ -113,6 +120,10 @@ struct StepMeta {
 // dtype: 0 = fp32 operands, 1 = fp16 operands
 hipError_t launch_conv_gemm(const ConvArgs &a, int dtype, hipStream_t st, ConvPlan plan);
 ConvPlan conv_gemm_plan(const ConvArgs &a, int dtype, int n_cu, long partial_cap);
+// One residual unit x + conv1x1(act7(conv7(a))) with its epilogue, fp16
+// operands; ru_gemm_supported says for which widths it runs.
+bool ru_gemm_supported(int Cout, int dtype);
+hipError_t launch_ru_gemm(const ConvArgs &a, hipStream_t st);
 const char *conv_gemm_tile_name(int dtype, int tile);
 
 hipError_t launch_halo_fill(const HaloTable &t, void *state, const StepMeta &m, int B,

@@ -135,7 +135,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int total)
     return x * q + (x < r ? x : r) + i;
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int KSUB>
+template <typename T, int BM, int BN, int WM, int WN, int KSUB, bool RU = false>
 __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
 {
     constexpr int BK0 = Traits<T>::BK;
@@ -149,7 +149,9 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
     constexpr int FM = TM / 16, FN = TN / 16;
     static_assert(WM * WN == 4, "4 waves");
     static_assert(FM >= 1 && FN >= 1 && TM % 16 == 0 && TN % 16 == 0, "wave tile");
-    constexpr int SMEM = 2 * (BM + BN) * LD * (int)sizeof(T);
+    constexpr int SMEM_MAIN = 2 * (BM + BN) * LD * (int)sizeof(T);
+    constexpr int SMEM_RU = RU ? (BM * (BN + 8) + 2 * BN * 72) * 2 : 0;  // h tile + 1x1 chunks
+    constexpr int SMEM = SMEM_MAIN > SMEM_RU ? SMEM_MAIN : SMEM_RU;
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
     __shared__ int rowb[BM];  // stream of each tile row
     T *As = (T *)smem;
@@ -289,6 +291,85 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
         __syncthreads();
     }
 
+    if constexpr (RU) {
+        // ---- residual unit: h = act7(conv7 + b7) into LDS (the staging
+        // buffers are free after the main loop's last barrier), then the 1x1
+        // conv over h with its weights streamed through LDS in K chunks
+        static_assert(sizeof(T) == 2, "fp16 operands");
+        constexpr int HP = BN + 8;           // h row pitch
+        constexpr int B1 = 64, LD1 = B1 + 8; // 1x1 K chunk and its pitch
+        constexpr int NK1 = BN / B1;
+        constexpr int W1_PT = BN * (B1 / 8) / 256;
+        static_assert(BN * (B1 / 8) % 256 == 0 && BN % B1 == 0, "1x1 chunks");
+        static_assert((BM * HP + 2 * BN * LD1) * 2 <= SMEM, "LDS");
+        half_t *hS = (half_t *)smem;
+        half_t *w1s = hS + BM * HP;
+        const half_t *W1 = (const half_t *)p.W1;
+        Chunk wr[W1_PT];
+        auto w1load = [&](int kc) {
+#pragma unroll
+            for (int i = 0; i < W1_PT; i++) {
+                const int k = tid + i * 256, row = k / (B1 / 8), c8 = (k % (B1 / 8)) * 8;
+                wr[i] = *(const Chunk *)(W1 + (long)row * BN + kc * B1 + c8);
+            }
+        };
+        auto w1store = [&](int buf) {
+#pragma unroll
+            for (int i = 0; i < W1_PT; i++) {
+                const int k = tid + i * 256, row = k / (B1 / 8), c8 = (k % (B1 / 8)) * 8;
+                *(Chunk *)(w1s + buf * BN * LD1 + row * LD1 + c8) = wr[i];
+            }
+        };
+        w1load(0);
+#pragma unroll
+        for (int j = 0; j < FN; j++) {
+            const int ch = cbase + j * 16 + lk * 4;  // one N tile: n0 == 0
+            const f4 b7 = *(const f4 *)(p.bias7 + ch);
+            f4 a7 = f4{0.f, 0.f, 0.f, 0.f}, ia7 = a7;
+            if (p.act7 == ACT_SNAKE) {
+                a7 = *(const f4 *)(p.alpha7 + ch);
+                ia7 = *(const f4 *)(p.inv_alpha7 + ch);
+            }
+#pragma unroll
+            for (int i = 0; i < FM; i++) {
+                const f4 v = acc[i][j] + b7;
+                f4 y;
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    y[e] = act_fn(v[e], p.act7, a7[e], ia7[e]);
+                store4<half_t>(hS + (rbase + i * 16 + lrow) * HP + ch, y);
+                acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        w1store(0);
+        __syncthreads();
+        for (int kc = 0; kc < NK1; kc++) {
+            if (kc + 1 < NK1)
+                w1load(kc + 1);
+            const half_t *Wb = w1s + (kc & 1) * BN * LD1;
+#pragma unroll
+            for (int sub = 0; sub < B1 / 32; sub++) {
+                h8 af[FM], bf[FN];
+#pragma unroll
+                for (int i = 0; i < FM; i++)
+                    af[i] = *(const h8 *)(hS + (rbase + i * 16 + lrow) * HP + kc * B1 + sub * 32 +
+                                          lk * 8);
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+                    bf[j] = *(const h8 *)(Wb + (cbase + j * 16 + lrow) * LD1 + sub * 32 + lk * 8);
+#pragma unroll
+                for (int i = 0; i < FM; i++)
+#pragma unroll
+                    for (int j = 0; j < FN; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[j], af[i],
+                                                                           acc[i][j], 0, 0, 0);
+            }
+            if (kc + 1 < NK1)
+                w1store((kc + 1) & 1);
+            __syncthreads();
+        }
+    }
+
     // ---- epilogue straight from the accumulators: weights are the MFMA's A
     // operand, so acc[i][j] holds 4 consecutive output columns of one row
     const bool split = p.splits > 1;
@@ -356,13 +437,26 @@ const TileDesc F_TILES[] = {
 constexpr int NH = sizeof(H_TILES) / sizeof(H_TILES[0]);
 constexpr int NF = sizeof(F_TILES) / sizeof(F_TILES[0]);
 
-template <typename T, int BM, int BN, int WM, int WN, int KSUB>
+template <typename T, int BM, int BN, int WM, int WN, int KSUB, bool RU = false>
 hipError_t launch_t(const ConvArgs &a, hipStream_t st)
 {
     int ntm = (a.M + BM - 1) / BM, ntn = a.N / BN;
-    hipLaunchKernelGGL((conv_gemm_kernel<T, BM, BN, WM, WN, KSUB>), dim3(ntm * ntn, a.splits),
+    hipLaunchKernelGGL((conv_gemm_kernel<T, BM, BN, WM, WN, KSUB, RU>), dim3(ntm * ntn, a.splits),
                        dim3(256), 0, st, a);
     return hipGetLastError();
+}
+
+void set_division(ConvArgs &a)
+{
+    // m / d == (t + ((m - t) >> s1)) >> s2, t = umulhi(mult, m), for all
+    // 32-bit m (round-up reciprocal, l = ceil(log2 d))
+    const uint32_t d = (uint32_t)a.rate_in;
+    int l = 0;
+    while ((1ull << l) < d)
+        l++;
+    a.div_m = (uint32_t)((((1ull << 32) * ((1ull << l) - d)) / d) + 1);
+    a.div_s1 = l < 1 ? l : 1;
+    a.div_s2 = l > 1 ? l - 1 : 0;
 }
 
 }  // namespace
@@ -420,17 +514,7 @@ hipError_t launch_conv_gemm(const ConvArgs &a0, int dtype, hipStream_t st, ConvP
         return hipErrorInvalidValue;
     ConvArgs a = a0;
     a.splits = plan.splits > 1 ? plan.splits : 1;
-    {
-        // m / d == (t + ((m - t) >> s1)) >> s2, t = umulhi(mult, m), for all
-        // 32-bit m (round-up reciprocal, l = ceil(log2 d))
-        const uint32_t d = (uint32_t)a.rate_in;
-        int l = 0;
-        while ((1ull << l) < d)
-            l++;
-        a.div_m = (uint32_t)((((1ull << 32) * ((1ull << l) - d)) / d) + 1);
-        a.div_s1 = l < 1 ? l : 1;
-        a.div_s2 = l > 1 ? l - 1 : 0;
-    }
+    set_division(a);
     hipError_t e = hipErrorInvalidValue;
     if (dtype) {
         switch (plan.tile) {
@@ -460,6 +544,27 @@ hipError_t launch_conv_gemm(const ConvArgs &a0, int dtype, hipStream_t st, ConvP
     else
         hipLaunchKernelGGL(splitk_reduce_kernel<float>, grid, dim3(256), 0, st, a);
     return hipGetLastError();
+}
+
+bool ru_gemm_supported(int Cout, int dtype)
+{
+    // 256 channels would need a 64 x 256 tile at one work-group per CU, which
+    // is slower than the two separate launches
+    return dtype == 1 && Cout == 128;
+}
+
+hipError_t launch_ru_gemm(const ConvArgs &a0, hipStream_t st)
+{
+    if (a0.M <= 0)
+        return hipSuccess;
+    ConvArgs a = a0;
+    a.splits = 1;
+    set_division(a);
+    if (a.N != a.Cout || a.s != 1 || a.Cin % 64 != 0)
+        return hipErrorInvalidValue;
+    if (a.Cout == 128)
+        return launch_t<half_t, 128, 128, 2, 2, 2, true>(a, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace snrvq
