@@ -113,10 +113,30 @@ WORKLOADS = {
 }
 
 
-def make_workload(name: str, cfg: dict, codec, total_steps: int, stream) -> dict:
-    """Per step, the decode calls (stream ids or None for fresh streams, new
-    frames per stream, host codes, the same codes in HBM); streams opened and
-    prefilled here, untimed."""
+LEFT_CONTEXT_FRAMES = 16  # stateless re-decode: left frames decoded again with every chunk
+
+
+def group_calls(n, codes_of, max_frames):
+    """Whole streams into calls of at most max_frames frames: lists of
+    (stream indices, frames per stream)."""
+    out, b0, B = [], 0, len(n)
+    while b0 < B:
+        b1, tot = b0, 0
+        while b1 < B and tot + int(n[b1]) <= max_frames:
+            tot += int(n[b1])
+            b1 += 1
+        out.append(list(range(b0, b1)))
+        b0 = b1
+    return out
+
+
+def make_workload(name: str, cfg: dict, codec, total_steps: int, stream,
+                  stateless: bool = False) -> dict:
+    """Per step, the decode calls (stream ids or None for fresh streams, frames
+    per stream, host codes, the same codes in HBM) and the new frames the step
+    delivers; streams opened and prefilled here, untimed.  stateless: every
+    chunk is decoded again from zero state together with up to 16 earlier
+    frames of its stream (fresh streams each call)."""
     import torch
     import rvq_inputs as RI
     dev = torch.device("cuda:0")
@@ -127,6 +147,29 @@ def make_workload(name: str, cfg: dict, codec, total_steps: int, stream) -> dict
         return (ids, n, codes, torch.from_numpy(codes).to(dev))
 
     steps = []
+    new_frames = []
+    if stateless:
+        if name not in ("c2", "c4"):
+            raise SystemExit("bench.py: the stateless re-decode runs on the c2 and c4 workloads")
+        off = RI.c4_offsets(cfg) if name == "c4" else np.zeros(Bn, np.int32)
+        hist = [RI.stream_codes(cfg, b, int(off[b]), part=0) for b in range(Bn)]
+        for j in range(total_steps):
+            n = RI.c4_chunk_sizes(cfg, j) if name == "c4" else np.full(Bn, 8, np.int32)
+            new = [RI.stream_codes(cfg, b, int(n[b]), part=1 + j) for b in range(Bn)]
+            win = []
+            for b in range(Bn):
+                left = hist[b][max(0, len(hist[b]) - LEFT_CONTEXT_FRAMES):]
+                win.append(np.concatenate([left, new[b]]))
+                hist[b] = np.concatenate([hist[b], new[b]])
+            wn = np.array([w.shape[0] for w in win], np.int32)
+            calls = []
+            for grp in group_calls(wn, None, cfg["max_frames_per_call"]):
+                calls.append(call(None, wn[grp], np.concatenate([win[b] for b in grp])))
+            steps.append(calls)
+            new_frames.append(int(n.sum()))
+        return {"steps": steps, "new_frames": new_frames, "streams": Bn,
+                "desc": f"{name}: {WORKLOADS[name]}; stateless re-decode with "
+                        f"{LEFT_CONTEXT_FRAMES} left frames, fresh streams every call"}
     if name == "c4":
         off = RI.c4_offsets(cfg)
         ids = [codec.stream_open() for _ in range(Bn)]
@@ -145,17 +188,10 @@ def make_workload(name: str, cfg: dict, codec, total_steps: int, stream) -> dict
             steps.append([call(ids, [8] * Bn, codes)])
     elif name == "c5":
         lens = RI.c5_lengths(cfg)
-        maxF = cfg["max_frames_per_call"]
-        calls, b0 = [], 0
-        while b0 < Bn:
-            b1, tot = b0, 0
-            while b1 < Bn and tot + lens[b1] <= maxF:
-                tot += int(lens[b1])
-                b1 += 1
-            codes = np.concatenate([RI.stream_codes(cfg, b, int(lens[b]), part=0)
-                                    for b in range(b0, b1)])
-            calls.append(call(None, lens[b0:b1], codes))
-            b0 = b1
+        calls = []
+        for grp in group_calls(lens, None, cfg["max_frames_per_call"]):
+            codes = np.concatenate([RI.stream_codes(cfg, b, int(lens[b]), part=0) for b in grp])
+            calls.append(call(None, lens[grp], codes))
         steps = [calls] * total_steps
     else:
         raise SystemExit(f"bench.py: no workload for config {name!r}")
@@ -403,6 +439,9 @@ def main() -> int:
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--stateless", action="store_true",
+                    help="comparison: decode every chunk again from zero state with up to 16 "
+                         "left frames (the pages' stateless variant) instead of carrying state")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run one plain streaming kernel (negation) that reads and "
                          "writes this many MiB: the known-size reference for HBM counters")
@@ -451,7 +490,7 @@ def main() -> int:
 
     # steps: warmup, timed (codes resident in HBM), profiled, host-codes
     total_steps = args.warmup + 3 * args.steps
-    wl = make_workload(args.config, cfg, codec, total_steps, stream)
+    wl = make_workload(args.config, cfg, codec, total_steps, stream, args.stateless)
     pcm = torch.empty(cfg["max_frames_per_call"] * hop, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
@@ -469,6 +508,8 @@ def main() -> int:
                     codec.stream_close(i)
 
     def step_frames(j):
+        if "new_frames" in wl:
+            return wl["new_frames"][j]
         return int(sum(int(np.sum(n)) for _, n, _, _ in wl["steps"][j]))
 
     for j in range(args.warmup):
@@ -550,7 +591,8 @@ def main() -> int:
     fpf = flops_per_frame(cfg)
     peak_f = PEAK_F16_TFLOPS if cfg["weight_dtype"] == "bf16" else PEAK_F32_TFLOPS
     out = {
-        "metric": METRIC if args.config == "c4" else f"codec frames/s ({args.config})",
+        "metric": (METRIC if args.config == "c4" and not args.stateless
+                   else f"codec frames/s ({args.config}{', stateless' if args.stateless else ''})"),
         "value": round(fps, 1),
         "unit": "frames/s",
         "n_gpus": 1,
@@ -563,7 +605,10 @@ def main() -> int:
         "dtype": "f16" if cfg["weight_dtype"] == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wl["desc"], "streams": wl["streams"], "frames_timed": frames,
-                   "mean_frames_per_step": frames / args.steps},
+                   "mean_frames_per_step": frames / args.steps,
+                   "decoded_frames_per_new_frame": round(
+                       sum(int(np.sum(n)) for j in range(args.warmup, args.warmup + args.steps)
+                           for _, n, _, _ in wl["steps"][j]) / frames, 3)},
         "audio_sec_per_s": round(fps / frame_rate, 1),
         "host_codes_frames_per_s": round(h_frames / h_elapsed, 1),
         "mfma_util_alg": round(fps * fpf / (peak_f * 1e12), 4),

@@ -456,3 +456,48 @@ def test_c5_offline_whole_vs_streamed_vs_oracle():
         same += int(np.array_equal(v, full[b]))
     say(f"c5 padded vs ragged: {same} of {len(grp)} streams bitwise equal")
     c.close()
+
+
+# --------------------------------------------------------------------------
+# Stateless window re-decode (comparison variant)
+# --------------------------------------------------------------------------
+def test_stateless_window_redecode_matches_stateful_c2():
+    """The pages' stateless variant decodes each chunk again from zero state
+    together with up to 16 earlier frames and keeps the new frames' samples.
+    For the Qwen-shaped decoder (left context 11 frames <= 16) that equals the
+    stateful decode in exact arithmetic: here within the bf16 bound, against
+    both the GPU's stateful decode and the oracle.  The window lengths are the
+    ones the chunk policy predicts."""
+    from oracle import policy
+    cfg = RI.get_config("c2")
+    w = RI.make_weights(cfg)
+    c = open_codec(cfg, w)
+    H = c.hop
+    B, T = 4, 60
+    plan = policy.chunk_plan(T)
+    codes = [RI.stream_codes(cfg, b, T, part=0) for b in range(B)]
+    say("case stateless c2: plan", plan)
+    ids = [c.stream_open() for _ in range(B)]
+    stateful = run_lockstep(c, ids, codes, plan)
+    for i in ids:
+        c.stream_close(i)
+    got = [[] for _ in range(B)]
+    wins, at = set(), 0
+    for n in plan:
+        w0 = max(0, at - 16)
+        wins.add(at + n - w0)
+        outs = decode_full_gpu(c, [cb[w0:at + n] for cb in codes])
+        for b in range(B):
+            got[b].append(outs[b][(at - w0) * H:])
+        at += n
+    assert wins <= set(policy.window_frame_counts(16)), sorted(wins)
+    m = oracle.Model(cfg, w)
+    for b in range(B):
+        g = np.concatenate(got[b])
+        e, _ = rel_err(g, stateful[b])
+        assert e <= tol_for(cfg), f"stream {b}: stateless vs stateful err/peak {e:.3e}"
+    ref = m.stream().decode(codes[0])
+    e, ac = rel_err(np.concatenate(got[0]), ref)
+    say(f"stateless stream 0 vs oracle: err/peak {e:.3e} AC-rel {ac:.3e}; windows {sorted(wins)}")
+    assert e <= tol_for(cfg)
+    c.close()
