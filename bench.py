@@ -241,6 +241,73 @@ def cpu_baseline(name: str, cfg: dict, weights: dict, budget_s: float) -> dict:
             "audio_sec_per_s": frames / dt / fr}
 
 
+def cu_masked_stream(torch, lo: int, hi: int):
+    """A stream (default priority) whose kernels run on CUs [lo, hi) only."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    words = (n_cu + 31) // 32
+    mask = (ctypes.c_uint32 * words)()
+    for cu in range(lo, hi):
+        mask[cu // 32] |= 1 << (cu % 32)
+    handle = ctypes.c_void_p()
+    rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(handle), ctypes.c_uint32(words), mask)
+    if rc != 0:
+        raise RuntimeError(f"hipExtStreamCreateWithCUMask failed ({rc})")
+    return torch.cuda.ExternalStream(handle.value)
+
+
+def cotenant_run(args, torch, timed_run, timed_frames, dec_stream, steps, solo_fps) -> dict:
+    """The same decode steps beside a synthetic stage-0 stand-in: back-to-back
+    bf16 8192^3 GEMMs on a second stream, enqueued to outlast the decode.
+    Decode frames/s alone and beside the load, and the slowdown."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda:0")
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda:0")
+    if args.cotenant == "masked":
+        k = max(1, min(n_cu - 1, int(round(n_cu * args.cu_fraction))))
+        dec = cu_masked_stream(torch, 0, k)
+        load = cu_masked_stream(torch, k, n_cu)
+        alone = timed_run(steps, False, dec)
+        solo = alone[0] / alone[1]
+    else:
+        k = n_cu
+        dec = torch.cuda.Stream()
+        load = torch.cuda.Stream()
+        alone = timed_run(steps, False, dec)
+        solo = alone[0] / alone[1]
+    # time one GEMM on the load stream, then enqueue enough for 3x the decode time
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(load):
+        torch.matmul(a, b)
+        e0.record(load)
+        torch.matmul(a, b)
+        e1.record(load)
+    torch.cuda.synchronize()
+    gemm_ms = e0.elapsed_time(e1)
+    # decode time alone, from the frames of these steps at the solo rate
+    decode_ms = 1e3 * timed_frames(steps) / max(1.0, solo)
+    n_gemm = 0
+    with torch.cuda.stream(load):
+        le0 = torch.cuda.Event(enable_timing=True)
+        le0.record(load)
+        while n_gemm * gemm_ms < 3 * decode_ms:
+            torch.matmul(a, b)
+            n_gemm += 1
+    le1 = torch.cuda.Event(enable_timing=True)
+    le1.record(load)
+    fr, el = timed_run(steps, False, dec, alone=False)
+    torch.cuda.synchronize()
+    load_tflops = n_gemm * 2 * 8192 ** 3 / (le0.elapsed_time(le1) / 1e3) / 1e12
+    co = fr / el
+    return {"mode": args.cotenant, "decode_cus": k, "load": "bf16 GEMM 8192^3 back to back",
+            "gemm_ms_alone": round(gemm_ms, 3), "gemms": n_gemm,
+            "load_tflops": round(load_tflops, 1),
+            "decode_frames_per_s_alone": round(solo, 1),
+            "decode_frames_per_s_beside_load": round(co, 1),
+            "decode_slowdown": round(solo / co - 1.0, 4)}
+
+
 def step_indices(warmup: int, steps: int, profiled: bool) -> list:
     """Chunk-schedule indices of the decode steps a run dispatches, in order:
     warmup, timed (codes in HBM), profiled (unless skipped), host codes."""
@@ -439,6 +506,12 @@ def main() -> int:
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--cotenant", choices=["shared", "masked"],
+                    help="also time the steps beside a synthetic bf16 GEMM load on another "
+                         "stream (default priority): sharing all CUs, or with the decode "
+                         "stream and the load stream on disjoint CU masks")
+    ap.add_argument("--cu-fraction", type=float, default=0.5,
+                    help="share of the CUs in the decode stream's mask (--cotenant masked)")
     ap.add_argument("--stateless", action="store_true",
                     help="comparison: decode every chunk again from zero state with up to 16 "
                          "left frames (the pages' stateless variant) instead of carrying state")
@@ -494,15 +567,16 @@ def main() -> int:
     pcm = torch.empty(cfg["max_frames_per_call"] * hop, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
-    def run_step(j, host_codes=False):
+    def run_step(j, host_codes=False, st=None):
+        st = stream if st is None else st
         for ids, n, codes, codes_dev in wl["steps"][j]:
             fresh = ids is None
             if fresh:
                 ids = [codec.stream_open() for _ in range(len(n))]
             if host_codes:
-                codec.decode_chunk(ids, n, codes, pcm, stream)
+                codec.decode_chunk(ids, n, codes, pcm, st)
             else:
-                codec.decode_chunk_device(ids, n, codes_dev, pcm, stream)
+                codec.decode_chunk_device(ids, n, codes_dev, pcm, st)
             if fresh:
                 for i in ids:
                     codec.stream_close(i)
@@ -516,16 +590,23 @@ def main() -> int:
         run_step(j)
     torch.cuda.synchronize()
 
-    def timed_run(steps, host_codes: bool):
+    def timed_run(steps, host_codes: bool, st=None, alone=True):
+        """Frames and seconds of the steps on stream st.  alone=False: other
+        work runs on the device, so only this stream's events time it."""
+        st = stream if st is None else st
         fr = sum(step_frames(j) for j in steps)
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
+        if alone:
+            torch.cuda.synchronize()
         t0 = time.perf_counter()
-        ev0.record(stream)
+        ev0.record(st)
         for j in steps:
-            run_step(j, host_codes)
-        ev1.record(stream)
+            run_step(j, host_codes, st)
+        ev1.record(st)
+        if not alone:
+            ev1.synchronize()
+            return fr, ev0.elapsed_time(ev1) / 1e3
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         return fr, max(wall, ev0.elapsed_time(ev1) / 1e3)
@@ -588,6 +669,12 @@ def main() -> int:
         roof["alg_bytes_per_launch"] = int(d["bytes_per_launch"])
         roof["alg_flops_per_launch"] = int(d["flops_per_launch"])
 
+    cot = None
+    if args.cotenant:
+        cot = cotenant_run(args, torch, timed_run, lambda st: sum(step_frames(j) for j in st),
+                           stream,
+                           range(args.warmup, args.warmup + args.steps), fps)
+
     fpf = flops_per_frame(cfg)
     peak_f = PEAK_F16_TFLOPS if cfg["weight_dtype"] == "bf16" else PEAK_F32_TFLOPS
     out = {
@@ -614,6 +701,8 @@ def main() -> int:
         "mfma_util_alg": round(fps * fpf / (peak_f * 1e12), 4),
         "roofline": roof,
     }
+    if cot:
+        out["cotenant"] = cot
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.config, cfg, w, args.cpu_baseline_seconds)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 2)
