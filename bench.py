@@ -241,6 +241,32 @@ def cpu_baseline(name: str, cfg: dict, weights: dict, budget_s: float) -> dict:
             "audio_sec_per_s": frames / dt / fr}
 
 
+def graph_latency(torch, codec, cfg, stream, reps: int = 50) -> dict:
+    """Latency of one-stream steps (1 and 8 new frames), each waited for:
+    eager decode_chunk against decode_chunk_graph; medians in microseconds."""
+    import rvq_inputs as RI
+    out = {}
+    for n in (1, 8):
+        pcm = torch.empty(n * codec.hop, dtype=torch.float32, device="cuda:0")
+        res = {}
+        for mode in ("eager", "graph"):
+            sid = codec.stream_open()
+            fn = codec.decode_chunk_graph if mode == "graph" else codec.decode_chunk
+            ts = []
+            for r in range(reps + 5):
+                codes = RI.stream_codes(cfg, 0, n, part=1000 + r)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                fn([sid], [n], codes, pcm, stream)
+                torch.cuda.synchronize()
+                if r >= 5:
+                    ts.append(time.perf_counter() - t0)
+            codec.stream_close(sid)
+            res[mode] = round(1e6 * float(np.median(ts)), 1)
+        out[f"{n}_frame_step_us"] = res
+    return out
+
+
 def cu_masked_stream(torch, lo: int, hi: int):
     """A stream (default priority) whose kernels run on CUs [lo, hi) only."""
     import ctypes
@@ -512,6 +538,9 @@ def main() -> int:
                          "stream and the load stream on disjoint CU masks")
     ap.add_argument("--cu-fraction", type=float, default=0.5,
                     help="share of the CUs in the decode stream's mask (--cotenant masked)")
+    ap.add_argument("--graph", action="store_true",
+                    help="run every step through decode_chunk_graph (host codes, one graph "
+                         "launch per step, captured once per chunk shape)")
     ap.add_argument("--stateless", action="store_true",
                     help="comparison: decode every chunk again from zero state with up to 16 "
                          "left frames (the pages' stateless variant) instead of carrying state")
@@ -534,6 +563,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.rocprof_summary:
         return rocprof_summary(args)
+    if args.graph:
+        args.no_profile = True  # graph steps record no per-kernel events
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build decodes on one GPU only (asked for --gpus {args.gpus}, "
@@ -573,7 +604,9 @@ def main() -> int:
             fresh = ids is None
             if fresh:
                 ids = [codec.stream_open() for _ in range(len(n))]
-            if host_codes:
+            if args.graph and not fresh:
+                codec.decode_chunk_graph(ids, n, codes, pcm, st)
+            elif host_codes:
                 codec.decode_chunk(ids, n, codes, pcm, st)
             else:
                 codec.decode_chunk_device(ids, n, codes_dev, pcm, st)
@@ -669,6 +702,10 @@ def main() -> int:
         roof["alg_bytes_per_launch"] = int(d["bytes_per_launch"])
         roof["alg_flops_per_launch"] = int(d["flops_per_launch"])
 
+    glat = None
+    if args.graph:
+        glat = graph_latency(torch, codec, cfg, stream)
+
     cot = None
     if args.cotenant:
         cot = cotenant_run(args, torch, timed_run, lambda st: sum(step_frames(j) for j in st),
@@ -678,8 +715,9 @@ def main() -> int:
     fpf = flops_per_frame(cfg)
     peak_f = PEAK_F16_TFLOPS if cfg["weight_dtype"] == "bf16" else PEAK_F32_TFLOPS
     out = {
-        "metric": (METRIC if args.config == "c4" and not args.stateless
-                   else f"codec frames/s ({args.config}{', stateless' if args.stateless else ''})"),
+        "metric": (METRIC if args.config == "c4" and not (args.stateless or args.graph)
+                   else f"codec frames/s ({args.config}{', stateless' if args.stateless else ''}"
+                        f"{', graph replay' if args.graph else ''})"),
         "value": round(fps, 1),
         "unit": "frames/s",
         "n_gpus": 1,
@@ -703,6 +741,8 @@ def main() -> int:
     }
     if cot:
         out["cotenant"] = cot
+    if glat:
+        out["graph_latency"] = glat
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.config, cfg, w, args.cpu_baseline_seconds)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 2)

@@ -177,6 +177,24 @@ int decode_chunk_device(codec_t *codec, int32_t B, const int32_t *stream_ids,
                         const int32_t *n_frames, const int32_t *codes_dev, float *pcm,
                         int64_t pcm_capacity, codec_hip_stream stream);
 
+/* The same step as decode_chunk, replayed from a HIP graph (the pages'
+ * streaming decoders capture CUDA graphs per input shape; AREX article on
+ * Fish Audio Drama 3, "two stages share one card", and the AI-infra
+ * handbook's Qwen3-TTS case, "third stop: the streaming vocoder").  The
+ * first call for a chunk shape -- B, n_frames[0..B) and the pcm address --
+ * captures the step's device work (metadata copy and every kernel) into a
+ * graph; later calls with the same shape fill the step's metadata (codes,
+ * slots, positions) into that graph's own pinned buffer and launch the
+ * graph, one launch instead of one per kernel.  Results are bit-identical to
+ * decode_chunk.  Up to 64 shapes are kept (least recently used evicted),
+ * each as two graph instances used in turn; a call waits for the replay two
+ * calls back of its shape.  Checks and errors are those of decode_chunk
+ * (CODEC_EHIP if capture or instantiation fails).  Profiling events are not
+ * recorded for graph steps. */
+int decode_chunk_graph(codec_t *codec, int32_t B, const int32_t *stream_ids,
+                       const int32_t *n_frames, const int32_t *codes, float *pcm,
+                       int64_t pcm_capacity, codec_hip_stream stream);
+
 /* Waits for the codec's device work and returns through *bad_codes the
  * number of out-of-range codes seen by decode_chunk_device since the last
  * call (then resets it).  CODEC_ERANGE when it is nonzero. */

@@ -63,6 +63,7 @@ _lib = None
 
 EXPORTS = ["codec_open", "codec_close", "codec_info", "codec_last_error", "stream_open",
            "stream_close", "stream_prefill", "decode_chunk", "decode_chunk_device",
+           "decode_chunk_graph",
            "codec_device_status", "codec_debug_capture", "codec_debug_read_state",
            "codec_profile_enable", "codec_profile_read", "codec_chunk_plan",
            "codec_resolve_initial_chunk_frames"]
@@ -90,6 +91,8 @@ def lib():
                                C.c_int64, C.c_void_p]
     L.decode_chunk_device.argtypes = [C.c_void_p, C.c_int32, _I32P, _I32P, C.c_void_p,
                                       C.c_void_p, C.c_int64, C.c_void_p]
+    L.decode_chunk_graph.argtypes = [C.c_void_p, C.c_int32, _I32P, _I32P, _I32P, C.c_void_p,
+                                     C.c_int64, C.c_void_p]
     L.codec_device_status.argtypes = [C.c_void_p, C.POINTER(C.c_int64)]
     L.codec_debug_capture.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int64, C.c_void_p]
     L.codec_debug_read_state.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int64,
@@ -234,6 +237,16 @@ class Codec:
         _check(lib().decode_chunk(self._h, len(ids), _ptr(ids), _ptr(n), _ptr(codes),
                                   C.c_void_p(pcm.data_ptr()), pcm.numel(),
                                   _stream_handle(stream)), self._h)
+
+    def decode_chunk_graph(self, stream_ids, n_frames, codes, pcm, stream=None):
+        """decode_chunk replayed from a graph captured per chunk shape (B,
+        n_frames, pcm buffer); same arguments and results."""
+        ids = _i32(stream_ids)
+        n = _i32(n_frames)
+        codes = _i32(codes)
+        _check(lib().decode_chunk_graph(self._h, len(ids), _ptr(ids), _ptr(n), _ptr(codes),
+                                        C.c_void_p(pcm.data_ptr()), pcm.numel(),
+                                        _stream_handle(stream)), self._h)
 
     def decode_chunk_device(self, stream_ids, n_frames, codes_dev, pcm, stream=None):
         """codes_dev: an int32 CUDA tensor [sum n, K] already on the device."""

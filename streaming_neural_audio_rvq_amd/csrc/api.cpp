@@ -19,6 +19,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <string>
 #include <unordered_map>
 #include <unordered_set>
@@ -121,6 +122,19 @@ struct codec {
     size_t meta_cap = 0;  // int32 elements
     unsigned long long *bad_codes = nullptr;  // device counter (device-resident codes)
     void *pinned[2]{};
+    // captured step graphs, keyed by (B, n[0..B), pcm address); two instances
+    // per key, each with its own pinned metadata buffer
+    struct GraphEntry {
+        hipGraphExec_t exec[2]{};
+        void *pinned[2]{};
+        hipEvent_t done[2]{};
+        int next = 0;
+        uint64_t last_use = 0;
+    };
+    std::map<std::vector<int64_t>, GraphEntry> graphs;
+    uint64_t graph_clock = 0;
+    bool capturing = false;
+    hipStream_t cap_stream = nullptr;  // graphs are captured here, launched on the caller's
     hipEvent_t pin_ev[2]{};
     int pin_i = 0;
     StepMeta last_meta{};
@@ -395,13 +409,14 @@ template <class Fn>
 int timed(codec *c, const char *name, int64_t units, hipStream_t s, Fn &&fn)
 {
     hipEvent_t a = nullptr, b = nullptr;
-    if (c->prof) {
+    const bool prof = c->prof && !c->capturing;
+    if (prof) {
         a = get_ev(c);
         b = get_ev(c);
         (void)hipEventRecord(a, s);
     }
     hipError_t e = fn();
-    if (c->prof) {
+    if (prof) {
         (void)hipEventRecord(b, s);
         c->recs.push_back({cls_id(c, name), a, b, units});
     }
@@ -584,15 +599,19 @@ int enqueue_transformer(codec *c, int B, int F, const StepMeta &m, hipStream_t s
 // One decode step over B streams (slots[] / n[] / codes[] already validated).
 // codes: host array (copied with the metadata) or, when codes_on_device,
 // a device array read in place.
-int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int32_t *codes,
-                 float *pcm, hipStream_t s, bool codes_on_device = false)
+// Step metadata written into host buffer hp; m points into the device copy.
+struct MetaLayout {
+    size_t total = 0;  // int32 elements to copy
+    StepMeta m{};
+};
+
+MetaLayout fill_meta(codec *c, int32_t *hp, int B, const int *slots, const int32_t *n,
+                     const int32_t *codes, bool codes_on_device)
 {
     const codec_cfg &g = c->cfg;
     int F = 0;
     for (int b = 0; b < B; b++)
         F += n[b];
-
-    // ---- batch assembly into the pinned ring, one H2D copy ----
     size_t ncodes = codes_on_device ? 0 : (size_t)F * g.K;
     size_t o_codes = 0, o_fs = round4(o_codes + ncodes), o_cu = round4(o_fs + F),
            o_slot = round4(o_cu + B + 1), o_fresh = round4(o_slot + B),
@@ -604,10 +623,6 @@ int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int3
             o_tile[i] = total;
             total = round4(total + B + 1);
         }
-    int pi = c->pin_i;
-    c->pin_i ^= 1;
-    HIPCHK(c, hipEventSynchronize(c->pin_ev[pi]));  // the copy that last read this buffer is done
-    int32_t *hp = (int32_t *)c->pinned[pi];
     if (!codes_on_device)
         memcpy(hp + o_codes, codes, sizeof(int32_t) * (size_t)F * g.K);
     int acc = 0;
@@ -638,12 +653,24 @@ int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int3
         m.tile_cu[i] = dm + o_tile[i];
         m.n_tiles[i] = tc[B];
     }
-    int rc = timed(c, "h2d_meta", (int64_t)total * 4, s, [&] {
-        return hipMemcpyAsync(c->meta_dev, hp, total * 4, hipMemcpyHostToDevice, s);
+    MetaLayout out;
+    out.total = total;
+    out.m = m;
+    return out;
+}
+
+// The step's device work on stream s: the metadata copy from hp, then every
+// kernel.  Only asynchronous calls, so that a graph can capture it.
+int enqueue_device(codec *c, int B, int F, const MetaLayout &ml, const int32_t *hp, float *pcm,
+                   hipStream_t s)
+{
+    const codec_cfg &g = c->cfg;
+    const StepMeta &m = ml.m;
+    int rc = timed(c, "h2d_meta", (int64_t)ml.total * 4, s, [&] {
+        return hipMemcpyAsync(c->meta_dev, hp, ml.total * 4, hipMemcpyHostToDevice, s);
     });
     if (rc)
         return rc;
-    HIPCHK(c, hipEventRecord(c->pin_ev[pi], s));
 
     // ---- device work ----
     rc = timed(c, "halo_fill", B, s,
@@ -761,14 +788,38 @@ int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int3
                [&] { return launch_halo_save(c->halo_save, c->state, m, B, s); });
     if (rc)
         return rc;
+    c->last_meta = m;
+    c->lastF = F;
+    c->lastB = B;
+    return CODEC_OK;
+}
 
+// Host bookkeeping of a step that has been enqueued.
+void step_done(codec *c, int B, const int *slots, const int32_t *n)
+{
     for (int b = 0; b < B; b++) {
         c->slot_pos[slots[b]] += n[b];
         c->slot_fresh[slots[b]] = 0;
     }
-    c->last_meta = m;
-    c->lastF = F;
-    c->lastB = B;
+}
+
+int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int32_t *codes,
+                 float *pcm, hipStream_t s, bool codes_on_device = false)
+{
+    int F = 0;
+    for (int b = 0; b < B; b++)
+        F += n[b];
+    // batch assembly into the pinned ring, one H2D copy
+    int pi = c->pin_i;
+    c->pin_i ^= 1;
+    HIPCHK(c, hipEventSynchronize(c->pin_ev[pi]));  // the copy that last read this buffer is done
+    int32_t *hp = (int32_t *)c->pinned[pi];
+    MetaLayout ml = fill_meta(c, hp, B, slots, n, codes, codes_on_device);
+    int rc = enqueue_device(c, B, F, ml, hp, pcm, s);
+    if (rc)
+        return rc;
+    HIPCHK(c, hipEventRecord(c->pin_ev[pi], s));
+    step_done(c, B, slots, n);
     return CODEC_OK;
 }
 
@@ -1172,6 +1223,17 @@ int codec_close(codec_t *c)
         if (c->pinned[i])
             (void)hipHostFree(c->pinned[i]);
     }
+    if (c->cap_stream)
+        (void)hipStreamDestroy(c->cap_stream);
+    for (auto &kv : c->graphs)
+        for (int i = 0; i < 2; i++) {
+            if (kv.second.exec[i])
+                (void)hipGraphExecDestroy(kv.second.exec[i]);
+            if (kv.second.done[i])
+                (void)hipEventDestroy(kv.second.done[i]);
+            if (kv.second.pinned[i])
+                (void)hipHostFree(kv.second.pinned[i]);
+        }
     for (void *p : c->allocs)
         (void)hipFree(p);
     delete c;
@@ -1314,6 +1376,106 @@ int decode_chunk_device(codec_t *c, int32_t B, const int32_t *ids, const int32_t
         return rc;
     HIPCHK(c, hipSetDevice(c->dev));
     return enqueue_step(c, B, slots.data(), n, codes_dev, pcm, (hipStream_t)stream, true);
+}
+
+#define SNRVQ_MAX_GRAPHS 64
+
+static void graph_free(codec *c, codec::GraphEntry &e)
+{
+    for (int i = 0; i < 2; i++) {
+        if (e.done[i])
+            (void)hipEventSynchronize(e.done[i]);
+        if (e.exec[i])
+            (void)hipGraphExecDestroy(e.exec[i]);
+        if (e.done[i])
+            (void)hipEventDestroy(e.done[i]);
+        if (e.pinned[i])
+            (void)hipHostFree(e.pinned[i]);
+    }
+    (void)c;
+}
+
+int decode_chunk_graph(codec_t *c, int32_t B, const int32_t *ids, const int32_t *n,
+                       const int32_t *codes, float *pcm, int64_t pcm_capacity,
+                       codec_hip_stream stream)
+{
+    if (!c)
+        return set_err(nullptr, CODEC_EINVAL, "decode_chunk_graph: NULL codec");
+    std::vector<int> slots;
+    int rc = check_step(c, B, ids, n, codes, pcm, pcm_capacity, false, slots);
+    if (rc)
+        return rc;
+    HIPCHK(c, hipSetDevice(c->dev));
+    hipStream_t s = (hipStream_t)stream;
+    int F = 0;
+    std::vector<int64_t> key;
+    key.reserve((size_t)B + 2);
+    key.push_back(B);
+    for (int b = 0; b < B; b++) {
+        key.push_back(n[b]);
+        F += n[b];
+    }
+    key.push_back((int64_t)(uintptr_t)pcm);
+    auto it = c->graphs.find(key);
+    if (it == c->graphs.end()) {
+        if (c->graphs.size() >= SNRVQ_MAX_GRAPHS) {  // evict the least recently used shape
+            auto lru = c->graphs.begin();
+            for (auto jt = c->graphs.begin(); jt != c->graphs.end(); ++jt)
+                if (jt->second.last_use < lru->second.last_use)
+                    lru = jt;
+            graph_free(c, lru->second);
+            c->graphs.erase(lru);
+        }
+        it = c->graphs.emplace(key, codec::GraphEntry{}).first;
+    }
+    codec::GraphEntry &e = it->second;
+    e.last_use = ++c->graph_clock;
+    const int inst = e.next;
+    e.next ^= 1;
+    if (!e.pinned[inst]) {
+        HIPCHK(c, hipHostMalloc(&e.pinned[inst], c->meta_cap * 4, hipHostMallocDefault));
+        HIPCHK(c, hipEventCreateWithFlags(&e.done[inst], hipEventDisableTiming));
+    } else {
+        HIPCHK(c, hipEventSynchronize(e.done[inst]));  // its last replay read the buffer
+    }
+    int32_t *hp = (int32_t *)e.pinned[inst];
+    MetaLayout ml = fill_meta(c, hp, B, slots.data(), n, codes, false);
+    if (!e.exec[inst]) {
+        // capture on the codec's own stream (the caller's may be the null
+        // stream, which cannot be captured); nothing runs during capture
+        if (!c->cap_stream)
+            HIPCHK(c, hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking));
+        hipGraph_t graph = nullptr;
+        c->capturing = true;
+        hipError_t ce = hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal);
+        if (ce != hipSuccess) {
+            c->capturing = false;
+            return fail(c, CODEC_EHIP, "decode_chunk_graph: capture failed: %s",
+                        hipGetErrorString(ce));
+        }
+        rc = enqueue_device(c, B, F, ml, hp, pcm, c->cap_stream);
+        ce = hipStreamEndCapture(c->cap_stream, &graph);
+        c->capturing = false;
+        if (rc) {
+            if (graph)
+                (void)hipGraphDestroy(graph);
+            return rc;
+        }
+        if (ce != hipSuccess)
+            return fail(c, CODEC_EHIP, "decode_chunk_graph: capture failed: %s",
+                        hipGetErrorString(ce));
+        ce = hipGraphInstantiate(&e.exec[inst], graph, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(graph);
+        if (ce != hipSuccess) {
+            e.exec[inst] = nullptr;
+            return fail(c, CODEC_EHIP, "decode_chunk_graph: instantiate failed: %s",
+                        hipGetErrorString(ce));
+        }
+    }
+    HIPCHK(c, hipGraphLaunch(e.exec[inst], s));
+    HIPCHK(c, hipEventRecord(e.done[inst], s));
+    step_done(c, B, slots.data(), n);
+    return CODEC_OK;
 }
 
 int codec_device_status(codec_t *c, int64_t *bad)

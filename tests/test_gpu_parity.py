@@ -501,3 +501,36 @@ def test_stateless_window_redecode_matches_stateful_c2():
     say(f"stateless stream 0 vs oracle: err/peak {e:.3e} AC-rel {ac:.3e}; windows {sorted(wins)}")
     assert e <= tol_for(cfg)
     c.close()
+
+
+# --------------------------------------------------------------------------
+# Graph replay (one launch per step for a repeated chunk shape)
+# --------------------------------------------------------------------------
+def test_graph_replay_bitwise_equals_eager():
+    """decode_chunk_graph captures a step per chunk shape and replays it with
+    new codes and state; every replay must equal the eager decode_chunk of the
+    same step bit for bit.  Replays are interleaved with eager work and host
+    synchronisations, shapes change and come back (capture, cache hit)."""
+    cfg = RI.get_config("c2")
+    c = open_codec(cfg)
+    H = c.hop
+    B = 4
+    plan = [1, 2, 4, 8, 8, 8, 8, 3, 8, 8, 2, 8, 8]
+    T = sum(plan)
+    codes = [RI.stream_codes(cfg, b, T, part=7) for b in range(B)]
+    ids_g = [c.stream_open() for _ in range(B)]
+    ids_e = [c.stream_open() for _ in range(B)]
+    pcm_g = torch.empty(max(plan) * B * H, dtype=torch.float32, device="cuda")
+    at = 0
+    say("case graph replay: plan", plan)
+    for k, n in enumerate(plan):
+        packed = np.concatenate([cb[at:at + n] for cb in codes])
+        c.decode_chunk_graph(ids_g, [n] * B, packed, pcm_g)
+        torch.cuda.synchronize()
+        got = pcm_g[:n * B * H].cpu().numpy()
+        pcm_e = torch.empty(n * B * H, dtype=torch.float32, device="cuda")
+        c.decode_chunk(ids_e, [n] * B, packed, pcm_e)
+        ref = pcm_e.cpu().numpy()
+        assert np.array_equal(got, ref), f"step {k} (n={n}): graph replay differs from eager"
+        at += n
+    c.close()
