@@ -719,7 +719,9 @@ int enqueue_device(codec *c, int B, int F, const MetaLayout &ml, const int32_t *
         for (int j = 0; j < 2; j++) {
             void *in = j == 0 ? c->a1[i] : c->a2[i];
             int inH = 6 * RU_DIL[j];
-            if (!c->fusable[i] && ru_gemm_supported(c->ch[i + 1], c->dtype)) {
+            // (with enough rows to fill the GPU without splitting K)
+            if (!c->fusable[i] && ru_gemm_supported(c->ch[i + 1], c->dtype) &&
+                (int64_t)F * ro >= 64LL * c->n_cu) {
                 // the whole residual unit in one launch: h never leaves the chip
                 a = conv_args(c, c->conv7[i][j], in, inH, ro, F * ro, m);
                 a.W1 = c->conv1[i][j].Wt;

@@ -483,16 +483,22 @@ ConvPlan conv_gemm_plan(const ConvArgs &a, int dtype, int n_cu, long partial_cap
         }
     }
     if (a.splits_allowed && partial_cap > 0) {
+        // the first tile whose K splits (>= 8 K stages each) cover the CUs;
+        // failing that (a few rows only), the most work-groups any split gives
         for (int i = 0; i < n; i++) {
             if (a.N % t[i].BN != 0 || a.Cin % t[i].BK != 0)
                 continue;
             long tiles = (long)((a.M + t[i].BM - 1) / t[i].BM) * (a.N / t[i].BN);
             int nk = Ktot / t[i].BK;
-            for (int sp = 2; sp <= 8; sp++) {
+            for (int sp = 2; sp <= 32; sp++) {
                 if (nk / sp < 8 || (long)sp * a.M * a.N > partial_cap)
                     break;
                 if (tiles * sp >= (long)n_cu)
                     return ConvPlan{i, sp};
+                if (tiles * sp > best_work) {
+                    best_work = tiles * sp;
+                    best = ConvPlan{i, sp};
+                }
             }
         }
     }
