@@ -466,39 +466,38 @@ void set_division(ConvArgs &a)
 // split, partials within the workspace) until the CUs are covered.
 ConvPlan conv_gemm_plan(const ConvArgs &a, int dtype, int n_cu, long partial_cap)
 {
+    // LDS bandwidth bounds this kernel, and a larger tile reads fewer LDS
+    // bytes per MFMA (a 64 x 64 wave tile half as many as a 32 x 32 one).  So
+    // the tiles are tried largest first, and the first that reaches 1.5 work-
+    // groups per CU -- alone, or with K split (>= 8 K stages per split) -- is
+    // taken; failing all, the plan with the most work-groups.
     const TileDesc *t = dtype ? H_TILES : F_TILES;
     const int n = dtype ? NH : NF;
     const int Ktot = a.taps * a.Cin;  // a K stage must not straddle two taps
+    const long target = 3L * n_cu / 2;
     ConvPlan best{-1, 1};
     long best_work = -1;
     for (int i = 0; i < n; i++) {
         if (a.N % t[i].BN != 0 || a.Cin % t[i].BK != 0)
             continue;
-        long tiles = (long)((a.M + t[i].BM - 1) / t[i].BM) * (a.N / t[i].BN);
-        if (tiles >= 2L * n_cu)
+        const long tiles = (long)((a.M + t[i].BM - 1) / t[i].BM) * (a.N / t[i].BN);
+        if (tiles >= target)
             return ConvPlan{i, 1};
         if (tiles > best_work) {
             best_work = tiles;
             best = ConvPlan{i, 1};
         }
-    }
-    if (a.splits_allowed && partial_cap > 0) {
-        // the first tile whose K splits (>= 8 K stages each) cover the CUs;
-        // failing that (a few rows only), the most work-groups any split gives
-        for (int i = 0; i < n; i++) {
-            if (a.N % t[i].BN != 0 || a.Cin % t[i].BK != 0)
-                continue;
-            long tiles = (long)((a.M + t[i].BM - 1) / t[i].BM) * (a.N / t[i].BN);
-            int nk = Ktot / t[i].BK;
-            for (int sp = 2; sp <= 32; sp++) {
-                if (nk / sp < 8 || (long)sp * a.M * a.N > partial_cap)
-                    break;
-                if (tiles * sp >= (long)n_cu)
-                    return ConvPlan{i, sp};
-                if (tiles * sp > best_work) {
-                    best_work = tiles * sp;
-                    best = ConvPlan{i, sp};
-                }
+        if (!a.splits_allowed || partial_cap <= 0)
+            continue;
+        const int nk = Ktot / t[i].BK;
+        for (int sp = 2; sp <= 32; sp++) {
+            if (nk / sp < 8 || (long)sp * a.M * a.N > partial_cap)
+                break;
+            if (tiles * sp >= target)
+                return ConvPlan{i, sp};
+            if (tiles * sp > best_work) {
+                best_work = tiles * sp;
+                best = ConvPlan{i, sp};
             }
         }
     }
