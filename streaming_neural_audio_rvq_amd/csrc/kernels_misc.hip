@@ -13,6 +13,7 @@ namespace {
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 // blockIdx.x = batch index b, blockIdx.y = halo layer.  Copies the slot's H
 // rows into the halo of stream b (zeros for a fresh stream).
@@ -143,10 +144,14 @@ __global__ __launch_bounds__(256) void final_conv_kernel(const T *A, int A_H, in
                                                          const int32_t *frame_stream, int M,
                                                          float *pcm)
 {
-    extern __shared__ float wsh[];  // [7][C]
+    extern __shared__ float wsh[];  // [7][C]: fp32, or fp16 pairs for fp16 operands
+    h2 *wsh16 = (h2 *)wsh;
     for (int i = threadIdx.x; i < 7 * C; i += blockDim.x) {
         int c = i / 7, j = i - c * 7;  // input layout [C][7]
-        wsh[j * C + c] = w[i];
+        if (sizeof(T) == 2)
+            ((half_t *)wsh16)[j * C + c] = (half_t)w[i];
+        else
+            wsh[j * C + c] = w[i];
     }
     __syncthreads();
     long m = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -161,13 +166,26 @@ __global__ __launch_bounds__(256) void final_conv_kernel(const T *A, int A_H, in
         float part = 0.f;
         for (int j = 0; j < 7; j++) {
             const T *row = A + (ext - (6 - j)) * C + qp * CQ;
-            const float *wj = wsh + j * C + qp * CQ;
-            for (int c = 0; c < CQ; c += VEC) {
-                float v[8];
-                unpack<T>(row + c, VEC, v);
+            if constexpr (sizeof(T) == 2) {
+                // fp16 operands: pairs of channels on v_dot2 (fp32 accumulation),
+                // taps then channel pairs in order
+                const h2 *wj = wsh16 + (j * C + qp * CQ) / 2;
+                for (int c = 0; c < CQ; c += 8) {
+                    const h8 v = *(const h8 *)(row + c);
 #pragma unroll
-                for (int e = 0; e < VEC; e++)
-                    part += wj[c + e] * v[e];
+                    for (int e = 0; e < 4; e++)
+                        part = __builtin_amdgcn_fdot2(h2{v[2 * e], v[2 * e + 1]}, wj[c / 2 + e],
+                                                      part, false);
+                }
+            } else {
+                const float *wj = wsh + j * C + qp * CQ;
+                for (int c = 0; c < CQ; c += VEC) {
+                    float v[8];
+                    unpack<T>(row + c, VEC, v);
+#pragma unroll
+                    for (int e = 0; e < VEC; e++)
+                        part += wj[c + e] * v[e];
+                }
             }
         }
         q[qp] = part;

@@ -49,6 +49,7 @@ namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t Chunk __attribute__((ext_vector_type(4)));
 
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
     __shared__ __attribute__((aligned(16))) half_t a2s[A2_ELEMS];  // a2; ConvT chunks (streamed)
     __shared__ __attribute__((aligned(16))) half_t wsm[W_ELEMS];
     __shared__ __attribute__((aligned(16))) float prm[P_COUNT * C];
-    __shared__ float wout_s[FINAL ? 7 * C : 1];  // final conv weights, [tap][channel]
+    __shared__ h2 wout_s[FINAL ? 7 * C / 2 : 1];  // final conv weights, fp16 [tap][channel]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
     if (FINAL) {
         for (int i = tid; i < 7 * C; i += NTH) {
             const int c = i / 7, j = i - c * 7;  // input layout [C][7]
-            wout_s[j * C + c] = p.w_out[i];
+            ((half_t *)wout_s)[j * C + c] = (half_t)p.w_out[i];
         }
     }
     half_t *const wTs = wsm;
@@ -505,15 +506,17 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
                 const int tt = i >> 2, qp = i & 3;
                 float part = 0.f;
                 if (tt < nsamp) {
+                    // taps, then channel pairs on v_dot2 (the per-layer final conv's order)
 #pragma unroll
                     for (int j = 0; j < 7; j++) {
-                        const float *wj = wout_s + j * C + qp * (C / 4);
+                        const h2 *wj = wout_s + (j * C + qp * (C / 4)) / 2;
 #pragma unroll
                         for (int c0 = 0; c0 < C / 4; c0 += 8) {
                             const h8 v = *(const h8 *)(a1s + L::off(tt + j, qp * (C / 4) + c0));
 #pragma unroll
-                            for (int e = 0; e < 8; e++)
-                                part += wj[c0 + e] * (float)v[e];
+                            for (int e = 0; e < 4; e++)
+                                part = __builtin_amdgcn_fdot2(h2{v[2 * e], v[2 * e + 1]},
+                                                              wj[c0 / 2 + e], part, false);
                         }
                     }
                 }
