@@ -108,17 +108,25 @@ __global__ __launch_bounds__(256) void window_attention_kernel(AttnArgs a)
     const float q = a.qkv[(long)f * 3 * dm + h * hd + lane];
     const long ring_base = ((long)a.slot[b] * a.n_layers + a.layer) * W1 * dm;
     const float scale = 1.0f / sqrtf((float)hd);
+    // key kk: ring slot (jlo + kk) mod (W-1) while j < p0, else this step's row
+    const int nring = (int)(p0 - jlo > 0 ? p0 - jlo : 0);  // keys held in the ring
+    const int slot0 = (int)(jlo % W1);
+    const float *kr = a.kring + ring_base + h * hd + lane;
+    const float *vr = a.vring + ring_base + h * hd + lane;
+    const long row0 = (long)a.cu[b] * 3 * dm + h * hd + lane;  // this step's first frame
     float sc[SNRVQ_MAX_WINDOW];  // fully unrolled: stays in registers
     float mx = -INFINITY;
 #pragma unroll
     for (int kk = 0; kk < SNRVQ_MAX_WINDOW; kk++) {
         if (kk < nk) {
-            long j = jlo + kk;
             float kv;
-            if (j < p0)
-                kv = a.kring[ring_base + (j % W1) * dm + h * hd + lane];
-            else
-                kv = a.qkv[(long)(a.cu[b] + (j - p0)) * 3 * dm + dm + h * hd + lane];
+            if (kk < nring) {
+                int sl = slot0 + kk;
+                sl = sl >= W1 ? sl - W1 : sl;
+                kv = kr[(long)sl * dm];
+            } else {
+                kv = a.qkv[row0 + (long)(kk - nring + (jlo + nring - p0)) * 3 * dm + dm];
+            }
             float s = wave_sum(q * kv) * scale;
             sc[kk] = s;
             mx = fmaxf(mx, s);
@@ -136,12 +144,14 @@ __global__ __launch_bounds__(256) void window_attention_kernel(AttnArgs a)
 #pragma unroll
     for (int kk = 0; kk < SNRVQ_MAX_WINDOW; kk++) {
         if (kk < nk) {
-            long j = jlo + kk;
             float vv;
-            if (j < p0)
-                vv = a.vring[ring_base + (j % W1) * dm + h * hd + lane];
-            else
-                vv = a.qkv[(long)(a.cu[b] + (j - p0)) * 3 * dm + 2 * dm + h * hd + lane];
+            if (kk < nring) {
+                int sl = slot0 + kk;
+                sl = sl >= W1 ? sl - W1 : sl;
+                vv = vr[(long)sl * dm];
+            } else {
+                vv = a.qkv[row0 + (long)(kk - nring + (jlo + nring - p0)) * 3 * dm + 2 * dm];
+            }
             acc += sc[kk] * vv;
         }
     }
@@ -156,13 +166,14 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AttnArgs a)
     const int n = a.cu[b + 1] - a.cu[b];
     const int keep = n < W1 ? n : W1;
     const long ring_base = ((long)a.slot[b] * a.n_layers + a.layer) * W1 * dm;
-    for (int e = threadIdx.x; e < keep * dm; e += 256) {
-        int t = n - keep + e / dm;
-        int c = e % dm;
-        long p = (long)a.pos[b] + t;
-        long f = a.cu[b] + t;
-        a.kring[ring_base + (p % W1) * dm + c] = a.qkv[f * 3 * dm + dm + c];
-        a.vring[ring_base + (p % W1) * dm + c] = a.qkv[f * 3 * dm + 2 * dm + c];
+    int sl = (int)(((long)a.pos[b] + (n - keep)) % W1);  // ring slot of the first kept frame
+    for (int t = n - keep; t < n; t++) {
+        const long f = a.cu[b] + t;
+        for (int c = threadIdx.x; c < dm; c += 256) {
+            a.kring[ring_base + (long)sl * dm + c] = a.qkv[f * 3 * dm + dm + c];
+            a.vring[ring_base + (long)sl * dm + c] = a.qkv[f * 3 * dm + 2 * dm + c];
+        }
+        sl = sl + 1 == W1 ? 0 : sl + 1;
     }
 }
 
