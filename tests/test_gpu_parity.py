@@ -534,3 +534,29 @@ def test_graph_replay_bitwise_equals_eager():
         assert np.array_equal(got, ref), f"step {k} (n={n}): graph replay differs from eager"
         at += n
     c.close()
+
+
+# --------------------------------------------------------------------------
+# ELU decoder (per-layer path everywhere, residual-unit GEMM included)
+# --------------------------------------------------------------------------
+def test_elu_decoder_vs_oracle():
+    """The Qwen-shaped decoder with ELU instead of Snake (the selectable
+    activation): no fused stage applies, so every conv runs on the per-layer
+    kernels; 8 streams x 16 frames put enough rows into stage 2 for its
+    residual units to run as single launches.  Against the oracle."""
+    cfg = RI.get_config("c2", act="elu")
+    w = RI.make_weights(cfg)
+    c = open_codec(cfg, w)
+    B = 8
+    plan = [3, 16, 5]
+    codes = [RI.stream_codes(cfg, b, sum(plan), part=11) for b in range(B)]
+    say("case ELU decoder: plan", plan)
+    ids = [c.stream_open() for _ in range(B)]
+    got = run_lockstep(c, ids, codes, plan)
+    m = oracle.Model(cfg, w)
+    for b in (0, 5):
+        ref = m.stream().decode(codes[b])
+        e, ac = rel_err(got[b], ref)
+        say(f"ELU stream {b}: err/peak {e:.3e} AC-rel {ac:.3e}")
+        assert e <= tol_for(cfg)
+    c.close()
