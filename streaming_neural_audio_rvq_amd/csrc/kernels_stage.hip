@@ -90,17 +90,25 @@ struct Rows {
     {
         return PAD ? n * (C + 8) : (C == 64 ? n * 64 : ((n + 1) / 2) * 64);
     }
-    __device__ static __forceinline__ int off(int i, int c)
+    // off(i, c) == at(base(i), c): the row part once, then one add (padded)
+    // or one xor (permuted: c < C only touches the low bits base permutes)
+    __device__ static __forceinline__ int base(int i)
     {
-        if constexpr (PAD) {
-            return i * (C + 8) + c;
-        } else if constexpr (C == 64) {
-            return i * 64 + ((((c >> 3) ^ (i >> LOG_S)) & 7) << 3) + (c & 7);
-        } else {
-            return (i >> 1) * 64 + (((((i & 1) << 2) | (c >> 3)) ^ (i >> LOG_S)) & 7) * 8 +
-                   (c & 7);
-        }
+        if constexpr (PAD)
+            return i * (C + 8);
+        else if constexpr (C == 64)
+            return i * 64 + (((i >> LOG_S) & 7) << 3);
+        else
+            return (i >> 1) * 64 + (((((i & 1) << 2) ^ (i >> LOG_S)) & 7) << 3);
     }
+    __device__ static __forceinline__ int at(int b, int c)
+    {
+        if constexpr (PAD)
+            return b + c;
+        else
+            return b ^ c;
+    }
+    __device__ static __forceinline__ int off(int i, int c) { return at(base(i), c); }
 };
 
 // Per-channel parameter rows in LDS ([P_COUNT][C] fp32).
@@ -333,13 +341,13 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
             // epilogue: + bias -> x; Snake -> a1
 #pragma unroll
             for (int r = 0; r < S; r++) {
-                const int i = q * S + r - r1;
+                const int bi = L::base(q * S + r - r1);
 #pragma unroll
                 for (int n = 0; n < NB; n++) {
                     const int c = n * 16 + lg * 4;
                     x[r][n] = x[r][n] + *(const f4 *)(prm + P_BT * C + c);
                     if (qok)
-                        *(h4 *)(a1s + L::off(i, c)) =
+                        *(h4 *)(a1s + L::at(bi, c)) =
                             snake4(x[r][n], *(const f4 *)(prm + P_A1R0 * C + c),
                                    *(const f4 *)(prm + P_A1I0 * C + c));
                 }
@@ -392,33 +400,45 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
                 for (int n = 0; n < NB; n++)
                     acc[r][n] = f4{0.f, 0.f, 0.f, 0.f};
             // one K step of 32 of the conv7 (dilation D) from weights wp (row pitch wld);
-            // block n, A row l16 computes output channel ch7(n, l16)
-            auto step7 = [&](int k0, const half_t *wp, int wld) {
-                const int tap = k0 / C, c0 = k0 - tap * C;
-                const int sh = (tap - 6) * D;
+            // block n, A row l16 computes output channel ch7(n, l16); rb: each
+            // unit's input row base for this step's tap
+            auto step7 = [&](int k0, const half_t *wp, int wld, const int (&rb)[S]) {
+                const int c0 = k0 % C;
                 h8 wf[NB];
 #pragma unroll
                 for (int n = 0; n < NB; n++)
                     wf[n] = *(const h8 *)(wp + ch7(n, l16) * wld + lg * 8);
 #pragma unroll
                 for (int r = 0; r < S; r++) {
-                    const h8 xf = *(const h8 *)(in + L::off(rowi[r] + sh, c0 + lg * 8));
+                    const h8 xf = *(const h8 *)(in + L::at(rb[r], c0 + lg * 8));
 #pragma unroll
                     for (int n = 0; n < NB; n++)
                         acc[r][n] = mma(wf[n], xf, acc[r][n]);
                 }
             };
+            auto tap_bases = [&](int tap, int (&rb)[S]) {
+#pragma unroll
+                for (int r = 0; r < S; r++)
+                    rb[r] = L::base(rowi[r] + (tap - 6) * D);
+            };
             if constexpr (RES) {
 #pragma unroll
-                for (int k0 = 0; k0 < K7; k0 += 32)
-                    step7(k0, w7s + u * C * LD7 + k0, LD7);
+                for (int tap = 0; tap < 7; tap++) {
+                    int rb[S];
+                    tap_bases(tap, rb);
+#pragma unroll
+                    for (int c0 = 0; c0 < C; c0 += 32)
+                        step7(tap * C + c0, w7s + u * C * LD7 + tap * C + c0, LD7, rb);
+                }
             } else {
 #pragma unroll 1
                 for (int j7 = 0; j7 < N7C; j7++) {
                     const half_t *wb = wsm + ((NKT + u * (N7C + 1) + j7) & 1) * RU_BUF;
+                    int rb[S];
+                    tap_bases(j7 * KC / C, rb);  // a chunk holds one tap (KC == C)
 #pragma unroll
                     for (int kin = 0; kin < KC; kin += 32)
-                        step7(j7 * KC + kin, wb + kin, LDC);
+                        step7(j7 * KC + kin, wb + kin, LDC, rb);
                     advance();
                 }
             }
@@ -457,6 +477,7 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
                     }
                 }
                 const int t = q * S + r;
+                const int bo = L::base(u == 0 ? t - r2 : t - (t0 - 6));  // a2 / a_out row
 #pragma unroll
                 for (int n = 0; n < NB; n++) {
                     const int c = n * 16 + lg * 4;
@@ -464,14 +485,14 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
                     if (!rok[r])
                         continue;
                     if (u == 0) {
-                        *(h4 *)(a2s + L::off(t - r2, c)) =
+                        *(h4 *)(a2s + L::at(bo, c)) =
                             snake4(x[r][n], *(const f4 *)(prm + P_A1R1 * C + c),
                                    *(const f4 *)(prm + P_A1I1 * C + c));
                     } else {
                         const h4 o = snake4(x[r][n], *(const f4 *)(prm + P_ANR * C + c),
                                             *(const f4 *)(prm + P_ANI * C + c));
                         if (FINAL)
-                            *(h4 *)(a1s + L::off(t - (t0 - 6), c)) = o;
+                            *(h4 *)(a1s + L::at(bo, c)) = o;
                         else
                             *(h4 *)(p.next + ((long)(b + 1) + (long)cu0 * p.r_out + t) * C +
                                     c) = o;
