@@ -202,11 +202,17 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
     }
 
     Chunk ra[A_PT], rb[B_PT];
-    // a K stage of BK never straddles two taps (C_in is a multiple of BK)
+    // a K stage of BK never straddles two taps (C_in is a multiple of BK);
+    // the (tap, channel) of the next stage advances without a division
+    int g_tap = (ks0 * BK) / p.Cin, g_c0 = ks0 * BK - g_tap * p.Cin;
     auto gload = [&](int ks) {
-        int k0 = ks * BK;
-        int tap = k0 / p.Cin;
-        int c0 = k0 - tap * p.Cin;
+        const int k0 = ks * BK;
+        const int tap = g_tap, c0 = g_c0;
+        g_c0 += BK;
+        if (g_c0 == p.Cin) {
+            g_c0 = 0;
+            g_tap++;
+        }
         long off = (long)c0 - (long)(p.taps - 1 - tap) * p.dil * p.Cin;
 #pragma unroll
         for (int i = 0; i < A_PT; i++)
@@ -262,6 +268,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
 #pragma unroll
                 for (int j = 0; j < FN; j++)
                     bf[j] = *(const h8 *)(Bb + (cbase + j * 16 + lrow) * LD + sub * 32 + lk * 8);
+                __builtin_amdgcn_s_setprio(1);  // keep the matrix pipe fed
 #pragma unroll
                 for (int i = 0; i < FM; i++)
 #pragma unroll
@@ -286,6 +293,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
                                 bf[j][kk], af[i][kk], acc[i][j], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         if (ks + 1 < ks1)
             sstore(buf ^ 1);
         __syncthreads();
