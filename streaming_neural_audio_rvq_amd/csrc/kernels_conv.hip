@@ -17,8 +17,11 @@
 //
 // Tiles: 256 threads (4 waves of 64), BM x BN output tile, K staged in steps
 // of BK = 32 KSUB (fp16, v_mfma_f32_16x16x32_f16) or 16 (fp32,
-// v_mfma_f32_16x16x4_f32).  Global loads are 16-byte chunks double-buffered
-// through LDS.  The weights are the MFMA's A operand and the activation rows
+// v_mfma_f32_16x16x4_f32).  K stages are double-buffered in LDS.  fp16
+// stages go global -> LDS directly (16-byte global_load_lds: no register
+// staging and no LDS store instructions, which would otherwise share the LDS
+// port with the fragment reads), into unpadded rows with XOR-permuted 16-byte
+// chunks so that fragment reads stay conflict-free.  The weights are the MFMA's A operand and the activation rows
 // its B operand, so each lane's accumulator holds 4 consecutive output
 // columns of one row and the epilogue stores straight from registers (4
 // channels per lane, 16 lanes per row segment).  Work-groups are remapped so that each XCD
@@ -41,6 +44,8 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 typedef uint32_t Chunk __attribute__((ext_vector_type(4)));
+#define GLOBAL_PTR(p) ((const void __attribute__((address_space(1))) *)(p))
+#define LDS_PTR(p) ((void __attribute__((address_space(3))) *)(p))
 
 template <typename T>
 struct Traits;
@@ -142,22 +147,39 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
     constexpr int BK = BK0 * KSUB;
     constexpr int VEC = 16 / (int)sizeof(T);
     constexpr int CPR = BK / VEC;  // 16-byte chunks per tile row
-    constexpr int LD = BK + VEC;   // padded LDS row, elements
+    // fp16 tiles load global -> LDS directly (no register staging, no LDS
+    // store instructions) into unpadded rows whose 16-byte chunks are
+    // XOR-permuted so that a fragment read (16 rows, one chunk) is
+    // conflict-free; fp32 tiles stage through registers into padded rows
+    constexpr bool DIRECT = sizeof(T) == 2;
+    constexpr int LD = DIRECT ? BK : BK + VEC;  // LDS row, elements
     constexpr int A_CH = BM * CPR, B_CH = BN * CPR;
     constexpr int A_PT = (A_CH + 255) / 256, B_PT = (B_CH + 255) / 256;
+    // direct: one instruction of a wave fills 1 KB = RPI whole rows
+    constexpr int RPI = 64 / CPR;
+    constexpr int A_NI = BM / RPI, B_NI = BN / RPI;  // instructions per tile
+    static_assert(!DIRECT || (BM % RPI == 0 && BN % RPI == 0), "direct rows");
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 16, FN = TN / 16;
     static_assert(WM * WN == 4, "4 waves");
     static_assert(FM >= 1 && FN >= 1 && TM % 16 == 0 && TN % 16 == 0, "wave tile");
-    constexpr int SMEM_MAIN = 2 * (BM + BN) * LD * (int)sizeof(T);
-    constexpr int SMEM_RU = RU ? (BM * (BN + 8) + 2 * BN * 72) * 2 : 0;  // h tile + 1x1 chunks
-    constexpr int SMEM = SMEM_MAIN > SMEM_RU ? SMEM_MAIN : SMEM_RU;
-    __shared__ __attribute__((aligned(16))) char smem[SMEM];
+    // the two stage buffers are separate LDS objects and the K loop is
+    // unrolled by two, so every access names its buffer statically: the
+    // compiler then knows that reads of one buffer need not wait for the
+    // direct loads in flight into the other
+    constexpr int SMEM_BUF = (BM + BN) * LD * (int)sizeof(T);
+    constexpr int SMEM_RU0 = RU ? BM * (BN + 8) * 2 : 0;  // h tile
+    constexpr int SMEM_RU1 = RU ? 2 * BN * 72 * 2 : 0;    // 1x1 weight chunks
+    constexpr int SMEM0 = SMEM_BUF > SMEM_RU0 ? SMEM_BUF : SMEM_RU0;
+    constexpr int SMEM1 = SMEM_BUF > SMEM_RU1 ? SMEM_BUF : SMEM_RU1;
+    __shared__ __attribute__((aligned(16))) char smem0[SMEM0];
+    __shared__ __attribute__((aligned(16))) char smem1[SMEM1];
     __shared__ int rowb[BM];  // stream of each tile row
-    T *As = (T *)smem;
-    T *Bs = As + 2 * BM * LD;
+    T *const A0 = (T *)smem0, *const B0 = A0 + BM * LD;
+    T *const A1 = (T *)smem1, *const B1 = A1 + BM * LD;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ntm = (p.M + BM - 1) / BM, ntn = p.N / BN;
     const int tile = xcd_remap(blockIdx.x, ntm * ntn);
     const int tm = tile / ntn, tn = tile - tm * ntn;
@@ -172,40 +194,69 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
     const int ks0 = blockIdx.y * per;
     const int ks1 = ks0 + per < nk_all ? ks0 + per : nk_all;
 
-    const T *a_ptr[A_PT];
-    int a_lds[A_PT];
+    // physical chunk of logical chunk kc in row r: kc ^ swz(r); the 8 rows
+    // one 128-byte LDS line pass spans land on 8 distinct chunks
+    auto swz = [](int r) { return DIRECT ? (r * CPR / 8) & (CPR - 1) : 0; };
+
+    // load slot i of this thread: tile row, logical chunk, LDS offset
+    auto slot = [&](int i, int nrows, int &row, int &kc, int &lo) -> bool {
+        if constexpr (DIRECT) {
+            const int blk = i * 4 + wave;
+            row = blk * RPI + lane / CPR;
+            kc = (lane % CPR) ^ swz(row);
+            lo = blk * RPI * LD;  // wave-uniform
+            if (blk >= nrows / RPI) {
+                row = 0;
+                return false;
+            }
+            return true;
+        } else {
+            const int c = tid + i * 256;
+            row = c / CPR;
+            kc = c % CPR;
+            lo = row * LD + kc * VEC;
+            if (c >= nrows * CPR) {
+                row = 0;
+                return false;
+            }
+            return true;
+        }
+    };
+    constexpr int A_N = DIRECT ? (A_NI + 3) / 4 : A_PT;
+    constexpr int B_N = DIRECT ? (B_NI + 3) / 4 : B_PT;
+    constexpr bool A_FULL = DIRECT ? A_NI % 4 == 0 : A_CH % 256 == 0;
+    constexpr bool B_FULL = DIRECT ? B_NI % 4 == 0 : B_CH % 256 == 0;
+
+    const T *a_ptr[A_N];
+    int a_lds[A_N];
+    bool a_ok[A_N];
 #pragma unroll
-    for (int i = 0; i < A_PT; i++) {
-        int c = tid + i * 256;
-        int row = c / CPR, kc = c % CPR;
-        if (c >= A_CH)
-            row = 0;
+    for (int i = 0; i < A_N; i++) {
+        int row, kc;
+        a_ok[i] = slot(i, BM, row, kc, a_lds[i]);
         int m = m0 + row;
         int mm = m < p.M ? m : p.M - 1;
         int b = p.frame_stream[frame_of(p, mm)];
         long ext = (long)(b + 1) * p.A_H + mm;
         a_ptr[i] = A + ext * p.Cin + kc * VEC;
-        if ((A_CH % 256 == 0 || c < A_CH) && kc == 0)
+        if (a_ok[i] && (DIRECT ? lane % CPR == 0 : kc == 0))
             rowb[row] = b;
-        a_lds[i] = row * LD + kc * VEC;
     }
-    const T *b_ptr[B_PT];
-    int b_lds[B_PT];
+    const T *b_ptr[B_N];
+    int b_lds[B_N];
+    bool b_ok[B_N];
 #pragma unroll
-    for (int i = 0; i < B_PT; i++) {
-        int c = tid + i * 256;
-        int row = c / CPR, kc = c % CPR;
-        if (c >= B_CH)
-            row = 0;
+    for (int i = 0; i < B_N; i++) {
+        int row, kc;
+        b_ok[i] = slot(i, BN, row, kc, b_lds[i]);
         b_ptr[i] = W + (long)(n0 + row) * Ktot + kc * VEC;
-        b_lds[i] = row * LD + kc * VEC;
     }
 
-    Chunk ra[A_PT], rb[B_PT];
+    Chunk ra[DIRECT ? 1 : A_N], rb[DIRECT ? 1 : B_N];
     // a K stage of BK never straddles two taps (C_in is a multiple of BK);
     // the (tap, channel) of the next stage advances without a division
     int g_tap = (ks0 * BK) / p.Cin, g_c0 = ks0 * BK - g_tap * p.Cin;
-    auto gload = [&](int ks) {
+    auto gload = [&](int ks, T *Ab, T *Bb) {
         const int k0 = ks * BK;
         const int tap = g_tap, c0 = g_c0;
         g_c0 += BK;
@@ -214,26 +265,45 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
             g_tap++;
         }
         long off = (long)c0 - (long)(p.taps - 1 - tap) * p.dil * p.Cin;
+        if constexpr (DIRECT) {
 #pragma unroll
-        for (int i = 0; i < A_PT; i++)
-            if (A_CH % 256 == 0 || tid + i * 256 < A_CH)
-                ra[i] = *(const Chunk *)(a_ptr[i] + off);
+            for (int i = 0; i < A_N; i++)
+                if (A_FULL || a_ok[i])
+                    __builtin_amdgcn_global_load_lds(GLOBAL_PTR(a_ptr[i] + off),
+                                                     LDS_PTR(Ab + a_lds[i]), 16, 0, 0);
 #pragma unroll
-        for (int i = 0; i < B_PT; i++)
-            if (B_CH % 256 == 0 || tid + i * 256 < B_CH)
-                rb[i] = *(const Chunk *)(b_ptr[i] + k0);
+            for (int i = 0; i < B_N; i++)
+                if (B_FULL || b_ok[i])
+                    __builtin_amdgcn_global_load_lds(GLOBAL_PTR(b_ptr[i] + k0),
+                                                     LDS_PTR(Bb + b_lds[i]), 16, 0, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < A_N; i++)
+                if (A_FULL || a_ok[i])
+                    ra[i] = *(const Chunk *)(a_ptr[i] + off);
+#pragma unroll
+            for (int i = 0; i < B_N; i++)
+                if (B_FULL || b_ok[i])
+                    rb[i] = *(const Chunk *)(b_ptr[i] + k0);
+        }
     };
-    auto sstore = [&](int buf) {
-        T *Ab = As + buf * BM * LD;
-        T *Bb = Bs + buf * BN * LD;
+    auto sstore = [&](T *Ab, T *Bb) {
+        if constexpr (!DIRECT) {
 #pragma unroll
-        for (int i = 0; i < A_PT; i++)
-            if (A_CH % 256 == 0 || tid + i * 256 < A_CH)
-                *(Chunk *)(Ab + a_lds[i]) = ra[i];
+            for (int i = 0; i < A_N; i++)
+                if (A_FULL || a_ok[i])
+                    *(Chunk *)(Ab + a_lds[i]) = ra[i];
 #pragma unroll
-        for (int i = 0; i < B_PT; i++)
-            if (B_CH % 256 == 0 || tid + i * 256 < B_CH)
-                *(Chunk *)(Bb + b_lds[i]) = rb[i];
+            for (int i = 0; i < B_N; i++)
+                if (B_FULL || b_ok[i])
+                    *(Chunk *)(Bb + b_lds[i]) = rb[i];
+        }
+    };
+    // the direct loads of a stage must have landed before the barrier that
+    // publishes it
+    auto loads_done = [&]() {
+        if constexpr (DIRECT)
+            __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
     };
 
     f4 acc[FM][FN];
@@ -247,27 +317,20 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
     const int rbase = wm * TM, cbase = wn * TN;
     const int lrow = lane & 15, lk = lane >> 4;
 
-    if (ks0 < ks1) {
-        gload(ks0);
-        sstore(0);
-    }
-    __syncthreads();
-    for (int ks = ks0; ks < ks1; ks++) {
-        const int buf = (ks - ks0) & 1;
-        if (ks + 1 < ks1)
-            gload(ks + 1);
-        const T *Ab = As + buf * BM * LD;
-        const T *Bb = Bs + buf * BN * LD;
+    const int fsw = swz(lrow);  // fragment rows are lrow + multiples of 16
+    auto mma_stage = [&](const T *Ab, const T *Bb) {
 #pragma unroll
         for (int sub = 0; sub < KSUB; sub++) {
             if constexpr (sizeof(T) == 2) {
                 h8 af[FM], bf[FN];
 #pragma unroll
                 for (int i = 0; i < FM; i++)
-                    af[i] = *(const h8 *)(Ab + (rbase + i * 16 + lrow) * LD + sub * 32 + lk * 8);
+                    af[i] = *(const h8 *)(Ab + (rbase + i * 16 + lrow) * LD +
+                                          ((sub * 4 + lk) ^ fsw) * 8);
 #pragma unroll
                 for (int j = 0; j < FN; j++)
-                    bf[j] = *(const h8 *)(Bb + (cbase + j * 16 + lrow) * LD + sub * 32 + lk * 8);
+                    bf[j] = *(const h8 *)(Bb + (cbase + j * 16 + lrow) * LD +
+                                          ((sub * 4 + lk) ^ fsw) * 8);
                 __builtin_amdgcn_s_setprio(1);  // keep the matrix pipe fed
 #pragma unroll
                 for (int i = 0; i < FM; i++)
@@ -294,8 +357,32 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
             }
         }
         __builtin_amdgcn_s_setprio(0);
-        if (ks + 1 < ks1)
-            sstore(buf ^ 1);
+    };
+
+    if (ks0 < ks1) {
+        gload(ks0, A0, B0);
+        sstore(A0, B0);
+    }
+    loads_done();
+    __syncthreads();
+    int ks = ks0;
+    for (; ks + 1 < ks1; ks += 2) {
+        // stage ks is in buffer 0, stage ks + 1 goes to buffer 1
+        gload(ks + 1, A1, B1);
+        mma_stage(A0, B0);
+        sstore(A1, B1);
+        loads_done();
+        __syncthreads();
+        if (ks + 2 < ks1)
+            gload(ks + 2, A0, B0);
+        mma_stage(A1, B1);
+        if (ks + 2 < ks1)
+            sstore(A0, B0);
+        loads_done();
+        __syncthreads();
+    }
+    if (ks < ks1) {  // odd stage count: the last stage is in buffer 0
+        mma_stage(A0, B0);
         __syncthreads();
     }
 
@@ -309,9 +396,9 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
         constexpr int NK1 = BN / B1;
         constexpr int W1_PT = BN * (B1 / 8) / 256;
         static_assert(BN * (B1 / 8) % 256 == 0 && BN % B1 == 0, "1x1 chunks");
-        static_assert((BM * HP + 2 * BN * LD1) * 2 <= SMEM, "LDS");
-        half_t *hS = (half_t *)smem;
-        half_t *w1s = hS + BM * HP;
+        static_assert(BM * HP * 2 <= SMEM0 && 2 * BN * LD1 * 2 <= SMEM1, "LDS");
+        half_t *hS = (half_t *)smem0;
+        half_t *w1s = (half_t *)smem1;
         const half_t *W1 = (const half_t *)p.W1;
         Chunk wr[W1_PT];
         auto w1load = [&](int kc) {
