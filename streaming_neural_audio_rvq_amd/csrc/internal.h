@@ -46,7 +46,7 @@ __device__ __forceinline__ float snrvq_elu(float v) { return v > 0.f ? v : __exp
 // kernel rounds the same way: to fp32 first, then to fp16.
 __device__ __forceinline__ half_t snrvq_f16(float x)
 {
-    __asm__ volatile("" : "+v"(x));
+    __asm__("" : "+v"(x));
     return (half_t)x;
 }
 

@@ -35,6 +35,7 @@
 // kernel sums the splits in split order, then applies the same epilogue.
 // No atomics: the result depends only on the shapes, never on timing.
 #include "internal.h"
+#include <type_traits>
 
 namespace snrvq {
 namespace {
@@ -58,15 +59,49 @@ struct Traits<float> {
     static constexpr int BK = 16;
 };
 
-__device__ __forceinline__ float act_fn(float v, int act, float a, float ia)
+template <int ACT>
+__device__ __forceinline__ f4 act4t(f4 v, f4 a, f4 ia)
+{
+    f4 y;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        if constexpr (ACT == ACT_SNAKE)
+            y[e] = snrvq_snake(v[e], a[e], ia[e]);
+        else if constexpr (ACT == ACT_ELU)
+            y[e] = snrvq_elu(v[e]);
+        else if constexpr (ACT == ACT_GELU)
+            y[e] = 0.5f * v[e] * (1.f + erff(v[e] * 0.7071067811865475f));
+        else
+            y[e] = v[e];
+    }
+    return y;
+}
+
+// Activation of 4 values: one uniform branch, then 4 independent evaluations.
+__device__ __forceinline__ f4 act4(f4 v, int act, f4 a, f4 ia)
 {
     if (act == ACT_SNAKE)
-        return snrvq_snake(v, a, ia);
+        return act4t<ACT_SNAKE>(v, a, ia);
     if (act == ACT_ELU)
-        return snrvq_elu(v);
+        return act4t<ACT_ELU>(v, a, ia);
     if (act == ACT_GELU)
-        return 0.5f * v * (1.f + erff(v * 0.7071067811865475f));
+        return act4t<ACT_GELU>(v, a, ia);
     return v;
+}
+
+// Calls f(std::integral_constant<int, act>) for the runtime activation, so a
+// loop over a whole tile is compiled once per activation, branch-free inside.
+template <typename F>
+__device__ __forceinline__ void with_act(int act, F &&f)
+{
+    if (act == ACT_SNAKE)
+        f(std::integral_constant<int, ACT_SNAKE>());
+    else if (act == ACT_ELU)
+        f(std::integral_constant<int, ACT_ELU>());
+    else if (act == ACT_GELU)
+        f(std::integral_constant<int, ACT_GELU>());
+    else
+        f(std::integral_constant<int, ACT_NONE>());
 }
 
 template <typename T>
@@ -106,16 +141,7 @@ __device__ __forceinline__ void epilogue4(const ConvArgs &p, int m, int b, int n
     if (p.out32)
         *(f4 *)(p.out32 + orow * p.Cout + n) = v;
     if (p.out16) {
-        f4 y;
-        if (p.act == ACT_SNAKE) {
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-                y[e] = act_fn(v[e], ACT_SNAKE, al[e], ial[e]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-                y[e] = act_fn(v[e], p.act, 0.f, 0.f);
-        }
+        const f4 y = act4(v, p.act, al, ial);
         long base = ((long)(b + 1) * p.out_H + orow) * p.Cout + n;
         store4<T>((T *)p.out16 + base, y);
     }
@@ -416,26 +442,24 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
             }
         };
         w1load(0);
+        with_act(p.act7, [&](auto act) {
 #pragma unroll
-        for (int j = 0; j < FN; j++) {
-            const int ch = cbase + j * 16 + lk * 4;  // one N tile: n0 == 0
-            const f4 b7 = *(const f4 *)(p.bias7 + ch);
-            f4 a7 = f4{0.f, 0.f, 0.f, 0.f}, ia7 = a7;
-            if (p.act7 == ACT_SNAKE) {
-                a7 = *(const f4 *)(p.alpha7 + ch);
-                ia7 = *(const f4 *)(p.inv_alpha7 + ch);
+            for (int j = 0; j < FN; j++) {
+                const int ch = cbase + j * 16 + lk * 4;  // one N tile: n0 == 0
+                const f4 b7 = *(const f4 *)(p.bias7 + ch);
+                f4 a7 = f4{0.f, 0.f, 0.f, 0.f}, ia7 = a7;
+                if constexpr (decltype(act)::value == ACT_SNAKE) {
+                    a7 = *(const f4 *)(p.alpha7 + ch);
+                    ia7 = *(const f4 *)(p.inv_alpha7 + ch);
+                }
+#pragma unroll
+                for (int i = 0; i < FM; i++) {
+                    const f4 y = act4t<decltype(act)::value>(acc[i][j] + b7, a7, ia7);
+                    store4<half_t>(hS + (rbase + i * 16 + lrow) * HP + ch, y);
+                    acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+                }
             }
-#pragma unroll
-            for (int i = 0; i < FM; i++) {
-                const f4 v = acc[i][j] + b7;
-                f4 y;
-#pragma unroll
-                for (int e = 0; e < 4; e++)
-                    y[e] = act_fn(v[e], p.act7, a7[e], ia7[e]);
-                store4<half_t>(hS + (rbase + i * 16 + lrow) * HP + ch, y);
-                acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
+        });
         w1store(0);
         __syncthreads();
         for (int kc = 0; kc < NK1; kc++) {
@@ -477,21 +501,53 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
         bias4[j] = split ? f4{0.f, 0.f, 0.f, 0.f} : *(const f4 *)(p.bias + chj[j]);
         snake_params(p, chj[j], al4[j], ial4[j]);
     }
+    if (split) {
 #pragma unroll
-    for (int i = 0; i < FM; i++) {
-        const int r = rbase + i * 16 + lrow;
-        const int m = m0 + r;
-        if (m >= p.M)
-            continue;
-        const int b = rowb[r];
+        for (int i = 0; i < FM; i++) {
+            const int m = m0 + rbase + i * 16 + lrow;
+            if (m < p.M)
 #pragma unroll
-        for (int j = 0; j < FN; j++) {
-            if (split)
-                *(f4 *)(p.partial + ((long)blockIdx.y * p.M + m) * p.N + nj[j]) = acc[i][j];
-            else
-                epilogue4<T>(p, m, b, nj[j], chj[j], acc[i][j] + bias4[j], al4[j], ial4[j]);
+                for (int j = 0; j < FN; j++)
+                    *(f4 *)(p.partial + ((long)blockIdx.y * p.M + m) * p.N + nj[j]) = acc[i][j];
         }
+        return;
     }
+    // one code path per activation; per row block, the residual loads of all
+    // N fragments are issued together before any is used
+    with_act(p.out16 ? p.act : ACT_NONE, [&](auto act) {
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+            const int r = rbase + i * 16 + lrow;
+            const int m = m0 + r;
+            const int mc = m < p.M ? m : p.M - 1;  // loads stay in bounds
+            f4 v[FN];
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+                v[j] = acc[i][j] + bias4[j];
+            if (p.res) {
+                f4 rr[FN];
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+                    rr[j] = *(const f4 *)(p.res + (long)mc * p.Cout + nj[j]);
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+                    v[j] = v[j] + rr[j];
+            }
+            if (m >= p.M)
+                continue;
+            const long orow = (long)m * p.s;
+            if (p.out32)
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+                    *(f4 *)(p.out32 + orow * p.Cout + nj[j]) = v[j];
+            if (p.out16) {
+                T *o = (T *)p.out16 + ((long)(rowb[r] + 1) * p.out_H + orow) * p.Cout;
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+                    store4<T>(o + nj[j], act4t<decltype(act)::value>(v[j], al4[j], ial4[j]));
+            }
+        }
+    });
 }
 
 // Sum of the split-K partials in split order, + bias, then the epilogue.
