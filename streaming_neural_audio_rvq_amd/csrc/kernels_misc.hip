@@ -3,7 +3,9 @@
 //     slot and the halo rows of every extended conv input (one launch each
 //     per step, all layers at once);
 //   * RVQ gather-and-sum of the codebook rows of every frame;
-//   * the final causal conv to one channel (an N = 1 reduction, VALU);
+//   * the final causal conv to one channel: on the matrix cores for fp16
+//     operands (weights in row 0 of the A operand, 16 samples per MFMA
+//     column block), an N = 1 VALU reduction for fp32;
 //   * unextend: packed fp32 copy of an extended buffer (inspection only).
 #include "internal.h"
 
@@ -194,6 +196,48 @@ __global__ __launch_bounds__(256) void final_conv_kernel(const T *A, int A_H, in
     pcm[m] = tanh_out ? tanhf(acc) : acc;
 }
 
+// fp16 final conv on v_mfma_f32_16x16x32_f16, C a multiple of 32.  A wave
+// takes 16 consecutive packed samples (the B operand's columns); the A
+// operand's row 0 holds the weights of one (tap, 32-channel) K step, its other
+// rows zeros, so row 0 of the accumulator is the conv output.  K steps run
+// tap-major, channel-minor; the fused last stage runs the same sequence.
+__global__ __launch_bounds__(256) void final_conv_mfma_kernel(const half_t *A, int A_H, int C,
+                                                              int rate, const float *w,
+                                                              float bias, int tanh_out,
+                                                              const int32_t *frame_stream, int M,
+                                                              float *pcm)
+{
+    extern __shared__ float wsh[];  // fp16 [7][C]
+    half_t *w16 = (half_t *)wsh;
+    for (int i = threadIdx.x; i < 7 * C; i += blockDim.x) {
+        int c = i / 7, j = i - c * 7;  // input layout [C][7]
+        w16[j * C + c] = (half_t)w[i];
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
+    const long m0 = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 16;
+    if (m0 >= M)
+        return;
+    long m = m0 + l16;
+    const bool ok = m < M;
+    m = ok ? m : M - 1;
+    const long ext = (long)(frame_stream[m / rate] + 1) * A_H + m;
+    const h8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 7; j++) {
+        const half_t *row = A + (ext - (6 - j)) * C + lg * 8;
+        for (int k0 = 0; k0 < C; k0 += 32) {
+            const h8 wf = *(const h8 *)(w16 + j * C + k0 + lg * 8);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(l16 == 0 ? wf : zero,
+                                                        *(const h8 *)(row + k0), acc, 0, 0, 0);
+        }
+    }
+    if (lg == 0 && ok) {
+        const float y = bias + acc[0];
+        pcm[m] = tanh_out ? tanhf(y) : y;
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void unextend_kernel(const T *ext, int H, int C, int rate,
                                                        const int32_t *frame_stream, int M,
@@ -262,7 +306,11 @@ hipError_t launch_final_conv(const void *A, int dtype, int A_H, int C, int rate,
         return hipSuccess;
     dim3 grid((M + 255) / 256);
     size_t sh = sizeof(float) * 7 * C;
-    if (dtype)
+    if (dtype && C % 32 == 0)
+        hipLaunchKernelGGL(final_conv_mfma_kernel, dim3((M + 63) / 64), dim3(256), sh, st,
+                           (const half_t *)A, A_H, C, rate, w, b, final_tanh, frame_stream, M,
+                           pcm);
+    else if (dtype)
         hipLaunchKernelGGL(final_conv_kernel<half_t>, grid, dim3(256), sh, st, (const half_t *)A,
                            A_H, C, rate, w, b, final_tanh, frame_stream, M, pcm);
     else

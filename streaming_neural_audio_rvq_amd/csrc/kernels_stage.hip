@@ -66,6 +66,15 @@ __device__ __forceinline__ int ch7(int n, int row)
     return 32 * (n >> 1) + 8 * (row >> 2) + 4 * (n & 1) + (row & 3);
 }
 
+// LDS row of the k = 7 weights of output channel c: 16 n + row for
+// c == ch7(n, row), so that the 16 A rows of block n are consecutive in LDS
+// (rows 8 apart would share banks) and block n's operand is rows 16 n ..
+// 16 n + 15.
+__device__ __forceinline__ int w7_row(int c)
+{
+    return 16 * (2 * (c >> 5) + ((c >> 2) & 1)) + 4 * ((c >> 3) & 3) + (c & 3);
+}
+
 __device__ __forceinline__ h4 snake4(f4 v, f4 ar, f4 ai)
 {
     return h4{snrvq_f16(snrvq_snake(v[0], ar[0], ai[0])),
@@ -130,8 +139,17 @@ struct StageShape {
     static constexpr int NA2 = T + 18 + E;           // a2 rows: [t0 - 18 - E, t0 + T)
 };
 
+// Work-groups per CU: two for the streamed shapes of at most 4 waves (their
+// LDS fits twice), so one work-group's VALU phases overlap the other's
+// matrix phases and barrier waits; one otherwise.
+template <int NW, bool RES>
+constexpr int stage_wg_per_cu()
+{
+    return !RES && NW <= 4 ? 2 : 1;
+}
+
 template <int C, int S, int NW, bool FINAL, bool RES>
-__global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
+__global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_kernel(StageArgs p)
 {
     using SH = StageShape<C, S, NW, FINAL>;
     using L = Rows<C, S>;
@@ -149,21 +167,23 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
     constexpr int NCH = NKT + 2 * (N7C + 1);                // chunks per tile (streamed)
     static_assert(RES || (K7 % KC == 0 && C == KC), "streamed shapes");
     constexpr int RES_ELEMS = NT * LDT + 2 * C * LD7 + 2 * C * LD1;
-    constexpr int RU_BUF = C * LDC;  // one residual-unit chunk
+    constexpr int RU_BUF = C * LDC;    // one residual-unit chunk
     constexpr int CT_BUF = NT * LDCT;  // one ConvT chunk
+    constexpr int W_BUF = RU_BUF > CT_BUF ? RU_BUF : CT_BUF;
 
-    constexpr int A1_ELEMS = L::elems(SH::NA1);
-    constexpr int A2_OFF_CT = L::elems(18 + E);  // ConvT chunks sit after the a2 halo rows
-    constexpr int A2_MIN = L::elems(SH::NA2);
-    constexpr int A2_ELEMS =
-        RES ? A2_MIN : (A2_MIN > A2_OFF_CT + 2 * CT_BUF ? A2_MIN : A2_OFF_CT + 2 * CT_BUF);
-    constexpr int W_ELEMS = RES ? RES_ELEMS : 2 * RU_BUF;
+    // One activation buffer holds a1, then a2 (a1 is dead once the first
+    // unit's conv7 is done), then a_out (FINAL; a2 is dead once the second
+    // unit's conv7 is done).  Streamed weights (ConvT chunks included)
+    // alternate between two buffers.
+    constexpr int ACT_ELEMS = L::elems(SH::NA1) > L::elems(SH::NA2) ? L::elems(SH::NA1)
+                                                                    : L::elems(SH::NA2);
+    constexpr int W_ELEMS = RES ? RES_ELEMS : 2 * W_BUF;
 
-    __shared__ __attribute__((aligned(16))) half_t a1s[A1_ELEMS];  // a1, then a_out (FINAL)
-    __shared__ __attribute__((aligned(16))) half_t a2s[A2_ELEMS];  // a2; ConvT chunks (streamed)
+    __shared__ __attribute__((aligned(16))) half_t acts[ACT_ELEMS];
+    half_t *const a1s = acts, *const a2s = acts;
     __shared__ __attribute__((aligned(16))) half_t wsm[W_ELEMS];
     __shared__ __attribute__((aligned(16))) float prm[P_COUNT * C];
-    __shared__ h2 wout_s[FINAL ? 7 * C / 2 : 1];  // final conv weights, fp16 [tap][channel]
+    __shared__ __attribute__((aligned(16))) h2 wout_s[FINAL ? 7 * C / 2 : 8];  // final conv weights, fp16 [tap][channel]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
@@ -185,22 +205,23 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
     half_t *const w7s = wsm + NT * LDT;
     half_t *const w1s = w7s + 2 * C * LD7;
     if constexpr (RES) {
-        auto copy = [&](half_t *dst, int ld, const half_t *src, int rows, int cols) {
+        auto copy = [&](half_t *dst, int ld, const half_t *src, int rows, int cols, bool k7) {
             const int cpr = cols / 8;
             for (int i = tid; i < rows * cpr; i += NTH) {
                 const int r = i / cpr, c8 = (i - r * cpr) * 8;
-                *(h8 *)(dst + r * ld + c8) = *(const h8 *)(src + (long)r * cols + c8);
+                *(h8 *)(dst + (k7 ? w7_row(r) : r) * ld + c8) =
+                    *(const h8 *)(src + (long)r * cols + c8);
             }
         };
-        copy(wTs, LDT, p.WT, NT, KT);
+        copy(wTs, LDT, p.WT, NT, KT, false);
         for (int j = 0; j < 2; j++) {
-            copy(w7s + j * C * LD7, LD7, p.W7[j], C, K7);
-            copy(w1s + j * C * LD1, LD1, p.W1[j], C, C);
+            copy(w7s + j * C * LD7, LD7, p.W7[j], C, K7, true);
+            copy(w1s + j * C * LD1, LD1, p.W1[j], C, C, false);
         }
     }
 
     // ---- streamed weights: chunk j of the per-tile sequence
-    //   [0, NKT): ConvT K step j (32 wide, NT rows) -> a2s + A2_OFF_CT, buffer j & 1
+    //   [0, NKT): ConvT K step j (32 wide, NT rows)
     //   then per residual unit u: N7C conv7 chunks (KC wide), one conv1 chunk
     //   -> wsm, buffer j & 1
     constexpr int CT_PIECES = NT * 32 / 8, RU_PIECES = C * KC / 8;
@@ -235,18 +256,18 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
     };
     auto chunk_store = [&](int j, const Chunk(&r)[PPT]) {
         j %= NCH;
-        half_t *dst;
+        half_t *const dst = wsm + (j & 1) * W_BUF;
         int ldd, width, rows;
+        bool k7 = false;  // conv7 chunk: rows in w7_row order
         if (j < NKT) {
-            dst = a2s + A2_OFF_CT + (j & 1) * CT_BUF;
             ldd = LDCT;
             width = 32;
             rows = NT;
         } else {
-            dst = wsm + (j & 1) * RU_BUF;
             ldd = LDC;
             width = KC;
             rows = C;
+            k7 = (j - NKT) % (N7C + 1) < N7C;
         }
         const int n = rows * width / 8, ppr = width / 8;
 #pragma unroll
@@ -254,7 +275,7 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
             const int k = tid + i * NTH;
             if (k < n) {
                 const int row = k / ppr, c8 = (k - row * ppr) * 8;
-                *(Chunk *)(dst + row * ldd + c8) = r[i];
+                *(Chunk *)(dst + (k7 ? w7_row(row) : row) * ldd + c8) = r[i];
             }
         }
     };
@@ -326,7 +347,7 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
                     x[r][n] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NKT; ks++) {
-                const half_t *wp = RES ? wTs + ks * 32 : a2s + A2_OFF_CT + (ks & 1) * CT_BUF;
+                const half_t *wp = RES ? wTs + ks * 32 : wsm + (ks & 1) * W_BUF;
                 const int wld = RES ? LDT : LDCT;
 #pragma unroll
                 for (int r = 0; r < S; r++)
@@ -352,17 +373,12 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
                                    *(const f4 *)(prm + P_A1I0 * C + c));
                 }
             }
-            // left contexts of a stream's first tile (written by the halo fill)
+            // left context of a stream's first tile (written by the halo fill)
             if (first) {
                 const half_t *s1 = p.a1_ext + ((long)b * 6 + (long)cu0 * p.r_out) * C;
                 for (int k = tid; k < 6 * C / 8; k += NTH) {
                     const int r = k / (C / 8), c8 = (k - r * (C / 8)) * 8;
                     *(h8 *)(a1s + L::off(HX - 6 + r, c8)) = *(const h8 *)(s1 + r * C + c8);
-                }
-                const half_t *s2 = p.a2_ext + ((long)b * 18 + (long)cu0 * p.r_out) * C;
-                for (int k = tid; k < 18 * C / 8; k += NTH) {
-                    const int r = k / (C / 8), c8 = (k - r * (C / 8)) * 8;
-                    *(h8 *)(a2s + L::off(E + r, c8)) = *(const h8 *)(s2 + r * C + c8);
                 }
             }
             advance();  // a1 complete, ConvT chunks no longer read
@@ -400,14 +416,15 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
                 for (int n = 0; n < NB; n++)
                     acc[r][n] = f4{0.f, 0.f, 0.f, 0.f};
             // one K step of 32 of the conv7 (dilation D) from weights wp (row pitch wld);
-            // block n, A row l16 computes output channel ch7(n, l16); rb: each
+            // block n, A row l16 computes output channel ch7(n, l16) (LDS row
+            // 16 n + l16); rb: each
             // unit's input row base for this step's tap
             auto step7 = [&](int k0, const half_t *wp, int wld, const int (&rb)[S]) {
                 const int c0 = k0 % C;
                 h8 wf[NB];
 #pragma unroll
                 for (int n = 0; n < NB; n++)
-                    wf[n] = *(const h8 *)(wp + ch7(n, l16) * wld + lg * 8);
+                    wf[n] = *(const h8 *)(wp + (16 * n + l16) * wld + lg * 8);
 #pragma unroll
                 for (int r = 0; r < S; r++) {
                     const h8 xf = *(const h8 *)(in + L::at(rb[r], c0 + lg * 8));
@@ -433,7 +450,7 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
             } else {
 #pragma unroll 1
                 for (int j7 = 0; j7 < N7C; j7++) {
-                    const half_t *wb = wsm + ((NKT + u * (N7C + 1) + j7) & 1) * RU_BUF;
+                    const half_t *wb = wsm + ((NKT + u * (N7C + 1) + j7) & 1) * W_BUF;
                     int rb[S];
                     tap_bases(j7 * KC / C, rb);  // a chunk holds one tap (KC == C)
 #pragma unroll
@@ -442,11 +459,26 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
                     advance();
                 }
             }
+            // the unit's input is dead from here on (the streamed path's last
+            // conv7 chunk ended with a barrier): its rows take the next
+            // activation, whose left context a stream's first tile reads from
+            // the halo fill's buffers
+            if constexpr (RES)
+                __syncthreads();
+            if (first && (u == 0 || FINAL)) {
+                const half_t *sx = u == 0 ? p.a2_ext + ((long)b * 18 + (long)cu0 * p.r_out) * C
+                                          : p.ao_ext + ((long)b * 6 + (long)cu0 * p.r_out) * C;
+                const int nr = u == 0 ? 18 : 6, r0 = u == 0 ? E : 0;
+                for (int k = tid; k < nr * C / 8; k += NTH) {
+                    const int r = k / (C / 8), c8 = (k - r * (C / 8)) * 8;
+                    *(h8 *)(acts + L::off(r0 + r, c8)) = *(const h8 *)(sx + r * C + c8);
+                }
+            }
             // per unit: Snake(conv7 + b7) -> 1x1 conv -> + b1 + x.  The lane's conv7
             // accumulators of blocks 2k, 2k+1 hold channels 32k + 8 lg + 0..7 of
             // its row: exactly its B operand of the 1x1 conv's K step k.
             const half_t *w1p = RES ? w1s + u * C * LD1
-                                    : wsm + ((NKT + u * (N7C + 1) + N7C) & 1) * RU_BUF;
+                                    : wsm + ((NKT + u * (N7C + 1) + N7C) & 1) * W_BUF;
             const int w1ld = RES ? LD1 : LDC;
             const int PB7 = u ? P_B71 : P_B70, PA2R = u ? P_A2R1 : P_A2R0,
                       PA2I = u ? P_A2I1 : P_A2I0, PB1 = u ? P_B11 : P_B10;
@@ -500,15 +532,6 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
                 }
             }
             advance();  // a2 complete (u = 0) / a_out complete (u = 1)
-            if (FINAL && u == 0 && first) {
-                // left context of the final conv into a_out rows 0..5: a1 is
-                // no longer read, and phase 4 reads it after the next barrier
-                const half_t *s3 = p.ao_ext + ((long)b * 6 + (long)cu0 * p.r_out) * C;
-                for (int k = tid; k < 6 * C / 8; k += NTH) {
-                    const int r = k / (C / 8), c8 = (k - r * (C / 8)) * 8;
-                    *(h8 *)(a1s + L::off(r, c8)) = *(const h8 *)(s3 + r * C + c8);
-                }
-            }
         }
 
         if (FINAL) {
@@ -520,31 +543,29 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
                         *(const h8 *)(a1s + L::off(tend - 6 - (t0 - 6) + r, c8));
                 }
             }
-            // ---- phase 4: final conv, four threads per output sample, each
-            // over one quarter of the channels, combined as (q0+q1)+(q2+q3)
+            // ---- phase 4: final conv on the matrix cores, 16 samples per
+            // block: A row 0 holds the weights of one (tap, 32 channels) K
+            // step, the other rows zeros; K steps tap-major (the per-layer
+            // final conv's sequence)
             const int nsamp = tend - t0;
-            for (int i = tid; i < 4 * T; i += NTH) {
-                const int tt = i >> 2, qp = i & 3;
-                float part = 0.f;
-                if (tt < nsamp) {
-                    // taps, then channel pairs on v_dot2 (the per-layer final conv's order)
+            const h8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+            for (int blk = wave; blk * 16 < nsamp; blk += NW) {
+                int tt = blk * 16 + l16;
+                const bool ok = tt < nsamp;
+                tt = ok ? tt : nsamp - 1;
+                f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int j = 0; j < 7; j++) {
-                        const h2 *wj = wout_s + (j * C + qp * (C / 4)) / 2;
+                for (int j = 0; j < 7; j++) {
+                    const int bj = L::base(tt + j);
 #pragma unroll
-                        for (int c0 = 0; c0 < C / 4; c0 += 8) {
-                            const h8 v = *(const h8 *)(a1s + L::off(tt + j, qp * (C / 4) + c0));
-#pragma unroll
-                            for (int e = 0; e < 4; e++)
-                                part = __builtin_amdgcn_fdot2(h2{v[2 * e], v[2 * e + 1]},
-                                                              wj[c0 / 2 + e], part, false);
-                        }
+                    for (int k0 = 0; k0 < C; k0 += 32) {
+                        const h8 wf = *(const h8 *)((const half_t *)wout_s + j * C + k0 + lg * 8);
+                        acc = mma(l16 == 0 ? wf : zero,
+                                  *(const h8 *)(a1s + L::at(bj, k0 + lg * 8)), acc);
                     }
                 }
-                part += __shfl_xor(part, 1, 64);
-                part += __shfl_xor(part, 2, 64);
-                if (qp == 0 && tt < nsamp) {
-                    const float yv = p.b_out + part;
+                if (lg == 0 && ok) {
+                    const float yv = p.b_out + acc[0];
                     p.pcm[(long)cu0 * p.r_out + t0 + tt] = p.final_tanh ? tanhf(yv) : yv;
                 }
             }
@@ -556,21 +577,28 @@ __global__ __launch_bounds__(NW * 64) void stage_kernel(StageArgs p)
 template <int C, int S, int NW, bool FINAL, bool RES>
 hipError_t launch_stage_t(const StageArgs &a, hipStream_t st)
 {
-    const int grid = a.n_tiles < a.n_cu ? a.n_tiles : a.n_cu;
+    const int slots = a.n_cu * stage_wg_per_cu<NW, RES>();
+    const int grid = a.n_tiles < slots ? a.n_tiles : slots;
     if (grid <= 0)
         return hipSuccess;
     hipLaunchKernelGGL((stage_kernel<C, S, NW, FINAL, RES>), dim3(grid), dim3(NW * 64), 0, st, a);
     return hipGetLastError();
 }
 
+#ifndef NW_Q3
+#define NW_Q3 8
+#endif
+#ifndef NW_Q4
+#define NW_Q4 12
+#endif
 // instantiated shapes
 struct StageInst {
     int C, S, NW;
     bool final_stage, res;
 };
 constexpr StageInst INSTS[] = {
-    {64, 3, 8, false, false},  // Qwen-shaped stage 3, weights streamed
-    {32, 4, 8, true, true},    // Qwen-shaped stage 4 + final conv, weights resident
+    {64, 3, NW_Q3, false, false},  // Qwen-shaped stage 3, weights streamed
+    {32, 4, NW_Q4, true, true},    // Qwen-shaped stage 4 + final conv, weights resident
     {64, 4, 6, false, false},  // Fish-shaped stage 3, weights streamed
     {32, 2, 16, true, true},   // Fish-shaped stage 4 + final conv, weights resident
 };
@@ -594,9 +622,9 @@ hipError_t launch_stage_fused(const StageArgs &a, int C, int S, int T, bool fina
                               hipStream_t st)
 {
     if (C == 64 && S == 3 && !final_stage && T == tile_rows(INSTS[0]))
-        return launch_stage_t<64, 3, 8, false, false>(a, st);
+        return launch_stage_t<64, 3, NW_Q3, false, false>(a, st);
     if (C == 32 && S == 4 && final_stage && T == tile_rows(INSTS[1]))
-        return launch_stage_t<32, 4, 8, true, true>(a, st);
+        return launch_stage_t<32, 4, NW_Q4, true, true>(a, st);
     if (C == 64 && S == 4 && !final_stage && T == tile_rows(INSTS[2]))
         return launch_stage_t<64, 4, 6, false, false>(a, st);
     if (C == 32 && S == 2 && final_stage && T == tile_rows(INSTS[3]))
