@@ -189,21 +189,20 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
     constexpr int FM = TM / 16, FN = TN / 16;
     static_assert(WM * WN == 4, "4 waves");
     static_assert(FM >= 1 && FN >= 1 && TM % 16 == 0 && TN % 16 == 0, "wave tile");
-    // the two stage buffers are separate LDS objects and the K loop is
-    // unrolled by two, so every access names its buffer statically: the
-    // compiler then knows that reads of one buffer need not wait for the
-    // direct loads in flight into the other
+    // one LDS object holds both stage buffers and the row table; the K loop
+    // reads the current buffer while the next stage's direct loads are in
+    // flight into the other, and waits for them (vmcnt(0)) only before the
+    // barrier that publishes them
     constexpr int SMEM_BUF = (BM + BN) * LD * (int)sizeof(T);
     constexpr int SMEM_RU0 = RU ? BM * (BN + 8) * 2 : 0;  // h tile
     constexpr int SMEM_RU1 = RU ? 2 * BN * 72 * 2 : 0;    // 1x1 weight chunks
     constexpr int SMEM0 = SMEM_BUF > SMEM_RU0 ? SMEM_BUF : SMEM_RU0;
     constexpr int SMEM1 = SMEM_BUF > SMEM_RU1 ? SMEM_BUF : SMEM_RU1;
-    __shared__ __attribute__((aligned(16))) char smem0[SMEM0];
-    __shared__ __attribute__((aligned(16))) char smem1[SMEM1];
-    __shared__ int rowb[BM];  // stream of each tile row
+    __shared__ __attribute__((aligned(16))) char smem[SMEM0 + SMEM1 + BM * 4];
+    char *const smem0 = smem, *const smem1 = smem + SMEM0;
+    int *const rowb = (int *)(smem + SMEM0 + SMEM1);
     T *const A0 = (T *)smem0, *const B0 = A0 + BM * LD;
     T *const A1 = (T *)smem1, *const B1 = A1 + BM * LD;
-
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ntm = (p.M + BM - 1) / BM, ntn = p.N / BN;
@@ -391,24 +390,16 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
     }
     loads_done();
     __syncthreads();
-    int ks = ks0;
-    for (; ks + 1 < ks1; ks += 2) {
-        // stage ks is in buffer 0, stage ks + 1 goes to buffer 1
-        gload(ks + 1, A1, B1);
-        mma_stage(A0, B0);
-        sstore(A1, B1);
+    for (int ks = ks0; ks < ks1; ks++) {
+        const int buf = (ks - ks0) & 1;
+        T *const Ac = buf ? A1 : A0, *const Bc = buf ? B1 : B0;
+        T *const An = buf ? A0 : A1, *const Bn = buf ? B0 : B1;
+        if (ks + 1 < ks1)
+            gload(ks + 1, An, Bn);
+        mma_stage(Ac, Bc);
+        if (ks + 1 < ks1)
+            sstore(An, Bn);
         loads_done();
-        __syncthreads();
-        if (ks + 2 < ks1)
-            gload(ks + 2, A0, B0);
-        mma_stage(A1, B1);
-        if (ks + 2 < ks1)
-            sstore(A0, B0);
-        loads_done();
-        __syncthreads();
-    }
-    if (ks < ks1) {  // odd stage count: the last stage is in buffer 0
-        mma_stage(A0, B0);
         __syncthreads();
     }
 
