@@ -75,6 +75,11 @@ __device__ __forceinline__ int w7_row(int c)
     return 16 * (2 * (c >> 5) + ((c >> 2) & 1)) + 4 * ((c >> 3) & 3) + (c & 3);
 }
 
+// Chunk permutation of unpadded weight rows of 64 bytes (32 halves) and of
+// 128 bytes (64 halves): element k of row r sits at k ^ x(r).
+__device__ __forceinline__ int x64(int r) { return ((r >> 2) & 1) << 4; }
+__device__ __forceinline__ int x128(int r) { return ((r >> 1) & 3) << 4; }
+
 __device__ __forceinline__ h4 snake4(f4 v, f4 ar, f4 ai)
 {
     return h4{snrvq_f16(snrvq_snake(v[0], ar[0], ai[0])),
@@ -83,32 +88,35 @@ __device__ __forceinline__ h4 snake4(f4 v, f4 ar, f4 ai)
               snrvq_f16(snrvq_snake(v[3], ar[3], ai[3]))};
 }
 
-// fp16 activation rows in LDS.  The lanes of one MFMA operand read rows S
-// apart (one row of each unit), 16 bytes each; the layout spreads every 8
-// such lanes over all 32 banks.  Odd S: rows padded to an odd number of
-// 16-byte units.  Even S: rows unpadded, the 16-byte units of a row (of a row
-// pair when C = 32) permuted by (row / S) mod 8.  off(i, c): element offset
-// of channel c (a multiple of 4) of tile row i >= 0.
+// fp16 activation rows in LDS.  A 16-byte fragment read is served 16 lanes
+// per cycle: lanes 8k..8k+7 with lanes 8k+16..8k+23, i.e. 8 rows at two
+// neighbouring 16-byte chunks, over 64 four-byte banks; so the 16 reads of a
+// cycle must fall on 16 distinct 16-byte slots of a 256-byte line.  The MFMA
+// operand reads rows S apart (one row of each unit).  Odd S: rows padded to
+// C + 16 elements (a row stride of 3 x 10 slots walks all even slots).  Even
+// S: unpadded rows, row i stored at row position i ^ f(i) (low row bits
+// permuted by higher ones, so the rows of one read land on every row position
+// of the 256-byte line) with its 16-byte chunks permuted by g(i) (separating
+// the rows that still share a position).  off(i, c): element offset of
+// channel c (a multiple of 4) of tile row i >= 0.
 template <int C, int S>
 struct Rows {
     static constexpr bool PAD = S % 2 == 1;
-    static constexpr int LOG_S = S == 2 ? 1 : S == 4 ? 2 : 3;
-    static_assert(PAD || S == 2 || S == 4 || S == 8, "stride");
+    static_assert(PAD || (C == 32 && (S == 2 || S == 4)) || (C == 64 && S == 4), "layout");
     static_assert(C == 32 || C == 64, "channels");
-    static constexpr int elems(int n)
-    {
-        return PAD ? n * (C + 8) : (C == 64 ? n * 64 : ((n + 1) / 2) * 64);
-    }
+    static constexpr int elems(int n) { return PAD ? n * (C + 16) : ((n + 3) / 4) * 4 * C; }
     // off(i, c) == at(base(i), c): the row part once, then one add (padded)
-    // or one xor (permuted: c < C only touches the low bits base permutes)
+    // or one xor (permuted: c < C only touches the chunk bits g permutes)
     __device__ static __forceinline__ int base(int i)
     {
         if constexpr (PAD)
-            return i * (C + 8);
+            return i * (C + 16);
         else if constexpr (C == 64)
-            return i * 64 + (((i >> LOG_S) & 7) << 3);
+            return (i ^ ((i >> 2) & 1)) * 64 + (((i >> 3) & 3) << 4);
+        else if constexpr (S == 4)
+            return (i ^ ((i >> 2) & 3)) * 32 + (((i >> 4) & 1) << 4);
         else
-            return (i >> 1) * 64 + (((((i & 1) << 2) ^ (i >> LOG_S)) & 7) << 3);
+            return (i ^ ((i >> 2) & 3)) * 32 + (((i >> 3) & 1) << 4);
     }
     __device__ static __forceinline__ int at(int b, int c)
     {
@@ -160,9 +168,14 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
     static_assert(T > 0 && C % 32 == 0, "shape");
 
     // ---- weights: resident copies (RES) or streaming buffers
-    constexpr int LDT = KT + 8, LD7 = K7 + 8, LD1 = C + 8;  // resident pitches
-    constexpr int KC = 64;                                  // streamed residual-unit chunk
-    constexpr int LDC = KC + 8, LDCT = 32 + 8;              // streamed pitches
+    // weight rows are read 16 at a time (A operand rows) at two neighbouring
+    // chunks per cycle: resident ConvT / conv7 rows padded to a stride of 2
+    // mod 16 slots; 64- and 128-byte rows unpadded with their chunks permuted
+    // by row (x64 / x128 below)
+    static_assert(!RES || C == 32, "resident weights: 32 channels");
+    constexpr int LDT = KT + 16, LD7 = K7 + 48, LD1 = C;  // resident pitches
+    constexpr int KC = 64;                                // streamed residual-unit chunk
+    constexpr int LDC = KC, LDCT = 32;                    // streamed pitches
     constexpr int N7C = K7 / KC;                            // conv7 chunks per unit
     constexpr int NCH = NKT + 2 * (N7C + 1);                // chunks per tile (streamed)
     static_assert(RES || (K7 % KC == 0 && C == KC), "streamed shapes");
@@ -205,18 +218,20 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
     half_t *const w7s = wsm + NT * LDT;
     half_t *const w1s = w7s + 2 * C * LD7;
     if constexpr (RES) {
-        auto copy = [&](half_t *dst, int ld, const half_t *src, int rows, int cols, bool k7) {
+        // kind 0: plain rows, 1: conv7 rows (w7_row order), 2: 64-byte rows (x64)
+        auto copy = [&](half_t *dst, int ld, const half_t *src, int rows, int cols, int kind) {
             const int cpr = cols / 8;
             for (int i = tid; i < rows * cpr; i += NTH) {
                 const int r = i / cpr, c8 = (i - r * cpr) * 8;
-                *(h8 *)(dst + (k7 ? w7_row(r) : r) * ld + c8) =
-                    *(const h8 *)(src + (long)r * cols + c8);
+                const int o = kind == 1 ? w7_row(r) * ld + c8
+                                        : r * ld + (kind == 2 ? c8 ^ x64(r) : c8);
+                *(h8 *)(dst + o) = *(const h8 *)(src + (long)r * cols + c8);
             }
         };
-        copy(wTs, LDT, p.WT, NT, KT, false);
+        copy(wTs, LDT, p.WT, NT, KT, 0);
         for (int j = 0; j < 2; j++) {
-            copy(w7s + j * C * LD7, LD7, p.W7[j], C, K7, true);
-            copy(w1s + j * C * LD1, LD1, p.W1[j], C, C, false);
+            copy(w7s + j * C * LD7, LD7, p.W7[j], C, K7, 1);
+            copy(w1s + j * C * LD1, LD1, p.W1[j], C, C, 2);
         }
     }
 
@@ -275,7 +290,9 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
             const int k = tid + i * NTH;
             if (k < n) {
                 const int row = k / ppr, c8 = (k - row * ppr) * 8;
-                *(Chunk *)(dst + (k7 ? w7_row(row) : row) * ldd + c8) = r[i];
+                const int o = k7 ? w7_row(row) * ldd + (c8 ^ x128(w7_row(row)))
+                                 : row * ldd + (width == 32 ? c8 ^ x64(row) : c8 ^ x128(row));
+                *(Chunk *)(dst + o) = r[i];
             }
         }
     };
@@ -353,7 +370,8 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
                 for (int r = 0; r < S; r++)
 #pragma unroll
                     for (int n = 0; n < NB; n++) {
-                        const h8 wf = *(const h8 *)(wp + (r * C + n * 16 + l16) * wld + lg * 8);
+                        const h8 wf = *(const h8 *)(wp + (r * C + n * 16 + l16) * wld +
+                                                    (RES ? lg * 8 : (lg * 8) ^ x64(l16)));
                         x[r][n] = mma(wf, xf[ks], x[r][n]);
                     }
                 if (!RES && ks + 1 < NKT)
@@ -419,12 +437,12 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
             // block n, A row l16 computes output channel ch7(n, l16) (LDS row
             // 16 n + l16); rb: each
             // unit's input row base for this step's tap
-            auto step7 = [&](int k0, const half_t *wp, int wld, const int (&rb)[S]) {
+            auto step7 = [&](int k0, const half_t *wp, int wld, int wk, const int (&rb)[S]) {
                 const int c0 = k0 % C;
                 h8 wf[NB];
 #pragma unroll
                 for (int n = 0; n < NB; n++)
-                    wf[n] = *(const h8 *)(wp + (16 * n + l16) * wld + lg * 8);
+                    wf[n] = *(const h8 *)(wp + (16 * n + l16) * wld + wk);
 #pragma unroll
                 for (int r = 0; r < S; r++) {
                     const h8 xf = *(const h8 *)(in + L::at(rb[r], c0 + lg * 8));
@@ -445,7 +463,7 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
                     tap_bases(tap, rb);
 #pragma unroll
                     for (int c0 = 0; c0 < C; c0 += 32)
-                        step7(tap * C + c0, w7s + u * C * LD7 + tap * C + c0, LD7, rb);
+                        step7(tap * C + c0, w7s + u * C * LD7 + tap * C + c0, LD7, lg * 8, rb);
                 }
             } else {
 #pragma unroll 1
@@ -455,7 +473,7 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
                     tap_bases(j7 * KC / C, rb);  // a chunk holds one tap (KC == C)
 #pragma unroll
                     for (int kin = 0; kin < KC; kin += 32)
-                        step7(j7 * KC + kin, wb + kin, LDC, rb);
+                        step7(j7 * KC + kin, wb, LDC, (kin + lg * 8) ^ x128(l16), rb);
                     advance();
                 }
             }
@@ -504,7 +522,8 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
 #pragma unroll
                     for (int n = 0; n < NB; n++) {
                         const h8 wf =
-                            *(const h8 *)(w1p + (n * 16 + l16) * w1ld + kk * 32 + lg * 8);
+                            *(const h8 *)(w1p + (n * 16 + l16) * w1ld +
+                                          ((kk * 32 + lg * 8) ^ (RES ? x64(l16) : x128(l16))));
                         y[n] = mma(wf, hb[kk], y[n]);
                     }
                 }
