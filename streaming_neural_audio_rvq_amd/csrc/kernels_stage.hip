@@ -88,44 +88,34 @@ __device__ __forceinline__ h4 snake4(f4 v, f4 ar, f4 ai)
               snrvq_f16(snrvq_snake(v[3], ar[3], ai[3]))};
 }
 
-// fp16 activation rows in LDS.  A 16-byte fragment read is served 16 lanes
-// per cycle: lanes 8k..8k+7 with lanes 8k+16..8k+23, i.e. 8 rows at two
-// neighbouring 16-byte chunks, over 64 four-byte banks; so the 16 reads of a
-// cycle must fall on 16 distinct 16-byte slots of a 256-byte line.  The MFMA
-// operand reads rows S apart (one row of each unit).  Odd S: rows padded to
-// C + 16 elements (a row stride of 3 x 10 slots walks all even slots).  Even
-// S: unpadded rows, row i stored at row position i ^ f(i) (low row bits
-// permuted by higher ones, so the rows of one read land on every row position
-// of the 256-byte line) with its 16-byte chunks permuted by g(i) (separating
-// the rows that still share a position).  off(i, c): element offset of
-// channel c (a multiple of 4) of tile row i >= 0.
-template <int C, int S>
-struct Rows {
-    static constexpr bool PAD = S % 2 == 1;
-    static_assert(PAD || (C == 32 && (S == 2 || S == 4)) || (C == 64 && S == 4), "layout");
+// fp16 activation rows in LDS, phase-major: row i of a buffer sits in plane
+// i mod S at plane row i / S (+1: one spare row in front of every plane), rows
+// padded to C + 16 elements.  The MFMA operand of a unit reads rows S apart,
+// i.e. consecutive rows of one plane, and a k = 7 tap shifts them by a
+// constant: so every operand address is a per-lane base plus a compile-time
+// offset.  A 16-byte fragment read is served 16 lanes per cycle (lanes
+// 8k..8k+7 with 8k+16..8k+23: 8 rows at two neighbouring 16-byte chunks) over
+// 64 four-byte banks; a row stride of 6 (C = 32) or 10 (C = 64) 16-byte slots
+// puts those 16 reads on distinct slots of a 256-byte line.
+template <int C, int S, int NROWS>
+struct Planes {
     static_assert(C == 32 || C == 64, "channels");
-    static constexpr int elems(int n) { return PAD ? n * (C + 16) : ((n + 3) / 4) * 4 * C; }
-    // off(i, c) == at(base(i), c): the row part once, then one add (padded)
-    // or one xor (permuted: c < C only touches the chunk bits g permutes)
-    __device__ static __forceinline__ int base(int i)
+    static constexpr int P = C + 16;                      // row pitch, elements
+    static constexpr int QR = (NROWS + S - 1) / S + 1;    // rows per plane
+    static constexpr int PLANE = QR * P;
+    static constexpr int ELEMS = S * PLANE;
+    // element offset of channel c of row i >= 0
+    __device__ static __forceinline__ int off(int i, int c)
     {
-        if constexpr (PAD)
-            return i * (C + 16);
-        else if constexpr (C == 64)
-            return (i ^ ((i >> 2) & 1)) * 64 + (((i >> 3) & 3) << 4);
-        else if constexpr (S == 4)
-            return (i ^ ((i >> 2) & 3)) * 32 + (((i >> 4) & 1) << 4);
-        else
-            return (i ^ ((i >> 2) & 3)) * 32 + (((i >> 3) & 1) << 4);
+        return (i % S) * PLANE + (i / S + 1) * P + c;
     }
-    __device__ static __forceinline__ int at(int b, int c)
+    // lane base of plane row q (rows S q + k are at base(q) + rel(k))
+    __device__ static __forceinline__ int base(int q) { return (q + 1) * P; }
+    // offset of row S q + k from base(q); k may be negative (down to -S q - S)
+    __device__ static constexpr int rel(int k)
     {
-        if constexpr (PAD)
-            return b + c;
-        else
-            return b ^ c;
+        return (((k % S) + S) % S) * PLANE + ((k - (((k % S) + S) % S)) / S) * P;
     }
-    __device__ static __forceinline__ int off(int i, int c) { return at(base(i), c); }
 };
 
 // Per-channel parameter rows in LDS ([P_COUNT][C] fp32).
@@ -143,8 +133,12 @@ struct StageShape {
     static constexpr int HQ = (24 + E + S - 1) / S;  // input rows of recomputed halo
     static constexpr int HX = HQ * S;                // output rows of recomputed halo
     static constexpr int T = S * (16 * NW - HQ);     // output rows per tile
-    static constexpr int NA1 = T + HX;               // a1 rows: [t0 - HX, t0 + T)
-    static constexpr int NA2 = T + 18 + E;           // a2 rows: [t0 - 18 - E, t0 + T)
+    static constexpr int O2 = (18 + E + S - 1) / S * S;  // a2 rows before t0 (a multiple of S)
+    static constexpr int OO = (6 + S - 1) / S * S;       // final conv input rows before t0
+    static constexpr int NA1 = T + HX;                   // a1 rows: [t0 - HX, t0 + T)
+    static constexpr int NA2 = T + O2;                   // a2 rows: [t0 - O2, t0 + T)
+    static constexpr int NAO = FINAL ? T + OO : 0;       // a_out rows: [t0 - OO, t0 + T)
+    static constexpr int NROWS = NA1 > NA2 ? (NA1 > NAO ? NA1 : NAO) : (NA2 > NAO ? NA2 : NAO);
 };
 
 // Work-groups per CU: two for the streamed shapes of at most 4 waves (their
@@ -160,9 +154,9 @@ template <int C, int S, int NW, bool FINAL, bool RES>
 __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_kernel(StageArgs p)
 {
     using SH = StageShape<C, S, NW, FINAL>;
-    using L = Rows<C, S>;
+    using L = Planes<C, S, StageShape<C, S, NW, FINAL>::NROWS>;
     constexpr int NTH = NW * 64;
-    constexpr int E = SH::E, HQ = SH::HQ, HX = SH::HX, T = SH::T;
+    constexpr int E = SH::E, HQ = SH::HQ, HX = SH::HX, T = SH::T, O2 = SH::O2, OO = SH::OO;
     constexpr int CIN = 2 * C, NT = S * C, KT = 2 * CIN, NB = C / 16, NKT = KT / 32;
     constexpr int K7 = 7 * C;
     static_assert(T > 0 && C % 32 == 0, "shape");
@@ -188,8 +182,7 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
     // unit's conv7 is done), then a_out (FINAL; a2 is dead once the second
     // unit's conv7 is done).  Streamed weights (ConvT chunks included)
     // alternate between two buffers.
-    constexpr int ACT_ELEMS = L::elems(SH::NA1) > L::elems(SH::NA2) ? L::elems(SH::NA1)
-                                                                    : L::elems(SH::NA2);
+    constexpr int ACT_ELEMS = L::ELEMS;
     constexpr int W_ELEMS = RES ? RES_ELEMS : 2 * W_BUF;
 
     __shared__ __attribute__((aligned(16))) half_t acts[ACT_ELEMS];
@@ -337,8 +330,8 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
         const int tend = t0 + T < rows_b ? t0 + T : rows_b;  // rows [t0, tend)
         const bool first = t0 == 0, last = tend == rows_b;
         half_t *slot_state = p.state + (long)p.slot[b] * p.slot_elems;
-        const int r1 = t0 - HX;      // stream row of a1s row 0
-        const int r2 = t0 - 18 - E;  // stream row of a2s row 0
+        const int r1 = t0 - HX;  // stream row of a1 row 0
+        const int r2 = t0 - O2;  // stream row of a2 row 0 (r1, r2: multiples of S)
 
         // ---- phase 1: transposed conv of this wave's 16 input rows
         const int q0 = t0 / S;
@@ -378,15 +371,15 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
                     advance();
             }
             // epilogue: + bias -> x; Snake -> a1
+            const int b1 = L::base(q - r1 / S) + lg * 4;  // a1 rows S q + r
 #pragma unroll
             for (int r = 0; r < S; r++) {
-                const int bi = L::base(q * S + r - r1);
 #pragma unroll
                 for (int n = 0; n < NB; n++) {
                     const int c = n * 16 + lg * 4;
                     x[r][n] = x[r][n] + *(const f4 *)(prm + P_BT * C + c);
                     if (qok)
-                        *(h4 *)(a1s + L::at(bi, c)) =
+                        *(h4 *)(a1s + b1 + L::rel(r) + n * 16) =
                             snake4(x[r][n], *(const f4 *)(prm + P_A1R0 * C + c),
                                    *(const f4 *)(prm + P_A1I0 * C + c));
                 }
@@ -417,63 +410,64 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
                     *(h8 *)(d + r * C + c8) = *(const h8 *)(in + L::off(tend - nr - rin + r, c8));
                 }
             }
-            int rowi[S];  // tile row of each unit's lane row in the input (clamped into range)
-            bool rok[S];
+            bool rok[S];  // unit r's row of this lane is computed and kept
 #pragma unroll
             for (int r = 0; r < S; r++) {
-                int t = q * S + r;
+                const int t = q * S + r;
                 rok[r] = qok && t >= rlo && t < tend;
-                t = t < rlo ? rlo : t;
-                t = t < tend ? t : tend - 1;
-                rowi[r] = t - rin;
             }
+            // lane base of the input rows S qi + r.  Lanes with a kept row
+            // have qi >= 6 D / S; the others are clamped there, so every row
+            // they read lies at most one row before a plane, on its spare row.
+            int qi = q - rin / S;
+            qi = qi < 6 * D / S ? 6 * D / S : qi;
+            const int bin = L::base(qi) + lg * 8;
             f4 acc[S][NB];
 #pragma unroll
             for (int r = 0; r < S; r++)
 #pragma unroll
                 for (int n = 0; n < NB; n++)
                     acc[r][n] = f4{0.f, 0.f, 0.f, 0.f};
-            // one K step of 32 of the conv7 (dilation D) from weights wp (row pitch wld);
-            // block n, A row l16 computes output channel ch7(n, l16) (LDS row
-            // 16 n + l16); rb: each
-            // unit's input row base for this step's tap
-            auto step7 = [&](int k0, const half_t *wp, int wld, int wk, const int (&rb)[S]) {
-                const int c0 = k0 % C;
+            // one K step of 32 of the conv7 (dilation D) from weights wp (row
+            // pitch wld, lane element wk); block n, A row l16 computes output
+            // channel ch7(n, l16) (LDS row 16 n + l16); ro: offset of each
+            // unit's input row for this step's tap from the lane base
+            auto step7 = [&](int c0, const half_t *wp, int wld, int wk, const int (&ro)[S]) {
                 h8 wf[NB];
 #pragma unroll
                 for (int n = 0; n < NB; n++)
                     wf[n] = *(const h8 *)(wp + (16 * n + l16) * wld + wk);
 #pragma unroll
                 for (int r = 0; r < S; r++) {
-                    const h8 xf = *(const h8 *)(in + L::at(rb[r], c0 + lg * 8));
+                    const h8 xf = *(const h8 *)(in + bin + ro[r] + c0);
 #pragma unroll
                     for (int n = 0; n < NB; n++)
                         acc[r][n] = mma(wf[n], xf, acc[r][n]);
                 }
             };
-            auto tap_bases = [&](int tap, int (&rb)[S]) {
+            auto tap_offsets = [&](int tap, int (&ro)[S]) {
 #pragma unroll
                 for (int r = 0; r < S; r++)
-                    rb[r] = L::base(rowi[r] + (tap - 6) * D);
+                    ro[r] = L::rel(r + (tap - 6) * D);
             };
             if constexpr (RES) {
 #pragma unroll
                 for (int tap = 0; tap < 7; tap++) {
-                    int rb[S];
-                    tap_bases(tap, rb);
+                    int ro[S];
+                    tap_offsets(tap, ro);
 #pragma unroll
                     for (int c0 = 0; c0 < C; c0 += 32)
-                        step7(tap * C + c0, w7s + u * C * LD7 + tap * C + c0, LD7, lg * 8, rb);
+                        step7(c0, w7s + u * C * LD7 + tap * C + c0, LD7, lg * 8, ro);
                 }
             } else {
 #pragma unroll 1
                 for (int j7 = 0; j7 < N7C; j7++) {
                     const half_t *wb = wsm + ((NKT + u * (N7C + 1) + j7) & 1) * W_BUF;
-                    int rb[S];
-                    tap_bases(j7 * KC / C, rb);  // a chunk holds one tap (KC == C)
+                    int ro[S];
+                    tap_offsets(j7 * KC / C, ro);  // a chunk holds one tap (KC == C)
 #pragma unroll
                     for (int kin = 0; kin < KC; kin += 32)
-                        step7(j7 * KC + kin, wb, LDC, (kin + lg * 8) ^ x128(l16), rb);
+                        step7(kin, wb, LDC, (kin + lg * 8) ^ x128(l16), ro);
                     advance();
                 }
             }
@@ -486,7 +480,7 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
             if (first && (u == 0 || FINAL)) {
                 const half_t *sx = u == 0 ? p.a2_ext + ((long)b * 18 + (long)cu0 * p.r_out) * C
                                           : p.ao_ext + ((long)b * 6 + (long)cu0 * p.r_out) * C;
-                const int nr = u == 0 ? 18 : 6, r0 = u == 0 ? E : 0;
+                const int nr = u == 0 ? 18 : 6, r0 = u == 0 ? O2 - 18 : OO - 6;
                 for (int k = tid; k < nr * C / 8; k += NTH) {
                     const int r = k / (C / 8), c8 = (k - r * (C / 8)) * 8;
                     *(h8 *)(acts + L::off(r0 + r, c8)) = *(const h8 *)(sx + r * C + c8);
@@ -528,7 +522,9 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
                     }
                 }
                 const int t = q * S + r;
-                const int bo = L::base(u == 0 ? t - r2 : t - (t0 - 6));  // a2 / a_out row
+                // a2 row t - r2 / a_out row t - (t0 - OO): plane row q - r2 / S
+                // or q - (t0 - OO) / S, plane r
+                const int bo = L::base(q - (u == 0 ? r2 : t0 - OO) / S) + L::rel(r) + lg * 4;
 #pragma unroll
                 for (int n = 0; n < NB; n++) {
                     const int c = n * 16 + lg * 4;
@@ -536,14 +532,14 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
                     if (!rok[r])
                         continue;
                     if (u == 0) {
-                        *(h4 *)(a2s + L::at(bo, c)) =
+                        *(h4 *)(a2s + bo + n * 16) =
                             snake4(x[r][n], *(const f4 *)(prm + P_A1R1 * C + c),
                                    *(const f4 *)(prm + P_A1I1 * C + c));
                     } else {
                         const h4 o = snake4(x[r][n], *(const f4 *)(prm + P_ANR * C + c),
                                             *(const f4 *)(prm + P_ANI * C + c));
                         if (FINAL)
-                            *(h4 *)(a1s + L::at(bo, c)) = o;
+                            *(h4 *)(a1s + bo + n * 16) = o;
                         else
                             *(h4 *)(p.next + ((long)(b + 1) + (long)cu0 * p.r_out + t) * C +
                                     c) = o;
@@ -559,33 +555,41 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
                 for (int k = tid; k < 6 * C / 8; k += NTH) {
                     const int r = k / (C / 8), c8 = (k - r * (C / 8)) * 8;
                     *(h8 *)(d + r * C + c8) =
-                        *(const h8 *)(a1s + L::off(tend - 6 - (t0 - 6) + r, c8));
+                        *(const h8 *)(a1s + L::off(tend - 6 - (t0 - OO) + r, c8));
                 }
             }
-            // ---- phase 4: final conv on the matrix cores, 16 samples per
-            // block: A row 0 holds the weights of one (tap, 32 channels) K
-            // step, the other rows zeros; K steps tap-major (the per-layer
-            // final conv's sequence)
+            // ---- phase 4: final conv on the matrix cores.  A block is 16
+            // samples of one phase ph, S apart: tt = S (16 qb + l16) + ph, so
+            // its tap-j rows are consecutive rows of one plane.  A row 0 holds
+            // the weights of one (tap, 32 channels) K step, the other rows
+            // zeros; K steps tap-major (the per-layer final conv's sequence).
             const int nsamp = tend - t0;
             const h8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
-            for (int blk = wave; blk * 16 < nsamp; blk += NW) {
-                int tt = blk * 16 + l16;
-                const bool ok = tt < nsamp;
-                tt = ok ? tt : nsamp - 1;
-                f4 acc = {0.f, 0.f, 0.f, 0.f};
+            const int nqb = (nsamp + 16 * S - 1) / (16 * S);  // blocks per phase
 #pragma unroll
-                for (int j = 0; j < 7; j++) {
-                    const int bj = L::base(tt + j);
+            for (int ph = 0; ph < S; ph++) {
+                for (int qb = wave; qb < nqb; qb += NW) {
+                    int qq = 16 * qb + l16;
+                    const bool ok = S * qq + ph < nsamp;
+                    qq = ok ? qq : (nsamp - 1 - ph) / S;  // nsamp > ph when any lane is ok
+                    const int bq = L::base(qq) + lg * 8;
+                    f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int k0 = 0; k0 < C; k0 += 32) {
-                        const h8 wf = *(const h8 *)((const half_t *)wout_s + j * C + k0 + lg * 8);
-                        acc = mma(l16 == 0 ? wf : zero,
-                                  *(const h8 *)(a1s + L::at(bj, k0 + lg * 8)), acc);
+                    for (int j = 0; j < 7; j++) {
+                        // a_out row of sample tt, tap j: tt + j + OO - 6
+                        const int ro = L::rel(ph + j + OO - 6);
+#pragma unroll
+                        for (int k0 = 0; k0 < C; k0 += 32) {
+                            const h8 wf =
+                                *(const h8 *)((const half_t *)wout_s + j * C + k0 + lg * 8);
+                            acc = mma(l16 == 0 ? wf : zero, *(const h8 *)(a1s + bq + ro + k0), acc);
+                        }
                     }
-                }
-                if (lg == 0 && ok) {
-                    const float yv = p.b_out + acc[0];
-                    p.pcm[(long)cu0 * p.r_out + t0 + tt] = p.final_tanh ? tanhf(yv) : yv;
+                    if (lg == 0 && ok) {
+                        const float yv = p.b_out + acc[0];
+                        p.pcm[(long)cu0 * p.r_out + t0 + S * qq + ph] =
+                            p.final_tanh ? tanhf(yv) : yv;
+                    }
                 }
             }
             __syncthreads();  // a_out is read before the next tile writes a1
