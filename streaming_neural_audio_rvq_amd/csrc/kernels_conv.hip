@@ -9,7 +9,8 @@
 //     conv with N = s C_out whose output, in channels-last layout, is the
 //     plain row-major [q][s C_out] matrix;
 //   * 1x1 convs and linear layers (k = 1).
-// The epilogue adds the bias, optionally adds an fp32 residual and stores it
+// The accumulators start at the bias; the epilogue optionally adds an fp32
+// residual and stores it
 // (the residual stream), and stores the next layer's MFMA operand with the
 // next activation (Snake / ELU / GELU) applied, into that layer's extended
 // buffer.  So every activation is computed once per element, and every conv
@@ -331,21 +332,42 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
             __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
     };
 
-    f4 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++)
-            acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
-
     const int wm = wave / WN, wn = wave % WN;
     const int rbase = wm * TM, cbase = wn * TN;
     const int lrow = lane & 15, lk = lane >> 4;
+    const bool split = p.splits > 1;
+
+    // accumulators start at the bias (of the k = 7 conv in a residual-unit
+    // launch): the first MFMA of the K loop takes it as its C operand.
+    // Split-K partials start at zero and the reduce adds the bias.
+    // (loaded after the first stage's loads are issued, all four together)
+    f4 binit[FN];
+    auto load_bias = [&]() {
+        if (split) {
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+                binit[j] = f4{0.f, 0.f, 0.f, 0.f};
+        } else {
+#pragma unroll
+            for (int j = 0; j < FN; j++) {
+                const int ch = (n0 + cbase + j * 16 + lk * 4) % p.Cout;
+                binit[j] = *(const f4 *)((RU ? p.bias7 : p.bias) + ch);
+            }
+        }
+    };
+    f4 acc[FM][FN];
 
     const int fsw = swz(lrow);  // fragment rows are lrow + multiples of 16
-    auto mma_stage = [&](const T *Ab, const T *Bb) {
+    auto mma_stage = [&](const T *Ab, const T *Bb, auto first) {
 #pragma unroll
         for (int sub = 0; sub < KSUB; sub++) {
+            // C operand: the bias for the first MFMA of each output
+            auto cin = [&](int i, int j) {
+                if constexpr (decltype(first)::value)
+                    return sub == 0 ? binit[j] : acc[i][j];
+                else
+                    return acc[i][j];
+            };
             if constexpr (sizeof(T) == 2) {
                 h8 af[FM], bf[FN];
 #pragma unroll
@@ -362,7 +384,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
 #pragma unroll
                     for (int j = 0; j < FN; j++)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[j], af[i],
-                                                                           acc[i][j], 0, 0, 0);
+                                                                           cin(i, j), 0, 0, 0);
             } else {
                 f4 af[FM], bf[FN];
 #pragma unroll
@@ -378,7 +400,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
 #pragma unroll
                         for (int j = 0; j < FN; j++)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                bf[j][kk], af[i][kk], acc[i][j], 0, 0, 0);
+                                bf[j][kk], af[i][kk], kk == 0 ? cin(i, j) : acc[i][j], 0, 0, 0);
             }
         }
         __builtin_amdgcn_s_setprio(0);
@@ -388,15 +410,32 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
         gload(ks0, A0, B0);
         sstore(A0, B0);
     }
+    load_bias();
     loads_done();
     __syncthreads();
-    for (int ks = ks0; ks < ks1; ks++) {
+    // first K stage (buffer 0) peeled: its MFMAs start from the bias
+    if (ks0 < ks1) {
+        if (ks0 + 1 < ks1)
+            gload(ks0 + 1, A1, B1);
+        mma_stage(A0, B0, std::true_type());
+        if (ks0 + 1 < ks1)
+            sstore(A1, B1);
+        loads_done();
+        __syncthreads();
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+                acc[i][j] = binit[j];
+    }
+    for (int ks = ks0 + 1; ks < ks1; ks++) {
         const int buf = (ks - ks0) & 1;
         T *const Ac = buf ? A1 : A0, *const Bc = buf ? B1 : B0;
         T *const An = buf ? A0 : A1, *const Bn = buf ? B0 : B1;
         if (ks + 1 < ks1)
             gload(ks + 1, An, Bn);
-        mma_stage(Ac, Bc);
+        mma_stage(Ac, Bc, std::false_type());
         if (ks + 1 < ks1)
             sstore(An, Bn);
         loads_done();
@@ -437,7 +476,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
 #pragma unroll
             for (int j = 0; j < FN; j++) {
                 const int ch = cbase + j * 16 + lk * 4;  // one N tile: n0 == 0
-                const f4 b7 = *(const f4 *)(p.bias7 + ch);
+                const f4 b1 = *(const f4 *)(p.bias + ch);
                 f4 a7 = f4{0.f, 0.f, 0.f, 0.f}, ia7 = a7;
                 if constexpr (decltype(act)::value == ACT_SNAKE) {
                     a7 = *(const f4 *)(p.alpha7 + ch);
@@ -445,9 +484,9 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
                 }
 #pragma unroll
                 for (int i = 0; i < FM; i++) {
-                    const f4 y = act4t<decltype(act)::value>(acc[i][j] + b7, a7, ia7);
+                    const f4 y = act4t<decltype(act)::value>(acc[i][j], a7, ia7);
                     store4<half_t>(hS + (rbase + i * 16 + lrow) * HP + ch, y);
-                    acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+                    acc[i][j] = b1;  // the 1x1 conv starts at its bias
                 }
             }
         });
@@ -482,14 +521,12 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
 
     // ---- epilogue straight from the accumulators: weights are the MFMA's A
     // operand, so acc[i][j] holds 4 consecutive output columns of one row
-    const bool split = p.splits > 1;
-    f4 bias4[FN], al4[FN], ial4[FN];
+    f4 al4[FN], ial4[FN];
     int nj[FN], chj[FN];
 #pragma unroll
     for (int j = 0; j < FN; j++) {
         nj[j] = n0 + cbase + j * 16 + lk * 4;
         chj[j] = nj[j] % p.Cout;
-        bias4[j] = split ? f4{0.f, 0.f, 0.f, 0.f} : *(const f4 *)(p.bias + chj[j]);
         snake_params(p, chj[j], al4[j], ial4[j]);
     }
     if (split) {
@@ -514,7 +551,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
             f4 v[FN];
 #pragma unroll
             for (int j = 0; j < FN; j++)
-                v[j] = acc[i][j] + bias4[j];
+                v[j] = acc[i][j];  // bias included
             if (p.res) {
                 f4 rr[FN];
 #pragma unroll

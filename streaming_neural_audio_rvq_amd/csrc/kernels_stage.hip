@@ -14,8 +14,9 @@
 //
 // Arithmetic is the per-layer path's, operation for operation: the same fp16
 // operands (each activation applied once, then rounded), the same K order
-// (tap-major, channel-minor in steps of 32) on v_mfma_f32_16x16x32_f16, the
-// same fp32 epilogues, so both paths give bit-identical PCM.
+// (tap-major, channel-minor in steps of 32) on v_mfma_f32_16x16x32_f16 with
+// the accumulators starting at the bias, the same fp32 epilogues, so both
+// paths give bit-identical PCM.
 //
 // Work split.  The transposed conv maps input row q to output rows q S + r,
 // r < S.  Wave w of a work-group owns q-block w of the tile (16 input rows)
@@ -351,10 +352,12 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
                 xf[ks] = *(const h8 *)((tap ? x1 : x0) + c0);
             }
 #pragma unroll
-            for (int r = 0; r < S; r++)
+            for (int n = 0; n < NB; n++) {
+                const f4 bt = *(const f4 *)(prm + P_BT * C + n * 16 + lg * 4);
 #pragma unroll
-                for (int n = 0; n < NB; n++)
-                    x[r][n] = f4{0.f, 0.f, 0.f, 0.f};
+                for (int r = 0; r < S; r++)
+                    x[r][n] = bt;  // accumulators start at the bias
+            }
 #pragma unroll
             for (int ks = 0; ks < NKT; ks++) {
                 const half_t *wp = RES ? wTs + ks * 32 : wsm + (ks & 1) * W_BUF;
@@ -377,7 +380,6 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
 #pragma unroll
                 for (int n = 0; n < NB; n++) {
                     const int c = n * 16 + lg * 4;
-                    x[r][n] = x[r][n] + *(const f4 *)(prm + P_BT * C + c);
                     if (qok)
                         *(h4 *)(a1s + b1 + L::rel(r) + n * 16) =
                             snake4(x[r][n], *(const f4 *)(prm + P_A1R0 * C + c),
@@ -422,12 +424,16 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
             int qi = q - rin / S;
             qi = qi < 6 * D / S ? 6 * D / S : qi;
             const int bin = L::base(qi) + lg * 8;
+            const int PB7 = u ? P_B71 : P_B70, PA2R = u ? P_A2R1 : P_A2R0,
+                      PA2I = u ? P_A2I1 : P_A2I0, PB1 = u ? P_B11 : P_B10;
             f4 acc[S][NB];
 #pragma unroll
-            for (int r = 0; r < S; r++)
+            for (int n = 0; n < NB; n++) {
+                const f4 b7 = *(const f4 *)(prm + PB7 * C + ch7(n, 4 * lg));
 #pragma unroll
-                for (int n = 0; n < NB; n++)
-                    acc[r][n] = f4{0.f, 0.f, 0.f, 0.f};
+                for (int r = 0; r < S; r++)
+                    acc[r][n] = b7;  // accumulators start at the bias
+            }
             // one K step of 32 of the conv7 (dilation D) from weights wp (row
             // pitch wld, lane element wk); block n, A row l16 computes output
             // channel ch7(n, l16) (LDS row 16 n + l16); ro: offset of each
@@ -492,16 +498,13 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
             const half_t *w1p = RES ? w1s + u * C * LD1
                                     : wsm + ((NKT + u * (N7C + 1) + N7C) & 1) * W_BUF;
             const int w1ld = RES ? LD1 : LDC;
-            const int PB7 = u ? P_B71 : P_B70, PA2R = u ? P_A2R1 : P_A2R0,
-                      PA2I = u ? P_A2I1 : P_A2I0, PB1 = u ? P_B11 : P_B10;
 #pragma unroll
             for (int r = 0; r < S; r++) {
                 h8 hb[NB / 2];
 #pragma unroll
                 for (int n = 0; n < NB; n++) {
                     const int c = ch7(n, 4 * lg);
-                    const h4 hv = snake4(acc[r][n] + *(const f4 *)(prm + PB7 * C + c),
-                                         *(const f4 *)(prm + PA2R * C + c),
+                    const h4 hv = snake4(acc[r][n], *(const f4 *)(prm + PA2R * C + c),
                                          *(const f4 *)(prm + PA2I * C + c));
 #pragma unroll
                     for (int e = 0; e < 4; e++)
@@ -510,7 +513,7 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
                 f4 y[NB];
 #pragma unroll
                 for (int n = 0; n < NB; n++)
-                    y[n] = f4{0.f, 0.f, 0.f, 0.f};
+                    y[n] = *(const f4 *)(prm + PB1 * C + n * 16 + lg * 4);  // starts at the bias
 #pragma unroll
                 for (int kk = 0; kk < NB / 2; kk++) {
 #pragma unroll
@@ -528,7 +531,7 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
 #pragma unroll
                 for (int n = 0; n < NB; n++) {
                     const int c = n * 16 + lg * 4;
-                    x[r][n] = (y[n] + *(const f4 *)(prm + PB1 * C + c)) + x[r][n];
+                    x[r][n] = y[n] + x[r][n];
                     if (!rok[r])
                         continue;
                     if (u == 0) {
