@@ -80,6 +80,8 @@ __device__ __forceinline__ int w7_row(int c)
 // 128 bytes (64 halves): element k of row r sits at k ^ x(r).
 __device__ __forceinline__ int x64(int r) { return ((r >> 2) & 1) << 4; }
 __device__ __forceinline__ int x128(int r) { return ((r >> 1) & 3) << 4; }
+// and of 256-byte rows (128 halves)
+__device__ __forceinline__ int x256(int r) { return (r & 7) << 4; }
 
 __device__ __forceinline__ h4 snake4(f4 v, f4 ar, f4 ai)
 {
@@ -169,14 +171,21 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
     // by row (x64 / x128 below)
     static_assert(!RES || C == 32, "resident weights: 32 channels");
     constexpr int LDT = KT + 16, LD7 = K7 + 48, LD1 = C;  // resident pitches
-    constexpr int KC = 64;                                // streamed residual-unit chunk
-    constexpr int LDC = KC, LDCT = 32;                    // streamed pitches
-    constexpr int N7C = K7 / KC;                            // conv7 chunks per unit
-    constexpr int NCH = NKT + 2 * (N7C + 1);                // chunks per tile (streamed)
-    static_assert(RES || (K7 % KC == 0 && C == KC), "streamed shapes");
+    // streamed (64 channels): ConvT chunks of CTW K columns (64 when two
+    // buffers of it fit beside the activations, else 32); per residual unit
+    // chunks of TPC conv7 taps (two where the registers allow: fewer
+    // barriers), the last one tap 6 with the 1x1 weights
+    static_assert(RES || C == 64, "streamed weights: 64 channels");
+    constexpr int CTW = NT * 64 <= 12288 ? 64 : 32;
+    constexpr int TPC = S == 3 ? 2 : 1;
+    constexpr int NCT = KT / CTW;         // ConvT chunks
+    constexpr int NRC = 6 / TPC + 1;      // chunks per residual unit
+    constexpr int NCH = NCT + 2 * NRC;    // chunks per tile (streamed)
+    // chunk permutation of the rows of a conv7 chunk (TPC C columns)
+    auto xtap = [](int r) { return TPC == 2 ? x256(r) : x128(r); };
     constexpr int RES_ELEMS = NT * LDT + 2 * C * LD7 + 2 * C * LD1;
-    constexpr int RU_BUF = C * LDC;    // one residual-unit chunk
-    constexpr int CT_BUF = NT * LDCT;  // one ConvT chunk
+    constexpr int RU_BUF = C * 2 * C;  // one residual-unit chunk
+    constexpr int CT_BUF = NT * CTW;   // one ConvT chunk
     constexpr int W_BUF = RU_BUF > CT_BUF ? RU_BUF : CT_BUF;
 
     // One activation buffer holds a1, then a2 (a1 is dead once the first
@@ -230,63 +239,72 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
     }
 
     // ---- streamed weights: chunk j of the per-tile sequence
-    //   [0, NKT): ConvT K step j (32 wide, NT rows)
-    //   then per residual unit u: N7C conv7 chunks (KC wide), one conv1 chunk
+    //   [0, NCT): ConvT K columns [CTW j, CTW (j + 1)) (NT rows)
+    //   then per residual unit u, chunk c < NRC - 1: conv7 taps TPC c ..
+    //   TPC c + TPC - 1 (C rows in w7_row order, TPC C columns); the last
+    //   chunk: tap 6 (C x C, w7_row order) followed by the 1x1 weights (C x C)
     //   -> wsm, buffer j & 1
-    constexpr int CT_PIECES = NT * 32 / 8, RU_PIECES = C * KC / 8;
+    constexpr int CT_PIECES = NT * CTW / 8, RU_PIECES = C * 2 * C / 8;
     constexpr int PIECES = CT_PIECES > RU_PIECES ? CT_PIECES : RU_PIECES;
     constexpr int PPT = (PIECES + NTH - 1) / NTH;  // 16-byte pieces per thread
     Chunk pa[PPT], pb[PPT];                        // chunks jc + 1 and jc + 2
     auto chunk_load = [&](int j, Chunk(&r)[PPT]) {
         j %= NCH;
-        const half_t *src;
-        int ld, width, rows;
-        if (j < NKT) {
-            src = p.WT + j * 32;
-            ld = KT;
-            width = 32;
-            rows = NT;
-        } else {
-            const int u = (j - NKT) / (N7C + 1), c = (j - NKT) % (N7C + 1);
-            src = c < N7C ? p.W7[u] + c * KC : p.W1[u];
-            ld = c < N7C ? K7 : C;
-            width = KC;
-            rows = C;
-        }
-        const int n = rows * width / 8, ppr = width / 8;
+        if (j < NCT) {
+            constexpr int ppr = CTW / 8;
 #pragma unroll
-        for (int i = 0; i < PPT; i++) {
-            const int k = tid + i * NTH;
-            if (k < n) {
-                const int row = k / ppr, c8 = (k - row * ppr) * 8;
-                r[i] = *(const Chunk *)(src + (long)row * ld + c8);
+            for (int i = 0; i < PPT; i++) {
+                const int k = tid + i * NTH;
+                if (k < CT_PIECES) {
+                    const int row = k / ppr, c8 = (k - row * ppr) * 8;
+                    r[i] = *(const Chunk *)(p.WT + (long)row * KT + j * CTW + c8);
+                }
+            }
+        } else {
+            const int u = (j - NCT) / NRC, c = (j - NCT) % NRC;
+            const bool last = c == NRC - 1;
+            const int ppr = (last ? 2 * C : TPC * C) / 8;
+#pragma unroll
+            for (int i = 0; i < PPT; i++) {
+                const int k = tid + i * NTH;
+                if (k < C * ppr) {
+                    const int row = k / ppr, c8 = (k - row * ppr) * 8;
+                    const half_t *src = !last || c8 < C
+                                            ? p.W7[u] + (long)row * K7 + TPC * c * C + c8
+                                            : p.W1[u] + (long)row * C + (c8 - C);
+                    r[i] = *(const Chunk *)src;
+                }
             }
         }
     };
     auto chunk_store = [&](int j, const Chunk(&r)[PPT]) {
         j %= NCH;
         half_t *const dst = wsm + (j & 1) * W_BUF;
-        int ldd, width, rows;
-        bool k7 = false;  // conv7 chunk: rows in w7_row order
-        if (j < NKT) {
-            ldd = LDCT;
-            width = 32;
-            rows = NT;
-        } else {
-            ldd = LDC;
-            width = KC;
-            rows = C;
-            k7 = (j - NKT) % (N7C + 1) < N7C;
-        }
-        const int n = rows * width / 8, ppr = width / 8;
+        if (j < NCT) {
+            constexpr int ppr = CTW / 8;
 #pragma unroll
-        for (int i = 0; i < PPT; i++) {
-            const int k = tid + i * NTH;
-            if (k < n) {
-                const int row = k / ppr, c8 = (k - row * ppr) * 8;
-                const int o = k7 ? w7_row(row) * ldd + (c8 ^ x128(w7_row(row)))
-                                 : row * ldd + (width == 32 ? c8 ^ x64(row) : c8 ^ x128(row));
-                *(Chunk *)(dst + o) = r[i];
+            for (int i = 0; i < PPT; i++) {
+                const int k = tid + i * NTH;
+                if (k < CT_PIECES) {
+                    const int row = k / ppr, c8 = (k - row * ppr) * 8;
+                    *(Chunk *)(dst + row * CTW + (CTW == 64 ? c8 ^ x128(row) : c8 ^ x64(row))) =
+                        r[i];
+                }
+            }
+        } else {
+            const bool last = (j - NCT) % NRC == NRC - 1;
+            const int ppr = (last ? 2 * C : TPC * C) / 8;
+#pragma unroll
+            for (int i = 0; i < PPT; i++) {
+                const int k = tid + i * NTH;
+                if (k < C * ppr) {
+                    const int row = k / ppr, c8 = (k - row * ppr) * 8;
+                    const int lr = w7_row(row);
+                    const int o = !last    ? lr * TPC * C + (c8 ^ xtap(lr))
+                                  : c8 < C ? lr * C + (c8 ^ x128(lr))
+                                           : C * C + row * C + ((c8 - C) ^ x128(row));
+                    *(Chunk *)(dst + o) = r[i];
+                }
             }
         }
     };
@@ -360,17 +378,19 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
             }
 #pragma unroll
             for (int ks = 0; ks < NKT; ks++) {
-                const half_t *wp = RES ? wTs + ks * 32 : wsm + (ks & 1) * W_BUF;
-                const int wld = RES ? LDT : LDCT;
+                // streamed: K step ks is columns (32 ks) mod CTW of chunk 32 ks / CTW
+                const half_t *wp = RES ? wTs + ks * 32 : wsm + ((ks * 32 / CTW) & 1) * W_BUF;
+                const int wld = RES ? LDT : CTW;
+                const int wk = RES ? lg * 8
+                                   : ((ks * 32) % CTW + lg * 8) ^ (CTW == 64 ? x128(l16) : x64(l16));
 #pragma unroll
                 for (int r = 0; r < S; r++)
 #pragma unroll
                     for (int n = 0; n < NB; n++) {
-                        const h8 wf = *(const h8 *)(wp + (r * C + n * 16 + l16) * wld +
-                                                    (RES ? lg * 8 : (lg * 8) ^ x64(l16)));
+                        const h8 wf = *(const h8 *)(wp + (r * C + n * 16 + l16) * wld + wk);
                         x[r][n] = mma(wf, xf[ks], x[r][n]);
                     }
-                if (!RES && ks + 1 < NKT)
+                if (!RES && (ks + 1) * 32 % CTW == 0 && ks + 1 < NKT)
                     advance();
             }
             // epilogue: + bias -> x; Snake -> a1
@@ -467,22 +487,30 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
                 }
             } else {
 #pragma unroll 1
-                for (int j7 = 0; j7 < N7C; j7++) {
-                    const half_t *wb = wsm + ((NKT + u * (N7C + 1) + j7) & 1) * W_BUF;
-                    int ro[S];
-                    tap_offsets(j7 * KC / C, ro);  // a chunk holds one tap (KC == C)
+                for (int c = 0; c < NRC - 1; c++) {  // taps TPC c .. TPC c + TPC - 1
+                    const half_t *wb = wsm + ((NCT + u * NRC + c) & 1) * W_BUF;
+#pragma unroll 1
+                    for (int t2 = 0; t2 < TPC; t2++) {
+                        int ro[S];
+                        tap_offsets(TPC * c + t2, ro);
 #pragma unroll
-                    for (int kin = 0; kin < KC; kin += 32)
-                        step7(kin, wb, LDC, (kin + lg * 8) ^ x128(l16), ro);
+                        for (int kin = 0; kin < C; kin += 32)
+                            step7(kin, wb, TPC * C, (t2 * C + kin + lg * 8) ^ xtap(l16), ro);
+                    }
                     advance();
                 }
+                // tap 6: first half of the unit's last chunk
+                const half_t *wb = wsm + ((NCT + u * NRC + NRC - 1) & 1) * W_BUF;
+                int ro[S];
+                tap_offsets(6, ro);
+#pragma unroll
+                for (int kin = 0; kin < C; kin += 32)
+                    step7(kin, wb, C, (kin + lg * 8) ^ x128(l16), ro);
             }
-            // the unit's input is dead from here on (the streamed path's last
-            // conv7 chunk ended with a barrier): its rows take the next
+            // the unit's input is dead from here on: its rows take the next
             // activation, whose left context a stream's first tile reads from
             // the halo fill's buffers
-            if constexpr (RES)
-                __syncthreads();
+            __syncthreads();
             if (first && (u == 0 || FINAL)) {
                 const half_t *sx = u == 0 ? p.a2_ext + ((long)b * 18 + (long)cu0 * p.r_out) * C
                                           : p.ao_ext + ((long)b * 6 + (long)cu0 * p.r_out) * C;
@@ -496,8 +524,8 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
             // accumulators of blocks 2k, 2k+1 hold channels 32k + 8 lg + 0..7 of
             // its row: exactly its B operand of the 1x1 conv's K step k.
             const half_t *w1p = RES ? w1s + u * C * LD1
-                                    : wsm + ((NKT + u * (N7C + 1) + N7C) & 1) * W_BUF;
-            const int w1ld = RES ? LD1 : LDC;
+                                    : wsm + ((NCT + u * NRC + NRC - 1) & 1) * W_BUF + C * C;
+            const int w1ld = RES ? LD1 : C;
 #pragma unroll
             for (int r = 0; r < S; r++) {
                 h8 hb[NB / 2];
