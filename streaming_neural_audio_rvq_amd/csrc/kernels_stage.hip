@@ -653,7 +653,7 @@ struct StageInst {
 constexpr StageInst INSTS[] = {
     {64, 3, NW_Q3, false, false},  // Qwen-shaped stage 3, weights streamed
     {32, 4, NW_Q4, true, true},    // Qwen-shaped stage 4 + final conv, weights resident
-    {64, 4, 6, false, false},  // Fish-shaped stage 3, weights streamed
+    {64, 4, 8, false, false},  // Fish-shaped stage 3, weights streamed
     {32, 2, 16, true, true},   // Fish-shaped stage 4 + final conv, weights resident
 };
 
@@ -680,7 +680,7 @@ hipError_t launch_stage_fused(const StageArgs &a, int C, int S, int T, bool fina
     if (C == 32 && S == 4 && final_stage && T == tile_rows(INSTS[1]))
         return launch_stage_t<32, 4, NW_Q4, true, true>(a, st);
     if (C == 64 && S == 4 && !final_stage && T == tile_rows(INSTS[2]))
-        return launch_stage_t<64, 4, 6, false, false>(a, st);
+        return launch_stage_t<64, 4, 8, false, false>(a, st);
     if (C == 32 && S == 2 && final_stage && T == tile_rows(INSTS[3]))
         return launch_stage_t<32, 2, 16, true, true>(a, st);
     return hipErrorInvalidValue;
