@@ -127,12 +127,12 @@ __device__ __forceinline__ int frame_of(const ConvArgs &p, int m)
     return (int)((t + (((uint32_t)m - t) >> p.div_s1)) >> p.div_s2);
 }
 
-// Output of 4 consecutive columns n..n+3 (channel ch..ch+3 of the output
-// row) of packed input row m, bias added: + residual, fp32 store, activation
-// and compute-type store.  al / ial: Snake parameters of channels ch..ch+3.
+// Output of 4 consecutive columns n..n+3 of packed input row m (stream b),
+// bias included: + residual, fp32 store, activation and compute-type store.
+// al / ial: Snake parameters of the 4 output channels.
 template <typename T>
-__device__ __forceinline__ void epilogue4(const ConvArgs &p, int m, int b, int n, int ch, f4 v,
-                                          f4 al, f4 ial)
+__device__ __forceinline__ void epilogue4(const ConvArgs &p, int m, int b, int n, f4 v, f4 al,
+                                          f4 ial)
 {
     if (p.res) {
         f4 rr = *(const f4 *)(p.res + (long)m * p.Cout + n);
@@ -596,7 +596,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ConvArgs p)
     v = v + *(const f4 *)(p.bias + ch);
     f4 al, ial;
     snake_params(p, ch, al, ial);
-    epilogue4<T>(p, m, p.out16 ? p.frame_stream[frame_of(p, m)] : 0, n, ch, v, al, ial);
+    epilogue4<T>(p, m, p.out16 ? p.frame_stream[frame_of(p, m)] : 0, n, v, al, ial);
 }
 
 struct TileDesc {
