@@ -51,69 +51,76 @@ __global__ __launch_bounds__(256) void halo_save_kernel(HaloTable t, char *state
         *(u4 *)(dst + i) = *(const u4 *)(src + i);
 }
 
-__device__ __forceinline__ void load8(const uint16_t *p, float *v)
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void load4(const uint16_t *p, float *v)
 {
     // bf16 -> fp32 is exact: the bits move to the top half
-    u4 w = *(const u4 *)p;
+    u2 w = *(const u2 *)p;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < 2; i++) {
         v[2 * i] = __uint_as_float(w[i] << 16);
         v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
 }
-__device__ __forceinline__ void load8(const float *p, float *v)
+__device__ __forceinline__ void load4(const float *p, float *v)
 {
-    f4 a = *(const f4 *)p, b = *(const f4 *)(p + 4);
+    f4 a = *(const f4 *)p;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < 4; i++)
         v[i] = a[i];
-        v[4 + i] = b[i];
-    }
 }
-__device__ __forceinline__ void store8(half_t *p, const float *v)
+__device__ __forceinline__ void store4(half_t *p, const float *v)
 {
-    h8 h;
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-        h[i] = snrvq_f16(v[i]);
-    *(h8 *)p = h;
+    *(h4 *)p = h4{snrvq_f16(v[0]), snrvq_f16(v[1]), snrvq_f16(v[2]), snrvq_f16(v[3])};
 }
-__device__ __forceinline__ void store8(float *p, const float *v)
+__device__ __forceinline__ void store4(float *p, const float *v)
 {
     *(f4 *)p = f4{v[0], v[1], v[2], v[3]};
-    *(f4 *)(p + 4) = f4{v[4], v[5], v[6], v[7]};
 }
 
-// One thread owns 8 consecutive latent values of one frame and sums the K
+// One thread owns 4 consecutive latent values of one frame and sums the K
 // selected codebook rows in codebook order, in fp32.  The codebooks are one
-// contiguous [K][E][d_cb] array.
+// contiguous [K][E][d_cb] array.  Codebooks are taken 8 at a time: their
+// codes, then their rows are loaded before any is added, so a thread has up to
+// 8 row loads in flight instead of one.
 template <typename CB, typename OUT>
 __global__ __launch_bounds__(256) void rvq_gather_kernel(const CB *cb, const int32_t *codes,
                                                          int F, int K, int E, int d_cb, OUT *z,
                                                          unsigned long long *bad)
 {
-    const int per_frame = d_cb / 8;
+    const int per_frame = d_cb / 4;
     long g = (long)blockIdx.x * 256 + threadIdx.x;
     long f = g / per_frame;
     if (f >= F)
         return;
-    int d = (int)(g - f * per_frame) * 8;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int d = (int)(g - f * per_frame) * 4;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
     const int32_t *cf = codes + f * K;
-    for (int k = 0; k < K; k++) {
-        int e = cf[k];
-        if ((unsigned)e >= (unsigned)E) {  // only reachable with device-resident codes
-            if (d == 0)
-                atomicAdd(bad, 1ull);
-            e = 0;
-        }
-        float v[8];
-        load8(cb + ((long)k * E + e) * d_cb + d, v);
+    for (int k0 = 0; k0 < K; k0 += 8) {
+        int e[8];
 #pragma unroll
-        for (int i = 0; i < 8; i++)
-            acc[i] += v[i];
+        for (int j = 0; j < 8; j++) {
+            e[j] = k0 + j < K ? cf[k0 + j] : 0;
+            if ((unsigned)e[j] >= (unsigned)E) {  // only reachable with device-resident codes
+                if (d == 0)
+                    atomicAdd(bad, 1ull);
+                e[j] = 0;
+            }
+        }
+        float v[8][4];
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            if (k0 + j < K)
+                load4(cb + ((long)(k0 + j) * E + e[j]) * d_cb + d, v[j]);
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            if (k0 + j < K)
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    acc[i] += v[j][i];
     }
-    store8(z + f * d_cb + d, acc);
+    store4(z + f * d_cb + d, acc);
 }
 
 template <typename T>
@@ -281,7 +288,7 @@ hipError_t launch_rvq_gather(const void *cb, int cb_dtype, const int32_t *codes,
 {
     if (F <= 0)
         return hipSuccess;
-    long threads = (long)F * (d_cb / 8);
+    long threads = (long)F * (d_cb / 4);
     dim3 grid((unsigned)((threads + 255) / 256));
     if (cb_dtype == 1 && out_dtype == 1)
         hipLaunchKernelGGL((rvq_gather_kernel<uint16_t, half_t>), grid, dim3(256), 0, st,
