@@ -425,7 +425,7 @@ int timed(codec *c, const char *name, int64_t units, hipStream_t s, Fn &&fn)
     return CODEC_OK;
 }
 
-ConvArgs conv_args(codec *c, const Lin &L, const void *A, int A_H, int rate_in, int M,
+ConvArgs conv_args(codec *, const Lin &L, const void *A, int A_H, int rate_in, int M,
                    const StepMeta &m)
 {
     ConvArgs a{};

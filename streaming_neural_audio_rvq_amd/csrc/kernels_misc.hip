@@ -123,18 +123,8 @@ __global__ __launch_bounds__(256) void rvq_gather_kernel(const CB *cb, const int
     store4(z + f * d_cb + d, acc);
 }
 
-template <typename T>
-__device__ __forceinline__ void unpack(const T *p, int n, float *v);
-template <>
-__device__ __forceinline__ void unpack<half_t>(const half_t *p, int n, float *v)
-{
-    h8 h = *(const h8 *)p;
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-        v[i] = (float)h[i];
-}
-template <>
-__device__ __forceinline__ void unpack<float>(const float *p, int n, float *v)
+// 4 fp32 values (the fp32 final conv's operand load)
+__device__ __forceinline__ void unpack4(const float *p, float *v)
 {
     f4 a = *(const f4 *)p;
 #pragma unroll
@@ -190,7 +180,7 @@ __global__ __launch_bounds__(256) void final_conv_kernel(const T *A, int A_H, in
                 const float *wj = wsh + j * C + qp * CQ;
                 for (int c = 0; c < CQ; c += VEC) {
                     float v[8];
-                    unpack<T>(row + c, VEC, v);
+                    unpack4((const float *)(row + c), v);
 #pragma unroll
                     for (int e = 0; e < VEC; e++)
                         part += wj[c + e] * v[e];
