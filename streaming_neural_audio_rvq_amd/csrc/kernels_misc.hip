@@ -123,34 +123,19 @@ __global__ __launch_bounds__(256) void rvq_gather_kernel(const CB *cb, const int
     store4(z + f * d_cb + d, acc);
 }
 
-// 4 fp32 values (the fp32 final conv's operand load)
-__device__ __forceinline__ void unpack4(const float *p, float *v)
-{
-    f4 a = *(const f4 *)p;
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-        v[i] = a[i];
-}
-
-// pcm[m] = b + sum_j sum_c w[j][c] A[row(m) - (6 - j)][c]; one thread per
-// output sample, fp32 accumulation.  The channels are split in four
-// quarters, each summed taps-then-channels ascending, and combined as
-// b + ((q0 + q1) + (q2 + q3)) -- the order the fused last-stage kernel uses
-// with four threads per sample.
-template <typename T>
-__global__ __launch_bounds__(256) void final_conv_kernel(const T *A, int A_H, int C, int rate,
+// fp32 final conv: pcm[m] = b + sum_j sum_c w[j][c] A[row(m) - (6 - j)][c],
+// one thread per output sample, fp32 accumulation.  The channels are split in
+// four quarters, each summed taps-then-channels ascending, and combined as
+// b + ((q0 + q1) + (q2 + q3)).
+__global__ __launch_bounds__(256) void final_conv_kernel(const float *A, int A_H, int C, int rate,
                                                          const float *w, float bias, int tanh_out,
                                                          const int32_t *frame_stream, int M,
                                                          float *pcm)
 {
-    extern __shared__ float wsh[];  // [7][C]: fp32, or fp16 pairs for fp16 operands
-    h2 *wsh16 = (h2 *)wsh;
+    extern __shared__ float wsh[];  // [7][C]
     for (int i = threadIdx.x; i < 7 * C; i += blockDim.x) {
         int c = i / 7, j = i - c * 7;  // input layout [C][7]
-        if (sizeof(T) == 2)
-            ((half_t *)wsh16)[j * C + c] = (half_t)w[i];
-        else
-            wsh[j * C + c] = w[i];
+        wsh[j * C + c] = w[i];
     }
     __syncthreads();
     long m = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -158,33 +143,18 @@ __global__ __launch_bounds__(256) void final_conv_kernel(const T *A, int A_H, in
         return;
     int b = frame_stream[m / rate];
     long ext = (long)(b + 1) * A_H + m;
-    constexpr int VEC = 16 / (int)sizeof(T);
     const int CQ = C / 4;
     float q[4];
     for (int qp = 0; qp < 4; qp++) {
         float part = 0.f;
         for (int j = 0; j < 7; j++) {
-            const T *row = A + (ext - (6 - j)) * C + qp * CQ;
-            if constexpr (sizeof(T) == 2) {
-                // fp16 operands: pairs of channels on v_dot2 (fp32 accumulation),
-                // taps then channel pairs in order
-                const h2 *wj = wsh16 + (j * C + qp * CQ) / 2;
-                for (int c = 0; c < CQ; c += 8) {
-                    const h8 v = *(const h8 *)(row + c);
+            const float *row = A + (ext - (6 - j)) * C + qp * CQ;
+            const float *wj = wsh + j * C + qp * CQ;
+            for (int c = 0; c < CQ; c += 4) {
+                const f4 v = *(const f4 *)(row + c);
 #pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        part = __builtin_amdgcn_fdot2(h2{v[2 * e], v[2 * e + 1]}, wj[c / 2 + e],
-                                                      part, false);
-                }
-            } else {
-                const float *wj = wsh + j * C + qp * CQ;
-                for (int c = 0; c < CQ; c += VEC) {
-                    float v[8];
-                    unpack4((const float *)(row + c), v);
-#pragma unroll
-                    for (int e = 0; e < VEC; e++)
-                        part += wj[c + e] * v[e];
-                }
+                for (int e = 0; e < 4; e++)
+                    part += wj[c + e] * v[e];
             }
         }
         q[qp] = part;
@@ -303,16 +273,17 @@ hipError_t launch_final_conv(const void *A, int dtype, int A_H, int C, int rate,
         return hipSuccess;
     dim3 grid((M + 255) / 256);
     size_t sh = sizeof(float) * 7 * C;
-    if (dtype && C % 32 == 0)
+    // fp16 channel widths are multiples of 32 (the codec's configuration
+    // check); fp32 ones multiples of 16, so C / 4 is a whole number of f4s
+    if (dtype ? C % 32 : C % 16)
+        return hipErrorInvalidValue;
+    if (dtype)
         hipLaunchKernelGGL(final_conv_mfma_kernel, dim3((M + 63) / 64), dim3(256), sh, st,
                            (const half_t *)A, A_H, C, rate, w, b, final_tanh, frame_stream, M,
                            pcm);
-    else if (dtype)
-        hipLaunchKernelGGL(final_conv_kernel<half_t>, grid, dim3(256), sh, st, (const half_t *)A,
-                           A_H, C, rate, w, b, final_tanh, frame_stream, M, pcm);
     else
-        hipLaunchKernelGGL(final_conv_kernel<float>, grid, dim3(256), sh, st, (const float *)A,
-                           A_H, C, rate, w, b, final_tanh, frame_stream, M, pcm);
+        hipLaunchKernelGGL(final_conv_kernel, grid, dim3(256), sh, st, (const float *)A, A_H, C,
+                           rate, w, b, final_tanh, frame_stream, M, pcm);
     return hipGetLastError();
 }
 
