@@ -650,12 +650,17 @@ ConvPlan conv_gemm_plan(const ConvArgs &a, int dtype, int n_cu, long partial_cap
     // the tiles are tried largest first, and the first that reaches 1.5 work-
     // groups per CU -- alone, or with K split (>= 8 K stages per split) -- is
     // taken; failing all, the plan with the most work-groups.
+    // A short K (at most 16 stages) is not split when a tile covers three
+    // quarters of the CUs without it: there the reduce launch costs more than
+    // the idle CUs (the 128-stream projection: 7 us unsplit at 64 x 64, 13 us
+    // split at 128 x 32).
     const TileDesc *t = dtype ? H_TILES : F_TILES;
     const int n = dtype ? NH : NF;
     const int Ktot = a.taps * a.Cin;  // a K stage must not straddle two taps
     const long target = 3L * n_cu / 2;
     ConvPlan best{-1, 1};
     long best_work = -1;
+    int unsplit = -1;  // largest short-K tile reaching 3/4 of the CUs
     for (int i = 0; i < n; i++) {
         if (a.N % t[i].BN != 0 || a.Cin % t[i].BK != 0)
             continue;
@@ -666,14 +671,16 @@ ConvPlan conv_gemm_plan(const ConvArgs &a, int dtype, int n_cu, long partial_cap
             best_work = tiles;
             best = ConvPlan{i, 1};
         }
+        const int nk = Ktot / t[i].BK;
+        if (unsplit < 0 && nk <= 16 && 4 * tiles >= 3L * n_cu)
+            unsplit = i;
         if (!a.splits_allowed || partial_cap <= 0)
             continue;
-        const int nk = Ktot / t[i].BK;
         for (int sp = 2; sp <= 32; sp++) {
             if (nk / sp < 8 || (long)sp * a.M * a.N > partial_cap)
                 break;
             if (tiles * sp >= target)
-                return ConvPlan{i, sp};
+                return unsplit >= 0 ? ConvPlan{unsplit, 1} : ConvPlan{i, sp};
             if (tiles * sp > best_work) {
                 best_work = tiles * sp;
                 best = ConvPlan{i, sp};
