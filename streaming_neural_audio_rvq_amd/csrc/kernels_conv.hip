@@ -167,7 +167,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int total)
     return x * q + (x < r ? x : r) + i;
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int KSUB, bool RU = false>
+template <typename T, int BM, int BN, int WM, int WN, int KSUB, bool RU = false, int NBUF = 2>
 __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
 {
     constexpr int BK0 = Traits<T>::BK;
@@ -197,8 +197,12 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
     constexpr int SMEM_BUF = (BM + BN) * LD * (int)sizeof(T);
     constexpr int SMEM_RU0 = RU ? BM * (BN + 8) * 2 : 0;  // h tile
     constexpr int SMEM_RU1 = RU ? 2 * BN * 72 * 2 : 0;    // 1x1 weight chunks
+    // NBUF > 2 stage buffers (fp16 direct loads only): the loads of stage
+    // ks + NBUF - 1 are issued while stage ks is multiplied, so a stage's
+    // loads have NBUF - 1 stages of MFMA work to land in
+    static_assert(NBUF == 2 || (DIRECT && !RU), "deep pipeline: fp16 direct loads");
     constexpr int SMEM0 = SMEM_BUF > SMEM_RU0 ? SMEM_BUF : SMEM_RU0;
-    constexpr int SMEM1 = SMEM_BUF > SMEM_RU1 ? SMEM_BUF : SMEM_RU1;
+    constexpr int SMEM1 = (SMEM_BUF > SMEM_RU1 ? SMEM_BUF : SMEM_RU1) + (NBUF - 2) * SMEM_BUF;
     __shared__ __attribute__((aligned(16))) char smem[SMEM0 + SMEM1 + BM * 4];
     char *const smem0 = smem, *const smem1 = smem + SMEM0;
     int *const rowb = (int *)(smem + SMEM0 + SMEM1);
@@ -406,6 +410,50 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
         __builtin_amdgcn_s_setprio(0);
     };
 
+    if constexpr (NBUF > 2) {
+        // stage j of this split sits in buffer j mod NBUF; every wave issues
+        // the same LPS loads per stage, so "stage ks has landed" is a vmcnt
+        // of LPS times the number of younger stages in flight
+        static_assert(A_FULL && B_FULL, "uniform loads per wave");
+        constexpr int LPS = A_N + B_N;
+        auto bufA = [&](int j) { return (T *)(smem + (j % NBUF) * SMEM_BUF); };
+        auto bufB = [&](int j) { return bufA(j) + BM * LD; };
+        load_bias();
+        int issued = ks0;
+#pragma unroll
+        for (int i = 0; i < NBUF - 1; i++)
+            if (issued < ks1) {
+                gload(issued, bufA(issued - ks0), bufB(issued - ks0));
+                issued++;
+            }
+        if (ks0 >= ks1) {
+#pragma unroll
+            for (int i = 0; i < FM; i++)
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+                    acc[i][j] = binit[j];
+        }
+        for (int ks = ks0; ks < ks1; ks++) {
+            if (issued - ks - 1 == NBUF - 2)
+                __builtin_amdgcn_s_waitcnt(0x3f70 | ((LPS * (NBUF - 2)) & 15) |
+                                           (((LPS * (NBUF - 2)) >> 4) << 14));
+            else
+                __builtin_amdgcn_s_waitcnt(0x3f70);  // tail: everything
+            // stage ks is visible to every wave, and the buffer of stage
+            // ks - 1 is free (every wave is done with it).  A bare barrier:
+            // __syncthreads() would also wait for the younger stages' loads
+            // (its release fence waits for every outstanding memory op)
+            __asm__ volatile("s_barrier" ::: "memory");
+            if (issued < ks1) {
+                gload(issued, bufA(issued - ks0), bufB(issued - ks0));
+                issued++;
+            }
+            if (ks == ks0)
+                mma_stage(bufA(0), bufB(0), std::true_type());
+            else
+                mma_stage(bufA(ks - ks0), bufB(ks - ks0), std::false_type());
+        }
+    } else {
     if (ks0 < ks1) {
         gload(ks0, A0, B0);
         sstore(A0, B0);
@@ -440,6 +488,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
             sstore(An, Bn);
         loads_done();
         __syncthreads();
+    }
     }
 
     if constexpr (RU) {
@@ -609,18 +658,29 @@ const TileDesc H_TILES[] = {
     {128, 128, 64, "h128x128k64"}, {128, 64, 64, "h128x64k64"}, {64, 128, 64, "h64x128k64"},
     {64, 64, 64, "h64x64k64"},     {256, 32, 32, "h256x32"},    {128, 32, 32, "h128x32"},
     {32, 64, 32, "h32x64"},        {64, 32, 32, "h64x32"},
+    // three stage buffers: two work-groups per CU still fit (74 KB of LDS each)
+    {128, 64, 64, "h128x64k64b3"}, {64, 128, 64, "h64x128k64b3"},
 };
+// fp16 tiles tried first, unsplit: 128 x 128 (double-buffered), then the
+// three-buffer half tiles.  Timed alone on the 128-stream layer shapes, a
+// half tile with its loads three stages deep beats a split 128 x 128 tile on
+// the frame-rate layers (k = 7 conv 6352 x 512 x 3584: 35 us against 40 us
+// split in two; transposed conv 794 x 4096 x 2048: 28 against 35 us), while
+// on layers that fill the GPU unsplit the double-buffered 128 x 128 tile
+// stays ahead of every deeper pipeline (31760 x 256 x 1792: 33 us against
+// 42-50 us).
+const int H_UNSPLIT[] = {0, 8, 9};
 const TileDesc F_TILES[] = {
     {64, 64, 16, "f64x64"}, {128, 32, 16, "f128x32"}, {64, 32, 16, "f64x32"}, {64, 16, 16, "f64x16"},
 };
 constexpr int NH = sizeof(H_TILES) / sizeof(H_TILES[0]);
 constexpr int NF = sizeof(F_TILES) / sizeof(F_TILES[0]);
 
-template <typename T, int BM, int BN, int WM, int WN, int KSUB, bool RU = false>
+template <typename T, int BM, int BN, int WM, int WN, int KSUB, bool RU = false, int NBUF = 2>
 hipError_t launch_t(const ConvArgs &a, hipStream_t st)
 {
     int ntm = (a.M + BM - 1) / BM, ntn = a.N / BN;
-    hipLaunchKernelGGL((conv_gemm_kernel<T, BM, BN, WM, WN, KSUB, RU>), dim3(ntm * ntn, a.splits),
+    hipLaunchKernelGGL((conv_gemm_kernel<T, BM, BN, WM, WN, KSUB, RU, NBUF>), dim3(ntm * ntn, a.splits),
                        dim3(256), 0, st, a);
     return hipGetLastError();
 }
@@ -645,19 +705,27 @@ void set_division(ConvArgs &a)
 // split, partials within the workspace) until the CUs are covered.
 ConvPlan conv_gemm_plan(const ConvArgs &a, int dtype, int n_cu, long partial_cap)
 {
-    // LDS bandwidth bounds this kernel, and a larger tile reads fewer LDS
-    // bytes per MFMA (a 64 x 64 wave tile half as many as a 32 x 32 one).  So
-    // the tiles are tried largest first, and the first that reaches 1.5 work-
-    // groups per CU -- alone, or with K split (>= 8 K stages per split) -- is
-    // taken; failing all, the plan with the most work-groups.
+    // A larger tile reads fewer LDS and L2 bytes per MFMA (a 64 x 64 wave
+    // tile half as many as a 32 x 32 one).  First the unsplit candidates
+    // (H_UNSPLIT) are tried; then the tiles largest first, and the first that
+    // reaches 1.5 work-groups per CU -- alone, or with K split (>= 8 K stages
+    // per split) -- is taken; failing all, the plan with the most work-groups.
     // A short K (at most 16 stages) is not split when a tile covers three
     // quarters of the CUs without it: there the reduce launch costs more than
     // the idle CUs (the 128-stream projection: 7 us unsplit at 64 x 64, 13 us
     // split at 128 x 32).
     const TileDesc *t = dtype ? H_TILES : F_TILES;
-    const int n = dtype ? NH : NF;
+    const int n = dtype ? 8 : NF;  // tiles the split search walks, in order
     const int Ktot = a.taps * a.Cin;  // a K stage must not straddle two taps
     const long target = 3L * n_cu / 2;
+    if (dtype) {
+        for (int i : H_UNSPLIT) {
+            if (a.N % t[i].BN != 0 || a.Cin % t[i].BK != 0)
+                continue;
+            if ((long)((a.M + t[i].BM - 1) / t[i].BM) * (a.N / t[i].BN) >= target)
+                return ConvPlan{i, 1};
+        }
+    }
     ConvPlan best{-1, 1};
     long best_work = -1;
     int unsplit = -1;  // largest short-K tile reaching 3/4 of the CUs
@@ -717,6 +785,8 @@ hipError_t launch_conv_gemm(const ConvArgs &a0, int dtype, hipStream_t st, ConvP
         case 5: e = launch_t<half_t, 128, 32, 4, 1, 1>(a, st); break;
         case 6: e = launch_t<half_t, 32, 64, 2, 2, 1>(a, st); break;
         case 7: e = launch_t<half_t, 64, 32, 4, 1, 1>(a, st); break;
+        case 8: e = launch_t<half_t, 128, 64, 2, 2, 2, false, 3>(a, st); break;
+        case 9: e = launch_t<half_t, 64, 128, 2, 2, 2, false, 3>(a, st); break;
         }
     } else {
         switch (plan.tile) {
