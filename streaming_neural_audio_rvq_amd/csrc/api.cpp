@@ -673,13 +673,10 @@ int enqueue_device(codec *c, int B, int F, const MetaLayout &ml, const int32_t *
         return rc;
 
     // ---- device work ----
-    rc = timed(c, "halo_fill", B, s,
-               [&] { return launch_halo_fill(c->halo, c->state, m, B, s); });
-    if (rc)
-        return rc;
+    // the gather and the halo fill of every layer share one launch
     rc = timed(c, "rvq_gather", F, s, [&] {
-        return launch_rvq_gather(c->cb, c->cb_dtype, m.codes, F, g.K, g.E, g.d_cb, c->z, c->dtype,
-                                 c->bad_codes, s);
+        return launch_rvq_gather_fill(c->cb, c->cb_dtype, m.codes, F, g.K, g.E, g.d_cb, c->z,
+                                      c->dtype, c->bad_codes, c->halo, c->state, m, B, s);
     });
     if (rc)
         return rc;

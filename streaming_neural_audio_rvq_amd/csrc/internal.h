@@ -126,18 +126,18 @@ bool ru_gemm_supported(int Cout, int dtype);
 hipError_t launch_ru_gemm(const ConvArgs &a, hipStream_t st);
 const char *conv_gemm_tile_name(int dtype, int tile);
 
-hipError_t launch_halo_fill(const HaloTable &t, void *state, const StepMeta &m, int B,
-                            hipStream_t st);
 hipError_t launch_halo_save(const HaloTable &t, void *state, const StepMeta &m, int B,
                             hipStream_t st);
 
 // z[f][:] = sum_k cb[k][codes[f][k]][:] (cb is one [K][E][d_cb] array),
 // written in the compute type.  cb_dtype: 0 fp32 tables, 1 bf16 tables.
 // out_dtype: 0 fp32, 1 fp16.  Codes outside [0, E) are counted in *bad and
-// read as 0.
-hipError_t launch_rvq_gather(const void *cb, int cb_dtype, const int32_t *codes, int F, int K,
-                             int E, int d_cb, void *z, int out_dtype, unsigned long long *bad,
-                             hipStream_t st);
+// read as 0.  The same launch fills the halo rows of every layer of table t
+// from the streams' slots (zeros for fresh streams): the two are independent.
+hipError_t launch_rvq_gather_fill(const void *cb, int cb_dtype, const int32_t *codes, int F,
+                                  int K, int E, int d_cb, void *z, int out_dtype,
+                                  unsigned long long *bad, const HaloTable &t, void *state,
+                                  const StepMeta &m, int B, hipStream_t st);
 
 // pcm[m] = b + sum_{j, c} w[c][j] A_ext[row(m) - (6 - j), c], m < M (k = 7, Cout = 1).
 hipError_t launch_final_conv(const void *A, int dtype, int A_H, int C, int rate,

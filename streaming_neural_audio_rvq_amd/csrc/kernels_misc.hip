@@ -1,7 +1,7 @@
 // kernels_misc.hip -- the non-GEMM kernels of a decode step:
 //   * halo fill / save: move each stream's left context between its state
-//     slot and the halo rows of every extended conv input (one launch each
-//     per step, all layers at once);
+//     slot and the halo rows of every extended conv input (all layers at
+//     once; the fill shares one launch with the gather);
 //   * RVQ gather-and-sum of the codebook rows of every frame;
 //   * the final causal conv to one channel: on the matrix cores for fp16
 //     operands (weights in row 0 of the A operand, 16 samples per MFMA
@@ -17,14 +17,13 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
-// blockIdx.x = batch index b, blockIdx.y = halo layer.  Copies the slot's H
-// rows into the halo of stream b (zeros for a fresh stream).
-__global__ __launch_bounds__(256) void halo_fill_kernel(HaloTable t, const char *state,
-                                                        const int32_t *cu, const int32_t *slot,
-                                                        const int32_t *fresh)
+// Copies the slot's H rows of halo layer `layer` into the halo of stream b
+// (zeros for a fresh stream); one work-group.
+__device__ __forceinline__ void halo_fill_one(const HaloTable &t, int layer, int b,
+                                              const char *state, const int32_t *cu,
+                                              const int32_t *slot, const int32_t *fresh)
 {
-    const int b = blockIdx.x;
-    const HaloLayer L = t.l[blockIdx.y];
+    const HaloLayer &L = t.l[layer];
     const long row_bytes = (long)L.C * t.elem_bytes;
     const long bytes = (long)L.H * row_bytes;
     char *dst = (char *)L.ext + ((long)b * L.H + (long)cu[b] * L.rate) * row_bytes;
@@ -85,12 +84,12 @@ __device__ __forceinline__ void store4(float *p, const float *v)
 // codes, then their rows are loaded before any is added, so a thread has up to
 // 8 row loads in flight instead of one.
 template <typename CB, typename OUT>
-__global__ __launch_bounds__(256) void rvq_gather_kernel(const CB *cb, const int32_t *codes,
-                                                         int F, int K, int E, int d_cb, OUT *z,
-                                                         unsigned long long *bad)
+__device__ __forceinline__ void rvq_gather_body(int blk, const CB *cb, const int32_t *codes, int F,
+                                                int K, int E, int d_cb, OUT *z,
+                                                unsigned long long *bad)
 {
     const int per_frame = d_cb / 4;
-    long g = (long)blockIdx.x * 256 + threadIdx.x;
+    long g = (long)blk * 256 + threadIdx.x;
     long f = g / per_frame;
     if (f >= F)
         return;
@@ -121,6 +120,24 @@ __global__ __launch_bounds__(256) void rvq_gather_kernel(const CB *cb, const int
                     acc[i] += v[j][i];
     }
     store4(z + f * d_cb + d, acc);
+}
+
+// The step's first launch: the gather in work-groups [0, gblocks), the halo
+// fill of every (layer, stream) pair in the rest.  The two are independent,
+// so one launch runs them side by side instead of one after the other.
+template <typename CB, typename OUT>
+__global__ __launch_bounds__(256) void rvq_gather_fill_kernel(
+    const CB *cb, const int32_t *codes, int F, int K, int E, int d_cb, OUT *z,
+    unsigned long long *bad, int gblocks, HaloTable t, const char *state, const int32_t *cu,
+    const int32_t *slot, const int32_t *fresh, int B)
+{
+    const int blk = blockIdx.x;
+    if (blk < gblocks) {
+        rvq_gather_body(blk, cb, codes, F, K, E, d_cb, z, bad);
+        return;
+    }
+    const int j = blk - gblocks;
+    halo_fill_one(t, j / B, j % B, state, cu, slot, fresh);
 }
 
 // fp32 final conv: pcm[m] = b + sum_j sum_c w[j][c] A[row(m) - (6 - j)][c],
@@ -222,16 +239,6 @@ __global__ __launch_bounds__(256) void unextend_kernel(const T *ext, int H, int 
 
 }  // namespace
 
-hipError_t launch_halo_fill(const HaloTable &t, void *state, const StepMeta &m, int B,
-                            hipStream_t st)
-{
-    if (t.n == 0 || B == 0)
-        return hipSuccess;
-    hipLaunchKernelGGL(halo_fill_kernel, dim3(B, t.n), dim3(256), 0, st, t,
-                       (const char *)state, m.cu, m.slot, m.fresh);
-    return hipGetLastError();
-}
-
 hipError_t launch_halo_save(const HaloTable &t, void *state, const StepMeta &m, int B,
                             hipStream_t st)
 {
@@ -242,26 +249,33 @@ hipError_t launch_halo_save(const HaloTable &t, void *state, const StepMeta &m, 
     return hipGetLastError();
 }
 
-hipError_t launch_rvq_gather(const void *cb, int cb_dtype, const int32_t *codes, int F, int K,
-                             int E, int d_cb, void *z, int out_dtype, unsigned long long *bad,
-                             hipStream_t st)
+hipError_t launch_rvq_gather_fill(const void *cb, int cb_dtype, const int32_t *codes, int F,
+                                  int K, int E, int d_cb, void *z, int out_dtype,
+                                  unsigned long long *bad, const HaloTable &t, void *state,
+                                  const StepMeta &m, int B, hipStream_t st)
 {
-    if (F <= 0)
+    if (F <= 0 || B <= 0)
         return hipSuccess;
-    long threads = (long)F * (d_cb / 4);
-    dim3 grid((unsigned)((threads + 255) / 256));
+    const long threads = (long)F * (d_cb / 4);
+    const int gblocks = (int)((threads + 255) / 256);
+    const dim3 grid((unsigned)(gblocks + (long)t.n * B));
+    const char *sp = (const char *)state;
     if (cb_dtype == 1 && out_dtype == 1)
-        hipLaunchKernelGGL((rvq_gather_kernel<uint16_t, half_t>), grid, dim3(256), 0, st,
-                           (const uint16_t *)cb, codes, F, K, E, d_cb, (half_t *)z, bad);
+        hipLaunchKernelGGL((rvq_gather_fill_kernel<uint16_t, half_t>), grid, dim3(256), 0, st,
+                           (const uint16_t *)cb, codes, F, K, E, d_cb, (half_t *)z, bad, gblocks,
+                           t, sp, m.cu, m.slot, m.fresh, B);
     else if (cb_dtype == 0 && out_dtype == 0)
-        hipLaunchKernelGGL((rvq_gather_kernel<float, float>), grid, dim3(256), 0, st,
-                           (const float *)cb, codes, F, K, E, d_cb, (float *)z, bad);
+        hipLaunchKernelGGL((rvq_gather_fill_kernel<float, float>), grid, dim3(256), 0, st,
+                           (const float *)cb, codes, F, K, E, d_cb, (float *)z, bad, gblocks, t,
+                           sp, m.cu, m.slot, m.fresh, B);
     else if (cb_dtype == 1 && out_dtype == 0)
-        hipLaunchKernelGGL((rvq_gather_kernel<uint16_t, float>), grid, dim3(256), 0, st,
-                           (const uint16_t *)cb, codes, F, K, E, d_cb, (float *)z, bad);
+        hipLaunchKernelGGL((rvq_gather_fill_kernel<uint16_t, float>), grid, dim3(256), 0, st,
+                           (const uint16_t *)cb, codes, F, K, E, d_cb, (float *)z, bad, gblocks,
+                           t, sp, m.cu, m.slot, m.fresh, B);
     else
-        hipLaunchKernelGGL((rvq_gather_kernel<float, half_t>), grid, dim3(256), 0, st,
-                           (const float *)cb, codes, F, K, E, d_cb, (half_t *)z, bad);
+        hipLaunchKernelGGL((rvq_gather_fill_kernel<float, half_t>), grid, dim3(256), 0, st,
+                           (const float *)cb, codes, F, K, E, d_cb, (half_t *)z, bad, gblocks, t,
+                           sp, m.cu, m.slot, m.fresh, B);
     return hipGetLastError();
 }
 
