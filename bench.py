@@ -586,6 +586,8 @@ def main() -> int:
         del src, dst
 
     cfg = RI.get_config(args.config)
+    if args.graph:  # one spare slot for the single-stream latency probe
+        cfg["max_streams"] += 1
     w = RI.make_weights(cfg)
     codec = snr.Codec(cfg, RI.weight_bits(w))
     hop = codec.hop
