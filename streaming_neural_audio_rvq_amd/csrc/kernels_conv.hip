@@ -18,7 +18,8 @@
 //
 // Tiles: 256 threads (4 waves of 64), BM x BN output tile, K staged in steps
 // of BK = 32 KSUB (fp16, v_mfma_f32_16x16x32_f16) or 16 (fp32,
-// v_mfma_f32_16x16x4_f32).  K stages are double-buffered in LDS.  fp16
+// v_mfma_f32_16x16x4_f32).  K stages are double-buffered in LDS (three
+// buffers for the 128 x 64 and 64 x 128 tiles of the frame-rate layers).  fp16
 // stages go global -> LDS directly (16-byte global_load_lds: no register
 // staging and no LDS store instructions, which would otherwise share the LDS
 // port with the fragment reads), into unpadded rows with XOR-permuted 16-byte
@@ -453,42 +454,42 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
             else
                 mma_stage(bufA(ks - ks0), bufB(ks - ks0), std::false_type());
         }
-    } else {
-    if (ks0 < ks1) {
-        gload(ks0, A0, B0);
-        sstore(A0, B0);
-    }
-    load_bias();
-    loads_done();
-    __syncthreads();
-    // first K stage (buffer 0) peeled: its MFMAs start from the bias
-    if (ks0 < ks1) {
-        if (ks0 + 1 < ks1)
-            gload(ks0 + 1, A1, B1);
-        mma_stage(A0, B0, std::true_type());
-        if (ks0 + 1 < ks1)
-            sstore(A1, B1);
+    } else {  // two stage buffers
+        if (ks0 < ks1) {
+            gload(ks0, A0, B0);
+            sstore(A0, B0);
+        }
+        load_bias();
         loads_done();
         __syncthreads();
-    } else {
+        // first K stage (buffer 0) peeled: its MFMAs start from the bias
+        if (ks0 < ks1) {
+            if (ks0 + 1 < ks1)
+                gload(ks0 + 1, A1, B1);
+            mma_stage(A0, B0, std::true_type());
+            if (ks0 + 1 < ks1)
+                sstore(A1, B1);
+            loads_done();
+            __syncthreads();
+        } else {
 #pragma unroll
-        for (int i = 0; i < FM; i++)
+            for (int i = 0; i < FM; i++)
 #pragma unroll
-            for (int j = 0; j < FN; j++)
-                acc[i][j] = binit[j];
-    }
-    for (int ks = ks0 + 1; ks < ks1; ks++) {
-        const int buf = (ks - ks0) & 1;
-        T *const Ac = buf ? A1 : A0, *const Bc = buf ? B1 : B0;
-        T *const An = buf ? A0 : A1, *const Bn = buf ? B0 : B1;
-        if (ks + 1 < ks1)
-            gload(ks + 1, An, Bn);
-        mma_stage(Ac, Bc, std::false_type());
-        if (ks + 1 < ks1)
-            sstore(An, Bn);
-        loads_done();
-        __syncthreads();
-    }
+                for (int j = 0; j < FN; j++)
+                    acc[i][j] = binit[j];
+        }
+        for (int ks = ks0 + 1; ks < ks1; ks++) {
+            const int buf = (ks - ks0) & 1;
+            T *const Ac = buf ? A1 : A0, *const Bc = buf ? B1 : B0;
+            T *const An = buf ? A0 : A1, *const Bn = buf ? B0 : B1;
+            if (ks + 1 < ks1)
+                gload(ks + 1, An, Bn);
+            mma_stage(Ac, Bc, std::false_type());
+            if (ks + 1 < ks1)
+                sstore(An, Bn);
+            loads_done();
+            __syncthreads();
+        }
     }
 
     if constexpr (RU) {
