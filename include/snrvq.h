@@ -99,6 +99,13 @@ typedef struct {
  * all stages or for upsample stage i only. */
 #define CODEC_FLAG_PER_LAYER 1
 #define CODEC_FLAG_PER_LAYER_STAGE(i) (1 << (8 + (i)))
+/* Conv GEMM planner restrictions, for testing and comparison.  NO_SPLIT_K:
+ * never split a contraction over K (a split sums partials in another order,
+ * so without splits every tile choice gives bit-identical output).
+ * TWO_STAGE_BUFFERS: only tiles that double-buffer their K stages (not the
+ * three-buffer 128 x 64 / 64 x 128 tiles). */
+#define CODEC_FLAG_NO_SPLIT_K 2
+#define CODEC_FLAG_TWO_STAGE_BUFFERS 4
 
 typedef struct {
     int32_t hop;                 /* PCM samples per frame */

@@ -22,6 +22,8 @@ DTYPE_F32, DTYPE_BF16, DTYPE_F16 = 0, 1, 2
 ACT = {"snake": 0, "elu": 1}
 CAPTURE_LATENT, CAPTURE_DEC_INPUT = 0, 1
 FLAG_PER_LAYER = 1
+FLAG_NO_SPLIT_K = 2
+FLAG_TWO_STAGE_BUFFERS = 4
 MAX_STAGES = 8
 
 ERROR_NAMES = {1: "EINVAL", 2: "ESTREAM", 3: "EDUP", 4: "ERANGE", 5: "ENOSLOT", 6: "ETOOBIG",
@@ -150,6 +152,8 @@ def make_cfg(cfg: dict) -> codec_cfg:
     c.max_streams = cfg["max_streams"]
     c.max_frames_per_call = cfg["max_frames_per_call"]
     c.flags = (FLAG_PER_LAYER if cfg.get("per_layer", False) else 0) | \
+        (FLAG_NO_SPLIT_K if cfg.get("no_split_k", False) else 0) | \
+        (FLAG_TWO_STAGE_BUFFERS if cfg.get("two_stage_buffers", False) else 0) | \
         sum(1 << (8 + i) for i in cfg.get("per_layer_stages", ()))
     return c
 

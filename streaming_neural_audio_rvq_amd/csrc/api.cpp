@@ -457,7 +457,8 @@ void set_act(codec *c, ConvArgs &a, const ActP &p)
 int run_conv(codec *c, const char *name, const ConvArgs &a0, hipStream_t s, bool allow_split = true)
 {
     ConvArgs a = a0;
-    a.splits_allowed = allow_split;
+    a.splits_allowed = allow_split && !(c->cfg.flags & CODEC_FLAG_NO_SPLIT_K);
+    a.deep_allowed = !(c->cfg.flags & CODEC_FLAG_TWO_STAGE_BUFFERS);
     a.partial = c->splitk_ws;
     const ConvPlan plan = conv_gemm_plan(a, c->dtype, c->n_cu, c->splitk_cap);
     return timed(c, name, (int64_t)a.M, s,

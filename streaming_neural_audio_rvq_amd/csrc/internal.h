@@ -74,6 +74,7 @@ struct ConvArgs {
     int div_s1, div_s2;     //   (set by the launcher)
     int splits;             // split-K count (set by the launcher)
     int splits_allowed;     // 1: the planner may split K
+    int deep_allowed;       // 1: the planner may take the three-buffer tiles
     float *partial;         // split-K partials [splits][M][N] fp32
     // residual unit in one launch (k = 7 conv -> act7 -> 1x1 conv -> epilogue):
     // A, Wt describe the k = 7 conv, bias and everything after it the 1x1

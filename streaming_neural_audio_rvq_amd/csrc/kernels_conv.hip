@@ -652,6 +652,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ConvArgs p)
 struct TileDesc {
     int BM, BN, BK;
     const char *name;
+    bool deep = false;  // three K stage buffers
 };
 
 // fp16 operand tiles, in order of preference
@@ -660,7 +661,7 @@ const TileDesc H_TILES[] = {
     {64, 64, 64, "h64x64k64"},     {256, 32, 32, "h256x32"},    {128, 32, 32, "h128x32"},
     {32, 64, 32, "h32x64"},        {64, 32, 32, "h64x32"},
     // three stage buffers: two work-groups per CU still fit (74 KB of LDS each)
-    {128, 64, 64, "h128x64k64b3"}, {64, 128, 64, "h64x128k64b3"},
+    {128, 64, 64, "h128x64k64b3", true}, {64, 128, 64, "h64x128k64b3", true},
 };
 // fp16 tiles tried first, unsplit: 128 x 128 (double-buffered), then the
 // three-buffer half tiles.  Timed alone on the 128-stream layer shapes, a
@@ -721,7 +722,7 @@ ConvPlan conv_gemm_plan(const ConvArgs &a, int dtype, int n_cu, long partial_cap
     const long target = 3L * n_cu / 2;
     if (dtype) {
         for (int i : H_UNSPLIT) {
-            if (a.N % t[i].BN != 0 || a.Cin % t[i].BK != 0)
+            if (a.N % t[i].BN != 0 || a.Cin % t[i].BK != 0 || (t[i].deep && !a.deep_allowed))
                 continue;
             if ((long)((a.M + t[i].BM - 1) / t[i].BM) * (a.N / t[i].BN) >= target)
                 return ConvPlan{i, 1};

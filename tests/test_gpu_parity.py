@@ -184,6 +184,33 @@ def test_repeat_runs_bitwise_identical():
         assert np.array_equal(x, y)
 
 
+def test_three_buffer_tiles_bitwise_equal_double_buffered():
+    """The three-stage-buffer half tiles change how K stages are staged, not
+    the order of the sums: with K never split, steps whose frame-rate layers
+    take them (96 streams x 8 frames: there a 128 x 64 tile reaches 1.5
+    work-groups per CU and a 128 x 128 tile does not) decode bit for bit as
+    with double-buffered tiles only; the second step continues from the
+    first's state.  Stream 0 is also checked against the oracle."""
+    cfg = RI.get_config("c2", max_streams=96, max_frames_per_call=1024, no_split_k=True)
+    w = RI.make_weights(cfg)
+    B, plan = 96, [8, 8]
+    codes = [RI.stream_codes(cfg, b, sum(plan)) for b in range(B)]
+    outs = []
+    for variant in (cfg, dict(cfg, two_stage_buffers=True)):
+        say(f"case three-buffer tiles: two_stage_buffers={variant.get('two_stage_buffers', False)}")
+        codec = open_codec(variant, w)
+        ids = [codec.stream_open() for _ in range(B)]
+        outs.append(run_lockstep(codec, ids, codes, plan))
+        codec.close()
+    for x, y in zip(*outs):
+        assert np.isfinite(x).all()
+        assert np.array_equal(x, y)
+    ref = oracle.Model(cfg, w).decode_full(codes[0])
+    e, ac = rel_err(outs[0][0], ref)
+    say(f"stream 0: err/peak {e:.3e} AC-rel {ac:.3e}")
+    assert e <= tol_for(cfg)
+
+
 def test_c4_full_scale_sampled_parity():
     """The headline workload: 128 streams at staggered offsets (prefilled),
     steps of mixed chunk sizes {1,2,4,8,16}; sampled streams' chunks are
