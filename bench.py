@@ -442,6 +442,7 @@ def rocprof_summary(args) -> int:
         frames = [int(RI.c4_chunk_sizes(cfg, j).sum()) for j in idx]
         res["copy_mib"] = args.copy_mib
         per_cls = {}
+        whole = {}  # every dispatch of the decode steps
         for tag, path in (("FETCH_SIZE", args.pmc_fetch), ("WRITE_SIZE", args.pmc_write)):
             fn = [f for f in os.listdir(path) if f.endswith("counter_collection.csv")][0]
             rows = [r for r in csv.DictReader(open(os.path.join(path, fn)))
@@ -454,6 +455,11 @@ def rocprof_summary(args) -> int:
             st = _steady(rows, len(idx))
             seen = {}
             for r in st:
+                step_bytes = float(r["Counter_Value"]) * 1024.0 * factor
+                whole[tag] = whole.get(tag, 0.0) + step_bytes
+                if tag == "FETCH_SIZE":
+                    whole["kernel_ns"] = whole.get("kernel_ns", 0.0) + (
+                        int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
                 cls = kernel_class(r["Kernel_Name"], cfg)
                 if not cls.endswith(".fused"):
                     continue
@@ -483,6 +489,19 @@ def rocprof_summary(args) -> int:
             out.append(f"| {cls} | {n} | {c['units']} | {f:.1f} | {w:.1f} | {f + w:.1f} | "
                        f"{alg:.1f} |")
             res["traffic"][cls] = {"bytes_per_unit": round(f + w, 3)}
+        nsteps = len(idx)
+        step_b = (whole["FETCH_SIZE"] + whole["WRITE_SIZE"]) / nsteps
+        step_s = whole["kernel_ns"] * 1e-9 / nsteps
+        out.append(f"\nWhole decode step (every dispatch of the {nsteps} counted steps, "
+                   f"{sum(frames) / nsteps:.0f} frames per step): "
+                   f"{whole['FETCH_SIZE'] / nsteps / 1e6:.1f} MB fetched + "
+                   f"{whole['WRITE_SIZE'] / nsteps / 1e6:.1f} MB written = "
+                   f"{step_b / 1e6:.1f} MB per step ({step_b / (sum(frames) / nsteps) / 1e3:.1f} kB "
+                   f"per frame); over the counter run's own kernel time ({step_s * 1e6:.0f} us per "
+                   f"step) that is {step_b / step_s / 1e9:.0f} GB/s, "
+                   f"{step_b / step_s / 8e12:.3f} of the 8 TB/s HBM peak.\n")
+        res["step_hbm"] = {"bytes_per_step": round(step_b), "kernel_us_per_step":
+                           round(step_s * 1e6, 1), "GB_per_s": round(step_b / step_s / 1e9, 1)}
         src = os.path.join(ROOT, "streaming_neural_audio_rvq_amd", "csrc")
         h = hashlib.sha256()
         for fn in ("kernels_stage.hip", "internal.h"):
