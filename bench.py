@@ -355,8 +355,8 @@ def kernel_class(name: str, cfg: dict) -> str:
         for i, st in enumerate(cfg["strides"]):
             if ch[i + 1] == C and st == S:
                 return f"s{i}.fused"
-    for key, cls in (("halo_save", "halo_save"), ("halo_fill", "halo_fill"),
-                     ("rvq_gather", "rvq_gather"), ("final_conv", "final_conv")):
+    for key, cls in (("halo_save", "halo_save"), ("rvq_gather", "rvq_gather"),
+                     ("final_conv", "final_conv")):
         if key in name:
             return cls
     return ""

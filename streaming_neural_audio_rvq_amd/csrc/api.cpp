@@ -4,10 +4,13 @@
 // Decode step (all on the caller's stream):
 //   H2D of the packed step metadata (codes, frame->stream map, cu, slots,
 //   fresh flags, positions) from a pinned ring buffer;
-//   halo fill (every conv layer's left context, all streams, one launch);
-//   RVQ gather-and-sum -> projection GEMM -> input conv -> per stage
-//   [ConvT -> RU(d=1) -> RU(d=3)], each RU = conv7 launch + conv1 launch with
-//   the residual add fused into the conv1 epilogue -> final conv to PCM;
+//   one launch: the RVQ gather-and-sum of every frame beside the halo fill
+//   (every conv layer's left context, all streams);
+//   projection GEMM -> [windowed transformer] -> input conv -> per stage
+//   [ConvT -> RU(d=1) -> RU(d=3)] -> final conv to PCM, where an RU is a conv7
+//   launch and a conv1 launch with the residual add in its epilogue (one
+//   launch at 128 channels), and the late stages run as one fused kernel
+//   each, the last one with the final conv;
 //   halo save (last rows of every extended input back into the slots).
 // Every activation (Snake / ELU) is applied once, in the epilogue of the
 // layer that produces its input, so the stored left context is exactly the
