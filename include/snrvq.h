@@ -250,6 +250,17 @@ int codec_chunk_plan(int32_t total, const int32_t *ramp, int32_t n_ramp, int32_t
 int codec_resolve_initial_chunk_frames(int64_t value, int32_t has_value, int32_t steady,
                                        int32_t default_frames, int32_t *out);
 
+/* Test-only: the conv GEMM planner's choice for one launch shape -- host
+ * logic only, no device or codec needed.  M output rows, N output columns,
+ * Cin input channels per tap, taps; fp16 = 1 for fp16 operands (0: fp32);
+ * n_cu compute units; flags: CODEC_FLAG_NO_SPLIT_K and/or
+ * CODEC_FLAG_TWO_STAGE_BUFFERS.  *tile receives the tile's name (a static
+ * string; "none" when no tile fits the shape), *splits the number of K
+ * splits (1: unsplit), for the split-K workspace every codec allocates.
+ * CODEC_EINVAL for non-positive sizes or NULL outputs. */
+int codec_debug_conv_plan(int32_t M, int32_t N, int32_t Cin, int32_t taps, int32_t fp16,
+                          int32_t n_cu, int32_t flags, const char **tile, int32_t *splits);
+
 #ifdef __cplusplus
 }
 #endif

@@ -68,7 +68,7 @@ EXPORTS = ["codec_open", "codec_close", "codec_info", "codec_last_error", "strea
            "decode_chunk_graph",
            "codec_device_status", "codec_debug_capture", "codec_debug_read_state",
            "codec_profile_enable", "codec_profile_read", "codec_chunk_plan",
-           "codec_resolve_initial_chunk_frames"]
+           "codec_resolve_initial_chunk_frames", "codec_debug_conv_plan"]
 
 
 def lib():
@@ -107,6 +107,7 @@ def lib():
                                    C.c_int32, _I32P]
     L.codec_resolve_initial_chunk_frames.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.c_int32,
                                                      _I32P]
+    L.codec_debug_conv_plan.argtypes = [C.c_int32] * 7 + [C.POINTER(C.c_char_p), _I32P]
     _lib = L
     return L
 
@@ -326,3 +327,16 @@ def resolve_initial_chunk_frames(value, steady: int, default_frames: int = 0) ->
     if rc != CODEC_OK:
         raise ValueError(lib().codec_last_error(None).decode())
     return out.value
+
+
+def conv_plan(M: int, N: int, Cin: int, taps: int, fp16: bool = True, n_cu: int = 256,
+              flags: int = 0) -> tuple[str, int]:
+    """The conv GEMM planner's (tile name, K splits) for one launch shape
+    (host logic; for tests and inspection)."""
+    name = C.c_char_p()
+    splits = C.c_int32()
+    rc = lib().codec_debug_conv_plan(int(M), int(N), int(Cin), int(taps), int(bool(fp16)),
+                                     int(n_cu), int(flags), C.byref(name), C.byref(splits))
+    if rc != CODEC_OK:
+        raise ValueError(lib().codec_last_error(None).decode())
+    return name.value.decode(), splits.value

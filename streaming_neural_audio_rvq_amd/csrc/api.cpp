@@ -37,6 +37,8 @@ namespace {
 
 thread_local std::string g_err = "";
 
+constexpr long kSplitKCap = 16L << 20;  // split-K partials per codec: 64 MiB of fp32
+
 int set_err(std::string *dst, int code, const char *fmt, ...)
 {
     char buf[1024];
@@ -1125,7 +1127,7 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
     }
     if ((rc = dev_alloc(c, (void **)&c->pcm_scratch, F * hop * 4, ws)))
         return cleanup_fail(rc);
-    c->splitk_cap = 16L << 20;  // 64 MiB of fp32 partials
+    c->splitk_cap = kSplitKCap;
     if ((rc = dev_alloc(c, (void **)&c->splitk_ws, (size_t)c->splitk_cap * 4, ws)))
         return cleanup_fail(rc);
 
@@ -1649,6 +1651,31 @@ int codec_chunk_plan(int32_t total, const int32_t *ramp, int32_t n_ramp, int32_t
     if (cnt > cap)
         return set_err(nullptr, CODEC_EINVAL, "codec_chunk_plan: %d decodes exceed cap %d", cnt,
                        cap);
+    return CODEC_OK;
+}
+
+int codec_debug_conv_plan(int32_t M, int32_t N, int32_t Cin, int32_t taps, int32_t fp16,
+                          int32_t n_cu, int32_t flags, const char **tile, int32_t *splits)
+{
+    if (M <= 0 || N <= 0 || Cin <= 0 || taps <= 0 || n_cu <= 0 || !tile || !splits)
+        return set_err(nullptr, CODEC_EINVAL,
+                       "codec_debug_conv_plan: M=%d N=%d Cin=%d taps=%d n_cu=%d", M, N, Cin, taps,
+                       n_cu);
+    ConvArgs a{};
+    a.M = M;
+    a.N = N;
+    a.Cout = N;
+    a.Cin = Cin;
+    a.taps = taps;
+    a.dil = 1;
+    a.s = 1;
+    a.rate_in = 1;
+    a.splits_allowed = !(flags & CODEC_FLAG_NO_SPLIT_K);
+    a.deep_allowed = !(flags & CODEC_FLAG_TWO_STAGE_BUFFERS);
+    const int dt = fp16 ? 1 : 0;
+    const ConvPlan p = conv_gemm_plan(a, dt, n_cu, kSplitKCap);
+    *tile = conv_gemm_tile_name(dt, p.tile);
+    *splits = p.tile < 0 ? 0 : p.splits;
     return CODEC_OK;
 }
 

@@ -121,3 +121,48 @@ def test_open_without_gpu_reports_hip_error():
     cfg = RI.get_config("c1")
     e = open_err(cfg, RI.make_weights(cfg))
     assert e.code == snr.CODEC_EHIP
+
+
+def test_conv_planner_choices_on_the_128_stream_shapes():
+    """The planner's tile and K-split choices for the 128-stream decoder's
+    layers at 794 frames on 256 CUs (host logic only)."""
+    F = 794
+    # frame-rate layers: a 128 x 128 tile would leave CUs idle, a three-buffer
+    # half tile reaches 1.5 work-groups per CU unsplit
+    assert snr.conv_plan(F * 8, 512, 512, 7) == ("h128x64k64b3", 1)    # stage-0 k7 conv
+    assert snr.conv_plan(F, 8 * 512, 1024, 2) == ("h128x64k64b3", 1)   # stage-0 transposed conv
+    assert snr.conv_plan(F * 8, 512, 512, 1) == ("h128x64k64b3", 1)    # stage-0 1x1 conv
+    # layers that fill the GPU with 128 x 128 tiles
+    assert snr.conv_plan(F * 40, 256, 256, 7) == ("h128x128k64", 1)    # stage-1 k7 conv
+    assert snr.conv_plan(F * 8, 5 * 256, 512, 2) == ("h128x128k64", 1)  # stage-1 transposed conv
+    assert snr.conv_plan(F * 40, 4 * 128, 256, 2) == ("h128x128k64", 1)  # stage-2 transposed conv
+    # few rows, long K: the input conv splits K; the short-K projection does not
+    tile, sp = snr.conv_plan(F, 1024, 1024, 7)
+    assert sp > 1 and (1024 * 7 // 64) // sp >= 8
+    assert snr.conv_plan(F, 1024, 512, 1)[1] == 1
+
+
+def test_conv_planner_flags_and_invariants():
+    F = 794
+    NO_SPLIT, TWO_BUF = snr.FLAG_NO_SPLIT_K, snr.FLAG_TWO_STAGE_BUFFERS
+    assert snr.conv_plan(F, 1024, 1024, 7, flags=NO_SPLIT)[1] == 1
+    assert not snr.conv_plan(F * 8, 512, 512, 7, flags=TWO_BUF)[0].endswith("b3")
+    rng = np.random.default_rng(11)
+    for _ in range(400):
+        M = int(rng.integers(1, 400_000))
+        N = int(rng.choice([32, 64, 128, 192, 256, 512, 1024, 1280, 1536, 2048, 4096]))
+        Cin = int(rng.choice([32, 64, 128, 256, 512, 1024]))
+        taps = int(rng.choice([1, 2, 7]))
+        flags = int(rng.choice([0, NO_SPLIT, TWO_BUF, NO_SPLIT | TWO_BUF]))
+        tile, sp = snr.conv_plan(M, N, Cin, taps, flags=flags)
+        bm, bn, bk = (int(v) for v in re.match(r"h(\d+)x(\d+)(?:k(\d+))?", tile).groups("32"))
+        assert N % bn == 0 and Cin % bk == 0, (M, N, Cin, taps, tile)
+        assert sp >= 1 and (sp == 1 or (Cin * taps // bk) // sp >= 8), (M, N, Cin, taps, sp)
+        assert sp * M * N <= 16 << 20 or sp == 1
+        if flags & NO_SPLIT:
+            assert sp == 1
+        if flags & TWO_BUF:
+            assert not tile.endswith("b3")
+    with pytest.raises(ValueError):
+        snr.conv_plan(0, 64, 64, 1)
+
