@@ -372,6 +372,68 @@ def _steady(rows: list, n_steps: int) -> list:
     return [r for r in rows if int(r["Dispatch_Id"]) > first]
 
 
+def mfma_summary(args, cfg: dict, out: list, res: dict) -> None:
+    """Matrix-core use over the decode steps of a counter run with
+    SQ_INSTS_MFMA and SQ_VALU_MFMA_BUSY_CYCLES: MFMA instructions (every one a
+    16x16x32 fp16 product, 16,384 FLOP) and the matrix pipes' busy cycles
+    summed over all SIMDs, against the SIMDs' cycles at the nominal 2.4 GHz
+    over the dispatches' own durations."""
+    import csv
+    import rvq_inputs as RI
+    path = args.pmc_mfma
+    fn = [f for f in os.listdir(path) if f.endswith("counter_collection.csv")][0]
+    disp = {}
+    for r in csv.DictReader(open(os.path.join(path, fn))):
+        d = disp.setdefault(int(r["Dispatch_Id"]), {
+            "name": r["Kernel_Name"], "Kernel_Name": r["Kernel_Name"],
+            "Dispatch_Id": r["Dispatch_Id"],
+            "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    idx = step_indices(args.pmc_warmup, args.pmc_steps, False)
+    frames = sum(int(RI.c4_chunk_sizes(cfg, j).sum()) for j in idx)
+    st = _steady(list(disp.values()), len(idx))
+    n_simd = 4 * args.n_cu
+    agg = {}
+    for d in st:
+        a = agg.setdefault(d["name"], {"n": 0, "ns": 0, "mfma": 0.0, "busy": 0.0})
+        a["n"] += 1
+        a["ns"] += d["ns"]
+        a["mfma"] += d.get("SQ_INSTS_MFMA", 0.0)
+        a["busy"] += d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+    tot = {k: sum(a[k] for a in agg.values()) for k in ("ns", "mfma", "busy")}
+    nominal = 2.4e9  # cycles per second the published peak assumes
+    flops = 16384.0 * tot["mfma"]
+    alg = frames * flops_per_frame(cfg)
+    steps = len(idx)
+    out.append("## Matrix-core use over the decode steps\n")
+    busy = tot["busy"] / (n_simd * tot["ns"] * 1e-9 * nominal)
+    out.append(f"{steps} decode steps, {frames / steps:.0f} frames per step. Executed MFMA work "
+               f"{flops / steps / 1e9:.1f} GFLOP per step against {alg / steps / 1e9:.1f} GFLOP "
+               f"algorithmic (the fused stages recompute their tile halos); "
+               f"{tot['busy'] / max(tot['mfma'], 1):.1f} busy cycles per MFMA. Over the kernel "
+               f"time the matrix pipes of all {n_simd} SIMDs were busy {busy:.3f} of their "
+               f"cycles at the nominal 2.4 GHz; executed work ran at "
+               f"{flops / (tot['ns'] * 1e-9) / 1e12:.0f} TFLOP/s, algorithmic work at "
+               f"{alg / (tot['ns'] * 1e-9) / 1e12:.0f} TFLOP/s "
+               f"({alg / (tot['ns'] * 1e-9) / (PEAK_F16_TFLOPS * 1e12):.3f} of the published "
+               f"{PEAK_F16_TFLOPS / 1000:.1f} PFLOP/s).\n")
+    out.append("| kernel | calls | avg us | MFMA busy at 2.4 GHz | executed TFLOP/s |")
+    out.append("|---|---:|---:|---:|---:|")
+    res["mfma"] = {"busy_fraction_nominal": round(busy, 4),
+                   "executed_tflops": round(flops / (tot["ns"] * 1e-9) / 1e12, 1),
+                   "algorithmic_tflops": round(alg / (tot["ns"] * 1e-9) / 1e12, 1),
+                   "executed_gflop_per_step": round(flops / steps / 1e9, 2),
+                   "algorithmic_gflop_per_step": round(alg / steps / 1e9, 2)}
+    for k, a in sorted(agg.items(), key=lambda kv: -kv[1]["ns"])[:args.top]:
+        if a["mfma"] == 0:
+            continue
+        short = k if len(k) < 90 else k[:87] + "..."
+        b = a["busy"] / (n_simd * a["ns"] * 1e-9 * nominal)
+        out.append(f"| `{short}` | {a['n']} | {a['ns'] / a['n'] / 1e3:.1f} | {b:.3f} | "
+                   f"{16384.0 * a['mfma'] / (a['ns'] * 1e-9) / 1e12:.0f} |")
+    out.append("")
+
+
 def rocprof_summary(args) -> int:
     """Text summary of a rocprofv3 kernel trace of this benchmark, and of two
     counter runs (FETCH_SIZE, WRITE_SIZE) scaled by the same counters of a
@@ -510,6 +572,8 @@ def rocprof_summary(args) -> int:
         out.append("\nThe traffic holds for the kernel source whose SHA-256 (kernels_stage.hip "
                    "then internal.h) is recorded below; bench.py reports it only while the "
                    "source matches.\n")
+    if args.pmc_mfma:
+        mfma_summary(args, cfg, out, res)
     out.append("```json\n" + json.dumps(res, indent=1) + "\n```")
     text = "\n".join(out) + "\n"
     if args.rocprof_summary == "-":
@@ -576,6 +640,9 @@ def main() -> int:
     ap.add_argument("--kt-warmup", type=int, default=2)
     ap.add_argument("--pmc-fetch", help="rocprofv3 --pmc FETCH_SIZE output directory")
     ap.add_argument("--pmc-write", help="rocprofv3 --pmc WRITE_SIZE output directory")
+    ap.add_argument("--pmc-mfma", help="rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES "
+                    "output directory")
+    ap.add_argument("--n-cu", type=int, default=256, help="compute units (counter summaries)")
     ap.add_argument("--pmc-steps", type=int, default=2)
     ap.add_argument("--pmc-warmup", type=int, default=1)
     ap.add_argument("--top", type=int, default=30)
