@@ -434,6 +434,9 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
                 for (int j = 0; j < FN; j++)
                     acc[i][j] = binit[j];
         }
+        // the row table written above must be in LDS before the first bare
+        // barrier publishes it (lgkmcnt(0) only; the loads keep flying)
+        __builtin_amdgcn_s_waitcnt(0xc07f);
         for (int ks = ks0; ks < ks1; ks++) {
             if (issued - ks - 1 == NBUF - 2)
                 __builtin_amdgcn_s_waitcnt(0x3f70 | ((LPS * (NBUF - 2)) & 15) |
