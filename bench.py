@@ -363,13 +363,14 @@ def kernel_class(name: str, cfg: dict) -> str:
 
 
 def _steady(rows: list, n_steps: int) -> list:
-    """Dispatches of the decode steps: everything after the last prefill
-    call, whose end is marked by its state save (one per decode call)."""
-    saves = sorted(int(r["Dispatch_Id"]) for r in rows if "halo_save" in r["Kernel_Name"])
-    if len(saves) < n_steps:
+    """Dispatches of the decode steps: the last n_steps decode calls, each
+    opened by its gather launch (the first kernel of every call), and
+    everything after them."""
+    starts = sorted(int(r["Dispatch_Id"]) for r in rows if "rvq_gather" in r["Kernel_Name"])
+    if len(starts) < n_steps:
         raise SystemExit("trace holds fewer decode calls than the run's steps")
-    first = saves[len(saves) - n_steps - 1] if len(saves) > n_steps else 0
-    return [r for r in rows if int(r["Dispatch_Id"]) > first]
+    first = starts[len(starts) - n_steps]
+    return [r for r in rows if int(r["Dispatch_Id"]) >= first]
 
 
 def mfma_summary(args, cfg: dict, out: list, res: dict) -> None:

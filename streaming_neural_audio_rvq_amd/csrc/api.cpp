@@ -516,6 +516,8 @@ int enqueue_fused_stage(codec *c, int i, int F, const StepMeta &m, float *pcm, h
     a.r_out = c->rate[i + 1];
     a.act = c->cfg.act == CODEC_ACT_ELU ? ACT_ELU : ACT_SNAKE;
     a.n_cu = c->n_cu;
+    if (fin)
+        a.save = c->halo_save;  // the step's halo save rides on the last stage
     char nm[32];
     snprintf(nm, sizeof nm, "s%d.fused", i);
     return timed(c, nm, (int64_t)F * c->rate[i + 1], s, [&] {
@@ -789,10 +791,12 @@ int enqueue_device(codec *c, int B, int F, const MetaLayout &ml, const int32_t *
         if (rc)
             return rc;
     }
-    rc = timed(c, "halo_save", B, s,
-               [&] { return launch_halo_save(c->halo_save, c->state, m, B, s); });
-    if (rc)
-        return rc;
+    if (!c->fuse_T[c->S - 1]) {  // else the fused last stage saved the halos
+        rc = timed(c, "halo_save", B, s,
+                   [&] { return launch_halo_save(c->halo_save, c->state, m, B, s); });
+        if (rc)
+            return rc;
+    }
     c->last_meta = m;
     c->lastF = F;
     c->lastB = B;

@@ -104,6 +104,23 @@ struct HaloTable {
     int64_t slot_elems;
 };
 
+// Saves the last H rows of stream b's extended segment of halo layer `layer`
+// (they start at extended row b H + cu[b+1] rate) into its slot; threads
+// tid of nthreads share the copy.
+__device__ __forceinline__ void halo_save_one(const HaloTable &t, int layer, int b, char *state,
+                                              const int32_t *cu, const int32_t *slot, int tid,
+                                              int nthreads)
+{
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+    const HaloLayer &L = t.l[layer];
+    const long row_bytes = (long)L.C * t.elem_bytes;
+    const long bytes = (long)L.H * row_bytes;
+    const char *src = (const char *)L.ext + ((long)b * L.H + (long)cu[b + 1] * L.rate) * row_bytes;
+    char *dst = state + ((long)slot[b] * t.slot_elems + L.state_off) * t.elem_bytes;
+    for (long i = (long)tid * 16; i < bytes; i += (long)nthreads * 16)
+        *(u4v *)(dst + i) = *(const u4v *)(src + i);
+}
+
 // Per-step device metadata (one H2D copy).
 struct StepMeta {
     int32_t *codes;        // [F][K]
@@ -172,6 +189,8 @@ struct StageArgs {
     int n_streams, n_tiles;
     int r_in, r_out, act;
     int n_cu;                         // compute units of the device
+    HaloTable save;                   // last stage: the per-layer halos its work-groups save
+                                      // once their tiles are done (n = 0: none)
 };
 // Output rows per tile of an instantiated fused stage, or 0 when the shape
 // has none (then the per-layer path runs).  A stream's rows are cut into

@@ -35,19 +35,11 @@ __device__ __forceinline__ void halo_fill_one(const HaloTable &t, int layer, int
     }
 }
 
-// Saves the last H rows of stream b's extended segment (which start at
-// extended row b H + cu[b+1] rate) into its slot.
+// blockIdx.x = batch index b, blockIdx.y = halo layer.
 __global__ __launch_bounds__(256) void halo_save_kernel(HaloTable t, char *state,
                                                         const int32_t *cu, const int32_t *slot)
 {
-    const int b = blockIdx.x;
-    const HaloLayer L = t.l[blockIdx.y];
-    const long row_bytes = (long)L.C * t.elem_bytes;
-    const long bytes = (long)L.H * row_bytes;
-    const char *src = (const char *)L.ext + ((long)b * L.H + (long)cu[b + 1] * L.rate) * row_bytes;
-    char *dst = state + ((long)slot[b] * t.slot_elems + L.state_off) * t.elem_bytes;
-    for (long i = (long)threadIdx.x * 16; i < bytes; i += 256 * 16)
-        *(u4 *)(dst + i) = *(const u4 *)(src + i);
+    halo_save_one(t, blockIdx.y, blockIdx.x, state, cu, slot, threadIdx.x, 256);
 }
 
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));

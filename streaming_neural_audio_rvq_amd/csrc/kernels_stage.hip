@@ -626,6 +626,18 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
             __syncthreads();  // a_out is read before the next tile writes a1
         }
     }  // tile loop
+
+    // The last stage's work-groups also save the per-layer halos of the step
+    // (every earlier layer's output is final by now; this kernel neither
+    // reads those buffers' last rows nor writes their slot regions), so the
+    // step needs no separate save launch and the work fills the tail left
+    // by the last round of tiles.
+    if constexpr (FINAL) {
+        const int jobs = p.save.n * p.n_streams;
+        for (int j = blockIdx.x; j < jobs; j += gridDim.x)
+            halo_save_one(p.save, j / p.n_streams, j % p.n_streams, (char *)p.state, p.cu,
+                          p.slot, tid, NTH);
+    }
 }
 
 template <int C, int S, int NW, bool FINAL, bool RES>
