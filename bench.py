@@ -80,6 +80,14 @@ def layer_model(cfg: dict) -> dict:
         if i == S - 1:
             fpr += m["final_conv"]["fpr"]
             bpr = es * ci / s + 4
+            # the last fused stage also saves every per-layer halo of the step
+            # (read from the layers' buffers, written to the slots): the input
+            # conv's, each stage input's, and the residual-unit inputs of the
+            # stages without a fused kernel (widths above 64 channels)
+            fused = [es == 2 and cfg["act"] == "snake" and ch[k + 1] <= 64 for k in range(S)]
+            per_stream = 6 * dl + sum(ch[:S]) + sum(24 * ch[k + 1] for k in range(S)
+                                                       if not fused[k])
+            wpl += 2 * es * per_stream * cfg["n_streams"]
         else:
             bpr = es * ci / s + es * co
         m[f"s{i}.fused"] = dict(fpr=fpr, bpr=bpr, wpl=wpl)
