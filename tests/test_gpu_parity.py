@@ -354,7 +354,7 @@ def test_fused_stages_bitwise_equal_per_layer(name):
     layer = open_codec(dict(cfg, per_layer=True), w)
     steps = [[1, 3, 16, 2, 1], [8, 1, 1, 5, 2], [2, 16, 4, 1, 7]]
     codes = [RI.stream_codes(cfg, b, sum(s[b] for s in steps), part=3) for b in range(5)]
-    outs = {}
+    outs, states = {}, {}
     for tag, c in (("fused", fused), ("layer", layer)):
         ids = [c.stream_open() for _ in range(5)]
         at = [0] * 5
@@ -367,6 +367,11 @@ def test_fused_stages_bitwise_equal_per_layer(name):
             for b in range(5):
                 at[b] += st[b]
         outs[tag] = np.concatenate(res)
+        states[tag] = [c.read_state(i) for i in ids]
+    # the saved left contexts too: the fused stages write their own and the
+    # last one saves the per-layer ones; the per-layer path saves all in one launch
+    for a, b in zip(states["fused"], states["layer"]):
+        assert np.array_equal(a, b)
     d = np.abs(outs["fused"] - outs["layer"])
     say(f"{name}: max |fused - per-layer| = {d.max():.3e}")
     if d.max() > 0:
