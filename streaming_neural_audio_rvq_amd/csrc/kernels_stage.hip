@@ -594,32 +594,45 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
             // its tap-j rows are consecutive rows of one plane.  A row 0 holds
             // the weights of one (tap, 32 channels) K step, the other rows
             // zeros; K steps tap-major (the per-layer final conv's sequence).
+            // All S phases of a block run together: the input row of (phase
+            // ph, tap j) is ph + j rows on from the block's first, so the
+            // (ph, j) pairs with equal ph + j share one operand read (the S
+            // phases x 7 taps read S + 6 operands, not 7 S).  Each output
+            // keeps the tap-major K sequence.
             const int nsamp = tend - t0;
             const h8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
             const int nqb = (nsamp + 16 * S - 1) / (16 * S);  // blocks per phase
+            // lanes past the tile's last sample read the rows of the last
+            // plane row that has one (still below the buffer's NROWS rows:
+            // at most nsamp - 2 + S + OO), and store nothing
+            const int qmax = (nsamp - 1) / S;
+            for (int qb = wave; qb < nqb; qb += NW) {
+                const int qq = 16 * qb + l16;
+                const int bq = L::base(qq < qmax ? qq : qmax) + lg * 8;
+                f4 acc[S];
 #pragma unroll
-            for (int ph = 0; ph < S; ph++) {
-                for (int qb = wave; qb < nqb; qb += NW) {
-                    int qq = 16 * qb + l16;
-                    const bool ok = S * qq + ph < nsamp;
-                    qq = ok ? qq : (nsamp - 1 - ph) / S;  // nsamp > ph when any lane is ok
-                    const int bq = L::base(qq) + lg * 8;
-                    f4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int ph = 0; ph < S; ph++)
+                    acc[ph] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int j = 0; j < 7; j++) {
-                        // a_out row of sample tt, tap j: tt + j + OO - 6
-                        const int ro = L::rel(ph + j + OO - 6);
+                for (int j = 0; j < 7; j++) {
 #pragma unroll
-                        for (int k0 = 0; k0 < C; k0 += 32) {
-                            const h8 wf =
-                                *(const h8 *)((const half_t *)wout_s + j * C + k0 + lg * 8);
-                            acc = mma(l16 == 0 ? wf : zero, *(const h8 *)(a1s + bq + ro + k0), acc);
-                        }
+                    for (int k0 = 0; k0 < C; k0 += 32) {
+                        const h8 wf = *(const h8 *)((const half_t *)wout_s + j * C + k0 + lg * 8);
+                        const h8 wa = l16 == 0 ? wf : zero;
+#pragma unroll
+                        for (int ph = 0; ph < S; ph++)  // a_out row of sample tt, tap j: tt + j + OO - 6
+                            acc[ph] = mma(wa, *(const h8 *)(a1s + bq + L::rel(ph + j + OO - 6) + k0),
+                                          acc[ph]);
                     }
-                    if (lg == 0 && ok) {
-                        const float yv = p.b_out + acc[0];
-                        p.pcm[(long)cu0 * p.r_out + t0 + S * qq + ph] =
-                            p.final_tanh ? tanhf(yv) : yv;
+                }
+                if (lg == 0) {
+#pragma unroll
+                    for (int ph = 0; ph < S; ph++) {
+                        if (S * qq + ph < nsamp) {
+                            const float yv = p.b_out + acc[ph][0];
+                            p.pcm[(long)cu0 * p.r_out + t0 + S * qq + ph] =
+                                p.final_tanh ? tanhf(yv) : yv;
+                        }
                     }
                 }
             }
