@@ -105,6 +105,15 @@ def flops_per_frame(cfg: dict) -> float:
         for j in range(2):
             tot += (lm[f"s{i}.ru{j}.conv7"]["fpr"] + lm[f"s{i}.ru{j}.conv1"]["fpr"]) * rate[i + 1]
     tot += lm["final_conv"]["fpr"] * rate[-1]
+    if cfg["tf_layers"]:
+        # windowed transformer per frame: in/out projections, per layer the
+        # QKV, output and MLP projections and the attention products over
+        # its window of keys (the full window: the steady state)
+        dm = cfg["tf_heads"] * cfg["tf_head_dim"]
+        dl = cfg["d_lat"]
+        per_layer = 2 * dm * (3 * dm + dm + 2 * cfg["tf_mlp"]) + \
+            2 * 2 * cfg["tf_window"] * dm
+        tot += 2 * 2 * dl * dm + cfg["tf_layers"] * per_layer
     return float(tot)
 
 
