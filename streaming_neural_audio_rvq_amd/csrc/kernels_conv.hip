@@ -712,7 +712,8 @@ ConvPlan conv_gemm_plan(const ConvArgs &a, int dtype, int n_cu, long partial_cap
 {
     // A larger tile reads fewer LDS and L2 bytes per MFMA (a 64 x 64 wave
     // tile half as many as a 32 x 32 one).  First the unsplit candidates
-    // (H_UNSPLIT) are tried; then the tiles largest first, and the first that
+    // (H_UNSPLIT) are tried, then the rule for small problems below; then
+    // the tiles largest first, and the first that
     // reaches 1.5 work-groups per CU -- alone, or with K split (>= 8 K stages
     // per split) -- is taken; failing all, the plan with the most work-groups.
     // A short K (at most 16 stages) is not split when a tile covers three
@@ -729,6 +730,25 @@ ConvPlan conv_gemm_plan(const ConvArgs &a, int dtype, int n_cu, long partial_cap
                 continue;
             if ((long)((a.M + t[i].BM - 1) / t[i].BM) * (a.N / t[i].BN) >= target)
                 return ConvPlan{i, 1};
+        }
+        // Little work (at most 32 64 x 64 x 64 tile stages per CU: the layers
+        // of steps of a few frames): the 64 x 64 tile, which pads the fewest
+        // rows, with K split up to 1.5 work-groups per CU as below, except a
+        // K of at most 16 stages, where the reduce launch costs more than it
+        // saves.  (Qwen-shaped decoder, one stream decoding one frame per
+        // step: 230 us per step against 246 us with the largest tiles split;
+        // 8 streams of 8 frames: 245 against 261 us.)
+        if (a.N % t[3].BN == 0 && a.Cin % t[3].BK == 0) {
+            const long t64 = (long)((a.M + t[3].BM - 1) / t[3].BM) * (a.N / t[3].BN);
+            const int nk = Ktot / t[3].BK;
+            if (t64 * nk <= 32L * n_cu) {
+                int sp = 1;
+                if (a.splits_allowed && partial_cap > 0 && nk > 16)
+                    while (sp < 32 && t64 * sp < target && nk / (sp + 1) >= 8 &&
+                           (long)(sp + 1) * a.M * a.N <= partial_cap)
+                        sp++;
+                return ConvPlan{3, sp};
+            }
         }
     }
     ConvPlan best{-1, 1};

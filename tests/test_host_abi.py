@@ -142,6 +142,25 @@ def test_conv_planner_choices_on_the_128_stream_shapes():
     assert snr.conv_plan(F, 1024, 512, 1)[1] == 1
 
 
+def test_conv_planner_small_steps_take_64x64_tiles():
+    """Layers of steps of a few frames (little work per CU) take the 64 x 64
+    tile, K split up to 1.5 work-groups per CU with at least 8 K stages per
+    split, and K of at most 16 stages unsplit (timed on the Qwen-shaped decoder's
+    first layers at 1, 8 and 64 frames per step)."""
+    for F in (1, 8):
+        assert snr.conv_plan(F, 1024, 1024, 7) == ("h64x64k64", 14)      # input conv
+        assert snr.conv_plan(F, 8 * 512, 1024, 2) == ("h64x64k64", 4)    # stage-0 transposed conv
+        assert snr.conv_plan(F * 8, 512, 512, 7) == ("h64x64k64", 7)     # stage-0 k7 conv
+        assert snr.conv_plan(F * 8, 512, 512, 1) == ("h64x64k64", 1)     # stage-0 1x1 conv
+        assert snr.conv_plan(F * 8, 5 * 256, 512, 2) == ("h64x64k64", 1)  # 16 K stages: unsplit
+    assert snr.conv_plan(64, 1024, 1024, 7) == ("h64x64k64", 14)
+    assert snr.conv_plan(64 * 8, 512, 512, 7) == ("h64x64k64", 6)        # 64 tiles x 6 = 384
+    assert snr.conv_plan(64 * 40, 256, 256, 7) == ("h64x64k64", 3)       # 160 tiles x 3 = 480
+    # no split where the flags forbid it; the 794-frame input conv keeps the large tiles
+    assert snr.conv_plan(8, 1024, 1024, 7, flags=snr.FLAG_NO_SPLIT_K) == ("h64x64k64", 1)
+    assert snr.conv_plan(794, 1024, 1024, 7)[0] != "h64x64k64"
+
+
 def test_conv_planner_flags_and_invariants():
     F = 794
     NO_SPLIT, TWO_BUF = snr.FLAG_NO_SPLIT_K, snr.FLAG_TWO_STAGE_BUFFERS
