@@ -673,8 +673,12 @@ const TileDesc H_TILES[] = {
 // split in two; transposed conv 794 x 4096 x 2048: 28 against 35 us), while
 // on layers that fill the GPU unsplit the double-buffered 128 x 128 tile
 // stays ahead of every deeper pipeline (31760 x 256 x 1792: 33 us against
-// 42-50 us).
-const int H_UNSPLIT[] = {0, 8, 9};
+// 42-50 us).  Each is taken from the work-groups per CU (in quarters) given
+// beside it: 128 x 128 from 1.25 per CU, the half tiles from one per CU (at
+// 512 frames, k = 7 conv 20480 x 256 x 1792: 29 us on 320 128 x 128 tiles
+// against 37 us on 640 half tiles; transposed conv 512 x 4096 x 2048: 22 us on
+// 256 three-buffer half tiles against 27 us on 128 x 128 tiles split in three).
+const int H_UNSPLIT[][2] = {{0, 5}, {8, 4}, {9, 4}};
 const TileDesc F_TILES[] = {
     {64, 64, 16, "f64x64"}, {128, 32, 16, "f128x32"}, {64, 32, 16, "f64x32"}, {64, 16, 16, "f64x16"},
 };
@@ -725,10 +729,11 @@ ConvPlan conv_gemm_plan(const ConvArgs &a, int dtype, int n_cu, long partial_cap
     const int Ktot = a.taps * a.Cin;  // a K stage must not straddle two taps
     const long target = 3L * n_cu / 2;
     if (dtype) {
-        for (int i : H_UNSPLIT) {
+        for (const auto &u : H_UNSPLIT) {
+            const int i = u[0];
             if (a.N % t[i].BN != 0 || a.Cin % t[i].BK != 0 || (t[i].deep && !a.deep_allowed))
                 continue;
-            if ((long)((a.M + t[i].BM - 1) / t[i].BM) * (a.N / t[i].BN) >= target)
+            if (4L * ((a.M + t[i].BM - 1) / t[i].BM) * (a.N / t[i].BN) >= (long)u[1] * n_cu)
                 return ConvPlan{i, 1};
         }
         // Little work (at most 32 64 x 64 x 64 tile stages per CU: the layers

@@ -156,6 +156,10 @@ def test_conv_planner_small_steps_take_64x64_tiles():
     assert snr.conv_plan(64, 1024, 1024, 7) == ("h64x64k64", 14)
     assert snr.conv_plan(64 * 8, 512, 512, 7) == ("h64x64k64", 6)        # 64 tiles x 6 = 384
     assert snr.conv_plan(64 * 40, 256, 256, 7) == ("h64x64k64", 3)       # 160 tiles x 3 = 480
+    # 512 frames: 128 x 128 unsplit from 1.25 work-groups per CU, half tiles from one
+    assert snr.conv_plan(512 * 40, 256, 256, 7) == ("h128x128k64", 1)  # 320 tiles
+    assert snr.conv_plan(512, 8 * 512, 1024, 2) == ("h128x64k64b3", 1)  # 256 tiles
+    assert snr.conv_plan(512 * 8, 512, 512, 7) == ("h128x64k64b3", 1)
     # no split where the flags forbid it; the 794-frame input conv keeps the large tiles
     assert snr.conv_plan(8, 1024, 1024, 7, flags=snr.FLAG_NO_SPLIT_K) == ("h64x64k64", 1)
     assert snr.conv_plan(794, 1024, 1024, 7)[0] != "h64x64k64"
