@@ -252,8 +252,16 @@ def cpu_baseline(name: str, cfg: dict, weights: dict, budget_s: float) -> dict:
         sample = f"{nb} streams x {step} steps of the workload's chunks ({frames} frames)"
     dt = time.perf_counter() - t0
     fr = cfg["sample_rate"] / RI.hop(cfg)
+    cpu = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                cpu = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": frames / dt, "unit": "frames/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu, "host_cpus": os.cpu_count(), "kind": "oracle",
             "sample": f"{sample}, {dt:.1f} s, fp64, parallel across streams and channels",
             "audio_sec_per_s": frames / dt / fr}
 
@@ -581,7 +589,9 @@ def rocprof_summary(args) -> int:
                    f"step) that is {step_b / step_s / 1e9:.0f} GB/s, "
                    f"{step_b / step_s / 8e12:.3f} of the 8 TB/s HBM peak.\n")
         res["step_hbm"] = {"bytes_per_step": round(step_b), "kernel_us_per_step":
-                           round(step_s * 1e6, 1), "GB_per_s": round(step_b / step_s / 1e9, 1)}
+                           round(step_s * 1e6, 1), "GB_per_s": round(step_b / step_s / 1e9, 1),
+                           "frames_per_step": sum(frames) / nsteps}
+        res["library_source_sha256"] = source_digest()
         src = os.path.join(ROOT, "streaming_neural_audio_rvq_amd", "csrc")
         h = hashlib.sha256()
         for fn in ("kernels_stage.hip", "internal.h"):
@@ -624,6 +634,34 @@ def stored_traffic(cls: str, units_per_launch: float):
     return t["bytes_per_unit"] * units_per_launch
 
 
+def source_digest() -> str:
+    """SHA-256 over every library source file (name order)."""
+    import hashlib
+    src = os.path.join(ROOT, "streaming_neural_audio_rvq_amd", "csrc")
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(src)):
+        h.update(open(os.path.join(src, fn), "rb").read())
+    return h.hexdigest()
+
+
+def stored_step_hbm():
+    """HBM bytes per decoded frame of the whole decode step (every kernel),
+    from the committed counter summary of the 128-stream workload, or None
+    when absent or taken from other library source."""
+    import re
+    path = os.path.join(ROOT, "profiles", "stage_fused__qwen_128_streams__hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    mm = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not mm:
+        return None
+    rec = json.loads(mm.group(1))
+    st = rec.get("step_hbm", {})
+    if rec.get("library_source_sha256") != source_digest() or not st.get("frames_per_step"):
+        return None
+    return st["bytes_per_step"] / st["frames_per_step"]
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -641,7 +679,7 @@ def main() -> int:
                     help="share of the CUs in the decode stream's mask (--cotenant masked)")
     ap.add_argument("--graph", action="store_true",
                     help="run every step through decode_chunk_graph (host codes, one graph "
-                         "launch per step, captured once per chunk shape)")
+                         "launch per step, captured once per frame bucket)")
     ap.add_argument("--stateless", action="store_true",
                     help="comparison: decode every chunk again from zero state with up to 16 "
                          "left frames (the pages' stateless variant) instead of carrying state")
@@ -750,8 +788,24 @@ def main() -> int:
         wall = time.perf_counter() - t0
         return fr, max(wall, ev0.elapsed_time(ev1) / 1e3)
 
+    graph_info = None
+    if args.graph:
+        # one untimed pass over the timed steps' chunk schedule captures the
+        # graph of every frame bucket they use; the timed pass then replays
+        for j in range(args.warmup, args.warmup + args.steps):
+            run_step(j)
+        torch.cuda.synchronize()
+        i0 = codec.get_info()
+        graph_info = {"captures_before_timing": i0.graph_captures}
     # ---- timed region: K steps, codes already resident in HBM ----
     frames, elapsed = timed_run(range(args.warmup, args.warmup + args.steps), False)
+    if args.graph:
+        i1 = codec.get_info()
+        graph_info["captures_in_timed_steps"] = i1.graph_captures - i0.graph_captures
+        graph_info["replays_in_timed_steps"] = i1.graph_replays - i0.graph_replays
+        fr = [step_frames(j) for j in range(args.warmup, args.warmup + args.steps)]
+        graph_info["frame_buckets"] = sorted({(f + 31) // 32 * 32 if f > 32 else
+                                              1 << (f - 1).bit_length() for f in fr})
     if codec.device_status() != 0:
         raise RuntimeError("out-of-range codes in the benchmark input")
     fps = frames / elapsed
@@ -845,10 +899,18 @@ def main() -> int:
         "mfma_util_alg": round(fps * fpf / (peak_f * 1e12), 4),
         "roofline": roof,
     }
+    bpf = stored_step_hbm() if args.config == "c4" and not (args.stateless or args.graph) else None
+    out["step_hbm"] = None if bpf is None else {
+        "bytes_per_frame": round(bpf), "achieved": round(bpf * fps / 1e9, 1),
+        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(bpf * fps / 1e9 / PEAK_HBM_GBS, 4),
+        "source": "FETCH_SIZE + WRITE_SIZE of every dispatch of the step (committed counter "
+                  "summary) x this run's frames/s"}
     if cot:
         out["cotenant"] = cot
     if glat:
         out["graph_latency"] = glat
+    if graph_info:
+        out["graphs"] = graph_info
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.config, cfg, w, args.cpu_baseline_seconds)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 2)

@@ -117,6 +117,8 @@ typedef struct {
     int64_t state_bytes_per_stream;
     int64_t weight_bytes;
     int64_t workspace_bytes;
+    int64_t graph_captures;      /* decode_chunk_graph: graphs captured so far */
+    int64_t graph_replays;       /* decode_chunk_graph: steps that replayed one */
 } codec_info_t;
 
 /* ---- lifetime ----------------------------------------------------------- */
@@ -125,9 +127,13 @@ typedef struct {
  * once with the right shape and dtype), uploads and repacks the weights into
  * library-owned device memory on the current HIP device, and preallocates
  * the state slots of max_streams streams and the workspace of
- * max_frames_per_call frames.  Nothing is allocated later.  The caller's
- * host arrays may be freed on return.  On failure *out is NULL and the
- * message is available from codec_last_error(NULL). */
+ * max_frames_per_call frames.  No device or pinned memory is allocated
+ * later (decode_chunk_graph's first use of a bucket instantiates a graph,
+ * a runtime object).  The caller's host arrays may be freed on return.
+ * With BF16 weights the compute operands are fp16: CODEC_EINVAL if a conv
+ * or linear weight lies outside fp16's finite range (|w| > 65504) or the
+ * codebooks' largest entries could sum past it.  On failure *out is NULL
+ * and the message is available from codec_last_error(NULL). */
 int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *cfg,
                codec_t **out);
 
@@ -185,19 +191,25 @@ int decode_chunk_device(codec_t *codec, int32_t B, const int32_t *stream_ids,
                         int64_t pcm_capacity, codec_hip_stream stream);
 
 /* The same step as decode_chunk, replayed from a HIP graph (the pages'
- * streaming decoders capture CUDA graphs per input shape; AREX article on
- * Fish Audio Drama 3, "two stages share one card", and the AI-infra
- * handbook's Qwen3-TTS case, "third stop: the streaming vocoder").  The
- * first call for a chunk shape -- B, n_frames[0..B) and the pcm address --
- * captures the step's device work (metadata copy and every kernel) into a
- * graph; later calls with the same shape fill the step's metadata (codes,
- * slots, positions) into that graph's own pinned buffer and launch the
- * graph, one launch instead of one per kernel.  Results are bit-identical to
- * decode_chunk.  Up to 64 shapes are kept (least recently used evicted),
- * each as two graph instances used in turn; a call waits for the replay two
- * calls back of its shape.  Checks and errors are those of decode_chunk
- * (CODEC_EHIP if capture or instantiation fails).  Profiling events are not
- * recorded for graph steps. */
+ * streaming decoders capture CUDA graphs per input-shape bucket; AREX
+ * article on Fish Audio Drama 3, "two stages share one card", and the
+ * AI-infra handbook's Qwen3-TTS case, "third stop: the streaming vocoder").
+ * A step of F = sum n frames runs as the graph of its bucket: Fb = the next
+ * power of two for F <= 32, else the next multiple of 32.  The Fb - F extra
+ * frames belong to an internal pad stream (zero state, code 0, output
+ * discarded), so any mix of per-stream chunk sizes with the same B and
+ * bucket replays one graph: the per-stream layout travels in the step's
+ * metadata, copied before the launch from the codec's pinned buffers.  The
+ * first call for a (B, bucket) captures the step's kernels (the capture
+ * runs nothing) and instantiates the graph; up to 64 graphs are kept, the
+ * least recently used evicted.  The PCM is written to a codec buffer by the
+ * graph and copied to pcm after it, on the stream.  Results are those of
+ * decode_chunk for the same step within the parity bound (the pad frames
+ * change the step's size, hence possibly its K-split plan, never its
+ * arithmetic); replays of one bucket are bitwise repeatable.  Checks and
+ * errors are those of decode_chunk (CODEC_EHIP if capture or instantiation
+ * fails).  Profiling events are not recorded for graph steps; codec_info
+ * counts captures and replays. */
 int decode_chunk_graph(codec_t *codec, int32_t B, const int32_t *stream_ids,
                        const int32_t *n_frames, const int32_t *codes, float *pcm,
                        int64_t pcm_capacity, codec_hip_stream stream);
@@ -211,9 +223,24 @@ int codec_device_status(codec_t *codec, int64_t *bad_codes);
 
 #define CODEC_CAPTURE_LATENT 0    /* projected RVQ sum, [sum n][d_lat] */
 #define CODEC_CAPTURE_DEC_INPUT 1 /* input of the conv decoder (after the transformer) */
+/* Conv operands of the decoder, in network order (S = n_stages):
+ *   CODEC_CAPTURE_LAYER0 + 3 i          stage i's transposed-conv input,
+ *                                       activated: [sum n * r_i][C_i]
+ *   CODEC_CAPTURE_LAYER0 + 3 i + 1 + j  residual unit j's input of stage i,
+ *                                       activated: [sum n * r_{i+1}][C_{i+1}]
+ *   CODEC_CAPTURE_LAYER0 + 3 S          the final conv's input: [sum n * hop][C_S]
+ * (r_i = prod of strides before stage i, C_i = d_lat / 2^i).  These are the
+ * stored MFMA operands (fp16 for BF16 weights), widened to float32.  Inside
+ * a fused stage kernel the residual-unit and final-conv inputs never reach
+ * memory: capturing them needs a codec opened with CODEC_FLAG_PER_LAYER
+ * (same arithmetic, every layer stored), else CODEC_EINVAL. */
+#define CODEC_CAPTURE_LAYER0 2
 
-/* Copies an intermediate of the last decode step, as float32, packed like
- * the codes: [sum n][d_lat].  dst is device memory with capacity elements. */
+/* Copies an intermediate of the last decode step (any decode entry point)
+ * as float32, packed like the codes: stream after stream, rows of a stream
+ * in time order, [rows][channels].  dst is device memory with capacity
+ * elements; written asynchronously on the stream.  For layer-by-layer
+ * parity against a reference decode of the same frames. */
 int codec_debug_capture(codec_t *codec, int32_t what, float *dst, int64_t capacity,
                         codec_hip_stream stream);
 
@@ -244,11 +271,12 @@ int codec_profile_read(codec_t *codec, int32_t cap, const char **names, double *
 int codec_chunk_plan(int32_t total, const int32_t *ramp, int32_t n_ramp, int32_t steady,
                      int32_t initial, int32_t *out, int32_t cap, int32_t *n_out);
 
-/* Per-request initial chunk size (same section): has_value = 0 uses
- * default_frames; the result is clamped to steady.  CODEC_EINVAL when steady
- * <= 0 or the value is negative. */
-int codec_resolve_initial_chunk_frames(int64_t value, int32_t has_value, int32_t steady,
-                                       int32_t default_frames, int32_t *out);
+/* First-chunk size of one request, in frames (same section: a request may
+ * ask for its own first chunk).  has_request = 0 takes fallback instead of
+ * requested.  The size must be >= 0 and is capped at steady, which must be
+ * >= 1; CODEC_EINVAL otherwise (message via codec_last_error(NULL)). */
+int codec_initial_chunk_size(int64_t requested, int32_t has_request, int32_t steady,
+                             int32_t fallback, int32_t *out);
 
 /* Test-only: the conv GEMM planner's choice for one launch shape -- host
  * logic only, no device or codec needed.  M output rows, N output columns,

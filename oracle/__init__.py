@@ -71,6 +71,7 @@ def lib():
     L.orc_stream_pos.restype = C.c_long
     L.orc_stream_pos.argtypes = [C.c_void_p]
     L.orc_stream_decode.argtypes = [C.c_void_p, _I32, C.c_int, _D, _D, _D]
+    L.orc_stream_decode_tap.argtypes = [C.c_void_p, _I32, C.c_int, _D, C.c_int, _D]
     L.orc_decode_batch.argtypes = [C.POINTER(C.c_void_p), C.c_int, _I32, _I32, _D]
     L.orc_snake.argtypes = [_D, _D, C.c_int, C.c_long, _D]
     L.orc_elu.argtypes = [_D, C.c_long, _D]
@@ -273,6 +274,35 @@ class Stream:
         if rc:
             raise ValueError(f"oracle: decode status {rc}")
         return (pcm, cu, cx) if capture else pcm
+
+    def decode_tap(self, codes: np.ndarray, tap: int):
+        """Decode like ``decode`` and also return one conv operand of the
+        decoder, [rows][C] time-major: tap 3 i is stage i's transposed-conv
+        input, 3 i + 1 + j the input of its residual unit j, 3 S the final
+        conv's input (S = number of stages)."""
+        codes = np.ascontiguousarray(codes, dtype=np.int32)
+        n = codes.shape[0]
+        pcm = np.empty(n * self.model.hop)
+        out = np.empty(tap_shape(self.model.cfg, tap, n))
+        rc = lib().orc_stream_decode_tap(self._h, codes.ctypes.data_as(_I32), n, _d(pcm), tap,
+                                         _d(out))
+        if rc:
+            raise ValueError(f"oracle: decode status {rc}")
+        return pcm, out
+
+
+def tap_shape(cfg: dict, tap: int, n: int) -> tuple[int, int]:
+    """(rows, channels) of decoder tap ``tap`` for n frames (see decode_tap)."""
+    S = len(cfg["strides"])
+    ch = [cfg["d_lat"]]
+    rate = [1]
+    for s in cfg["strides"]:
+        ch.append(ch[-1] // 2)
+        rate.append(rate[-1] * s)
+    if tap == 3 * S:
+        return n * rate[S], ch[S]
+    i, k = divmod(tap, 3)
+    return (n * rate[i], ch[i]) if k == 0 else (n * rate[i + 1], ch[i + 1])
 
 
 def weights_f64(weights: dict) -> dict:

@@ -604,9 +604,39 @@ static void tf_frame(orc_stream *s, const double *x, long pos, double *y)
  * cap_u [n][d_lat] the projected latent, cap_x [n][d_lat] the decoder
  * input (after the transformer, equal to cap_u without one).
  * Returns 0, -1 for a code outside [0, E), -2 for n < 0.
+ *
+ * orc_stream_decode_tap also copies out one conv operand of the decoder
+ * (the activated input a conv multiplies), time-major [rows][C], for
+ * layer-by-layer comparisons: tap 3 i is the transposed conv input of stage
+ * i, tap 3 i + 1 + j the input of residual unit j of stage i, tap 3 S the
+ * final conv input.  Taking a tap changes nothing in the decode.
  */
+static int stream_decode(orc_stream *s, const int32_t *codes, int n, double *pcm, double *cap_u,
+                         double *cap_x, int tap, double *cap_tap);
+
+static void tap_copy(const double *a, int C, long T, double *dst)
+{
+    for (long t = 0; t < T; t++)
+        for (int c = 0; c < C; c++)
+            dst[t * C + c] = a[(long)c * T + t];
+}
+
 int orc_stream_decode(orc_stream *s, const int32_t *codes, int n, double *pcm, double *cap_u,
                       double *cap_x)
+{
+    return stream_decode(s, codes, n, pcm, cap_u, cap_x, -1, NULL);
+}
+
+int orc_stream_decode_tap(orc_stream *s, const int32_t *codes, int n, double *pcm, int tap,
+                          double *cap_tap)
+{
+    if (tap < 0 || tap > 3 * s->m->cfg.n_stages || !cap_tap)
+        return -3;
+    return stream_decode(s, codes, n, pcm, NULL, NULL, tap, cap_tap);
+}
+
+static int stream_decode(orc_stream *s, const int32_t *codes, int n, double *pcm, double *cap_u,
+                         double *cap_x, int tap, double *cap_tap)
 {
     const orc_model *m = s->m;
     const orc_cfg *c = &m->cfg;
@@ -652,6 +682,8 @@ int orc_stream_decode(orc_stream *s, const int32_t *codes, int n, double *pcm, d
         int ci = m->ch[i], co = m->ch[i + 1], sd = c->strides[i];
         double *a = zalloc((long)ci * T);
         act_apply(m, x, st->alpha, ci, T, a);
+        if (tap == 3 * i)
+            tap_copy(a, ci, T, cap_tap);
         long T2 = T * sd;
         double *xt = zalloc((long)co * T2);
         convT_stream(s->h_T[i], a, ci, T, st->wT, st->bT, co, sd, xt);
@@ -664,6 +696,8 @@ int orc_stream_decode(orc_stream *s, const int32_t *codes, int n, double *pcm, d
             double *a1 = zalloc((long)co * T), *h7 = zalloc((long)co * T);
             double *a2 = zalloc((long)co * T), *h1 = zalloc((long)co * T);
             act_apply(m, x, r->a1, co, T, a1);
+            if (tap == 3 * i + 1 + j)
+                tap_copy(a1, co, T, cap_tap);
             conv_stream(s->h_ru[i][j], a1, co, T, r->w7, r->b7, co, 7, RU_DIL[j], h7);
             act_apply(m, h7, r->a2, co, T, a2);
             orc_causal_conv(a2, co, T, r->w1, r->b1, co, 1, 1, h1);
@@ -675,6 +709,8 @@ int orc_stream_decode(orc_stream *s, const int32_t *codes, int n, double *pcm, d
     int cs = m->ch[c->n_stages];
     double *a = zalloc((long)cs * T);
     act_apply(m, x, m->out_alpha, cs, T, a);
+    if (tap == 3 * c->n_stages)
+        tap_copy(a, cs, T, cap_tap);
     conv_stream(s->h_out, a, cs, T, m->out_w, m->out_b, 1, 7, 1, pcm);
     if (c->final_tanh)
         for (long e = 0; e < T; e++)

@@ -9,26 +9,37 @@ reaches the next threshold; the final chunk always decodes.  Thresholds grow
 by the chunk ramp (1, 2, 4 frames) and then by the steady stride (8).  The
 stateless variant re-decodes each chunk with up to 16 frames of left context,
 and the section lists the window lengths that occur.  A per-request initial
-chunk size is validated and clamped to the steady size (the section's
-``resolve_initial_codec_chunk_frames``).
+chunk size is validated and capped at the steady size.
 """
 from __future__ import annotations
 
+import operator
 
-def resolve_initial_chunk_frames(value, steady_chunk_frames: int, default_frames: int = 0) -> int:
-    """Per-request initial chunk size: None -> default; must be an integer
-    >= 0; the result is clamped to the steady size (which must be positive)."""
-    if steady_chunk_frames <= 0:
-        raise ValueError(f"steady_chunk_frames must be positive, got {steady_chunk_frames}")
-    if value is None:
-        value = default_frames
+
+def initial_chunk_size(requested, steady: int, fallback: int = 0) -> int:
+    """Size of a request's first decode, in frames.
+
+    A request may name its own first-chunk size; without one (``None``) the
+    server's ``fallback`` applies.  The size is a whole number of frames, at
+    least 0, and never larger than the steady chunk: a larger request is cut
+    down to ``steady``.  The steady chunk itself must be at least one frame.
+
+    Errors: ``ValueError`` for a steady size below 1 or a negative request;
+    ``TypeError`` for a request that is not an integer (``bool`` and
+    non-integral numbers included).
+    """
+    if steady < 1:
+        raise ValueError(f"steady chunk size {steady} is below one frame")
+    chosen = fallback if requested is None else requested
+    if isinstance(chosen, bool):
+        raise TypeError("a chunk size is a frame count, not a flag")
     try:
-        frames = int(value)
-    except (TypeError, ValueError) as exc:
-        raise TypeError("initial chunk frames must be an integer") from exc
+        frames = operator.index(chosen)
+    except TypeError:
+        raise TypeError(f"chunk size {chosen!r} is not an integer frame count") from None
     if frames < 0:
-        raise ValueError("initial chunk frames must be >= 0")
-    return min(frames, int(steady_chunk_frames))
+        raise ValueError(f"chunk size {frames} is negative")
+    return steady if frames > steady else frames
 
 
 def strides(ramp, steady: int, initial: int = 0):

@@ -172,11 +172,14 @@ def make_weights(cfg: dict, seed: int = SEED_W) -> "OrderedDict[str, np.ndarray]
     """Random-init parameters as float32 arrays holding their exact values.
 
     For bf16 configurations every value is rounded to bf16 (the stored value);
-    ``weight_bits`` gives the matching uint16 patterns.
+    ``weight_bits`` gives the matching uint16 patterns.  With
+    ``cfg["zero_bias"]`` every bias (names ending in ``.bias``) is zero
+    instead; all other parameters keep the values they have without it.
     """
+    zero_bias = bool(cfg.get("zero_bias", False))
     key = (cfg["K"], cfg["E"], cfg["d_cb"], cfg["d_lat"], tuple(cfg["strides"]),
            cfg["tf_layers"], cfg["tf_heads"], cfg["tf_head_dim"], cfg["tf_mlp"],
-           cfg["weight_dtype"], seed)
+           cfg["weight_dtype"], seed, zero_bias)
     if key in _WEIGHT_CACHE:
         return _WEIGHT_CACHE[key]
     rng = np.random.default_rng(seed)
@@ -190,6 +193,8 @@ def make_weights(cfg: dict, seed: int = SEED_W) -> "OrderedDict[str, np.ndarray]
             v = rng.normal(0.0, 0.02, size=shape).astype(np.float32)
         if cfg["weight_dtype"] == "bf16":
             v = bf16_to_f32(bf16_bits(v)).reshape(shape)
+        if zero_bias and name.endswith(".bias"):
+            v = np.zeros(shape, np.float32)
         out[name] = v
     _WEIGHT_CACHE[key] = out
     return out

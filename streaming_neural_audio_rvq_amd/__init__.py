@@ -9,6 +9,7 @@ loudly otherwise -- there is no fallback implementation.
 from __future__ import annotations
 
 import ctypes as C
+import operator
 import os
 
 import numpy as np
@@ -20,7 +21,7 @@ CODEC_OK, CODEC_EINVAL, CODEC_ESTREAM, CODEC_EDUP, CODEC_ERANGE = 0, 1, 2, 3, 4
 CODEC_ENOSLOT, CODEC_ETOOBIG, CODEC_ENOMEM, CODEC_EHIP = 5, 6, 7, 8
 DTYPE_F32, DTYPE_BF16, DTYPE_F16 = 0, 1, 2
 ACT = {"snake": 0, "elu": 1}
-CAPTURE_LATENT, CAPTURE_DEC_INPUT = 0, 1
+CAPTURE_LATENT, CAPTURE_DEC_INPUT, CAPTURE_LAYER0 = 0, 1, 2
 FLAG_PER_LAYER = 1
 FLAG_NO_SPLIT_K = 2
 FLAG_TWO_STAGE_BUFFERS = 4
@@ -57,7 +58,8 @@ class codec_info_t(C.Structure):
                 ("max_streams", C.c_int32), ("max_frames_per_call", C.c_int32),
                 ("open_streams", C.c_int32), ("compute_dtype", C.c_int32),
                 ("state_bytes_per_stream", C.c_int64), ("weight_bytes", C.c_int64),
-                ("workspace_bytes", C.c_int64)]
+                ("workspace_bytes", C.c_int64), ("graph_captures", C.c_int64),
+                ("graph_replays", C.c_int64)]
 
 
 _I32P = C.POINTER(C.c_int32)
@@ -68,7 +70,7 @@ EXPORTS = ["codec_open", "codec_close", "codec_info", "codec_last_error", "strea
            "decode_chunk_graph",
            "codec_device_status", "codec_debug_capture", "codec_debug_read_state",
            "codec_profile_enable", "codec_profile_read", "codec_chunk_plan",
-           "codec_resolve_initial_chunk_frames", "codec_debug_conv_plan"]
+           "codec_initial_chunk_size", "codec_debug_conv_plan"]
 
 
 def lib():
@@ -105,7 +107,7 @@ def lib():
                                      C.POINTER(C.c_int64), _I32P]
     L.codec_chunk_plan.argtypes = [C.c_int32, _I32P, C.c_int32, C.c_int32, C.c_int32, _I32P,
                                    C.c_int32, _I32P]
-    L.codec_resolve_initial_chunk_frames.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.c_int32,
+    L.codec_initial_chunk_size.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.c_int32,
                                                      _I32P]
     L.codec_debug_conv_plan.argtypes = [C.c_int32] * 7 + [C.POINTER(C.c_char_p), _I32P]
     _lib = L
@@ -244,8 +246,8 @@ class Codec:
                                   _stream_handle(stream)), self._h)
 
     def decode_chunk_graph(self, stream_ids, n_frames, codes, pcm, stream=None):
-        """decode_chunk replayed from a graph captured per chunk shape (B,
-        n_frames, pcm buffer); same arguments and results."""
+        """decode_chunk replayed from the graph of its (B, frame bucket); same
+        arguments, results within the parity bound."""
         ids = _i32(stream_ids)
         n = _i32(n_frames)
         codes = _i32(codes)
@@ -310,20 +312,23 @@ def chunk_plan(total: int, ramp=(1, 2, 4), steady: int = 8, initial: int = 0) ->
     return out[: n.value].tolist()
 
 
-def resolve_initial_chunk_frames(value, steady: int, default_frames: int = 0) -> int:
-    """Per-request initial chunk size: None -> default; clamped to steady.
-    Non-integers raise TypeError (marshalling), library errors ValueError."""
-    has = value is not None
-    if has:
-        try:
-            v = int(value)
-        except (TypeError, ValueError) as exc:
-            raise TypeError("initial chunk frames must be an integer") from exc
+def initial_chunk_size(requested, steady: int, fallback: int = 0) -> int:
+    """First-chunk size of a request in frames (``None``: the fallback), capped
+    at the steady chunk size; the library validates it.  A request that is
+    not an integer raises TypeError here (marshalling); the library's
+    rejections (steady below 1, a negative size) raise ValueError."""
+    if requested is None:
+        has, v = 0, 0
     else:
-        v = 0
+        if isinstance(requested, bool):
+            raise TypeError("a chunk size is a frame count, not a flag")
+        try:
+            v = operator.index(requested)
+        except TypeError:
+            raise TypeError(f"chunk size {requested!r} is not an integer frame count") from None
+        has = 1
     out = C.c_int32()
-    rc = lib().codec_resolve_initial_chunk_frames(v, int(has), int(steady), int(default_frames),
-                                                  C.byref(out))
+    rc = lib().codec_initial_chunk_size(int(v), has, int(steady), int(fallback), C.byref(out))
     if rc != CODEC_OK:
         raise ValueError(lib().codec_last_error(None).decode())
     return out.value

@@ -38,6 +38,8 @@ namespace {
 thread_local std::string g_err = "";
 
 constexpr long kSplitKCap = 16L << 20;  // split-K partials per codec: 64 MiB of fp32
+// A graph step of F frames runs with Fb - F < kGraphPadMax pad frames.
+constexpr int kGraphPadMax = 32;
 
 int set_err(std::string *dst, int code, const char *fmt, ...)
 {
@@ -112,6 +114,10 @@ struct codec {
     float *x = nullptr, *pcm_scratch = nullptr;
     float *splitk_ws = nullptr;  // split-K partial sums
     long splitk_cap = 0;         // floats
+    // buffers of the step being enqueued (the codec's own: above and meta_dev)
+    float *partial_now = nullptr;
+    long partial_cap_now = 0;
+    void *meta_now = nullptr;
 
     void *state = nullptr;
     int64_t slot_elems = 0;
@@ -127,19 +133,24 @@ struct codec {
     size_t meta_cap = 0;  // int32 elements
     unsigned long long *bad_codes = nullptr;  // device counter (device-resident codes)
     void *pinned[2]{};
-    // captured step graphs, keyed by (B, n[0..B), pcm address); two instances
-    // per key, each with its own pinned metadata buffer
+    // Step graphs (decode_chunk_graph), keyed by (streams in the graph, frames
+    // in the graph): a step of F frames runs as a graph of the next bucket of
+    // Fb >= F frames, the difference decoded by the pad stream (slot pad_slot,
+    // zero state, codes 0, its output discarded).  The graph holds kernels
+    // only; the metadata copy before it and the PCM copy after it are plain
+    // stream operations, so every graph shares the codec's buffers.
     struct GraphEntry {
-        hipGraphExec_t exec[2]{};
-        void *pinned[2]{};
-        hipEvent_t done[2]{};
-        int next = 0;
+        hipGraphExec_t exec = nullptr;
+        hipEvent_t done = nullptr;
         uint64_t last_use = 0;
     };
-    std::map<std::vector<int64_t>, GraphEntry> graphs;
+    std::map<std::pair<int, int>, GraphEntry> graphs;
     uint64_t graph_clock = 0;
+    int64_t graph_captures = 0, graph_replays = 0;
     bool capturing = false;
     hipStream_t cap_stream = nullptr;  // graphs are captured here, launched on the caller's
+    int pad_slot = 0;                  // state slot of the graph pad stream (max_streams)
+    int allocF = 0, allocB = 0;        // frames and streams the workspace holds
     hipEvent_t pin_ev[2]{};
     int pin_i = 0;
     StepMeta last_meta{};
@@ -464,8 +475,8 @@ int run_conv(codec *c, const char *name, const ConvArgs &a0, hipStream_t s, bool
     ConvArgs a = a0;
     a.splits_allowed = allow_split && !(c->cfg.flags & CODEC_FLAG_NO_SPLIT_K);
     a.deep_allowed = !(c->cfg.flags & CODEC_FLAG_TWO_STAGE_BUFFERS);
-    a.partial = c->splitk_ws;
-    const ConvPlan plan = conv_gemm_plan(a, c->dtype, c->n_cu, c->splitk_cap);
+    a.partial = c->partial_now;
+    const ConvPlan plan = conv_gemm_plan(a, c->dtype, c->n_cu, c->partial_cap_now);
     return timed(c, name, (int64_t)a.M, s,
                  [&] { return launch_conv_gemm(a, c->dtype, s, plan); });
 }
@@ -613,74 +624,103 @@ struct MetaLayout {
     StepMeta m{};
 };
 
+// Metadata layout of a step of B streams and F frames (int32 offsets).
+struct MetaOffsets {
+    size_t codes, fs, cu, slot, fresh, pos, tile[CODEC_MAX_STAGES], total;
+};
+MetaOffsets meta_offsets(const codec *c, int B, int F, bool codes_on_device)
+{
+    MetaOffsets o{};
+    const size_t ncodes = codes_on_device ? 0 : (size_t)F * c->cfg.K;
+    o.codes = 0;
+    o.fs = round4(o.codes + ncodes);
+    o.cu = round4(o.fs + F);
+    o.slot = round4(o.cu + B + 1);
+    o.fresh = round4(o.slot + B);
+    o.pos = round4(o.fresh + B);
+    o.total = round4(o.pos + B);
+    for (int i = 0; i < c->S; i++)
+        if (c->fuse_T[i]) {
+            o.tile[i] = o.total;
+            o.total = round4(o.total + B + 1);
+        }
+    return o;
+}
+
+// Fills the step metadata into host buffer hp (its device copy goes to
+// c->meta_now).  codes: host codes of the first code_frames frames (the rest,
+// pad frames, get code 0), or with codes_on_device the device array itself.
+// For a graph (tile_bound), the fused stages' tile counts in the launch
+// arguments are the most any step of this (B, F) can have; the kernels read
+// the step's own count from the metadata.
 MetaLayout fill_meta(codec *c, int32_t *hp, int B, const int *slots, const int32_t *n,
-                     const int32_t *codes, bool codes_on_device)
+                     const int32_t *codes, bool codes_on_device, int code_frames = -1,
+                     bool tile_bound = false)
 {
     const codec_cfg &g = c->cfg;
     int F = 0;
     for (int b = 0; b < B; b++)
         F += n[b];
-    size_t ncodes = codes_on_device ? 0 : (size_t)F * g.K;
-    size_t o_codes = 0, o_fs = round4(o_codes + ncodes), o_cu = round4(o_fs + F),
-           o_slot = round4(o_cu + B + 1), o_fresh = round4(o_slot + B),
-           o_pos = round4(o_fresh + B), o_tc = round4(o_pos + B);
-    size_t total = o_tc;
-    size_t o_tile[CODEC_MAX_STAGES]{};
-    for (int i = 0; i < c->S; i++)
-        if (c->fuse_T[i]) {
-            o_tile[i] = total;
-            total = round4(total + B + 1);
-        }
-    if (!codes_on_device)
-        memcpy(hp + o_codes, codes, sizeof(int32_t) * (size_t)F * g.K);
+    if (code_frames < 0)
+        code_frames = F;
+    const MetaOffsets o = meta_offsets(c, B, F, codes_on_device);
+    if (!codes_on_device) {
+        memcpy(hp + o.codes, codes, sizeof(int32_t) * (size_t)code_frames * g.K);
+        memset(hp + o.codes + (size_t)code_frames * g.K, 0,
+               sizeof(int32_t) * (size_t)(F - code_frames) * g.K);
+    }
     int acc = 0;
-    hp[o_cu] = 0;
+    hp[o.cu] = 0;
     for (int b = 0; b < B; b++) {
         for (int f = 0; f < n[b]; f++)
-            hp[o_fs + acc + f] = b;
+            hp[o.fs + acc + f] = b;
         acc += n[b];
-        hp[o_cu + b + 1] = acc;
-        hp[o_slot + b] = slots[b];
-        hp[o_fresh + b] = c->slot_fresh[slots[b]] ? 1 : 0;
-        hp[o_pos + b] = (int32_t)c->slot_pos[slots[b]];
+        hp[o.cu + b + 1] = acc;
+        hp[o.slot + b] = slots[b];
+        hp[o.fresh + b] = c->slot_fresh[slots[b]] ? 1 : 0;
+        hp[o.pos + b] = (int32_t)c->slot_pos[slots[b]];
     }
-    int32_t *dm = (int32_t *)c->meta_dev;
-    StepMeta m{codes_on_device ? (int32_t *)codes : dm + o_codes, dm + o_fs, dm + o_cu,
-               dm + o_slot, dm + o_fresh, dm + o_pos};
+    int32_t *dm = (int32_t *)c->meta_now;
+    StepMeta m{codes_on_device ? (int32_t *)codes : dm + o.codes, dm + o.fs, dm + o.cu,
+               dm + o.slot, dm + o.fresh, dm + o.pos};
     m.B = B;
     // fused stages: each stream's output rows in tiles of fuse_T rows, the last shorter
     for (int i = 0; i < c->S; i++) {
         if (!c->fuse_T[i])
             continue;
-        int32_t *tc = hp + o_tile[i];
+        int32_t *tc = hp + o.tile[i];
         tc[0] = 0;
         for (int b = 0; b < B; b++) {
             const int64_t rows = (int64_t)n[b] * c->rate[i + 1];
             tc[b + 1] = tc[b] + (int32_t)((rows + c->fuse_T[i] - 1) / c->fuse_T[i]);
         }
-        m.tile_cu[i] = dm + o_tile[i];
-        m.n_tiles[i] = tc[B];
+        m.tile_cu[i] = dm + o.tile[i];
+        m.n_tiles[i] = tile_bound ? (int)(((int64_t)F * c->rate[i + 1] + c->fuse_T[i] - 1) /
+                                              c->fuse_T[i] + B)
+                                  : tc[B];
     }
     MetaLayout out;
-    out.total = total;
+    out.total = o.total;
     out.m = m;
     return out;
 }
 
-// The step's device work on stream s: the metadata copy from hp, then every
-// kernel.  Only asynchronous calls, so that a graph can capture it.
-int enqueue_device(codec *c, int B, int F, const MetaLayout &ml, const int32_t *hp, float *pcm,
-                   hipStream_t s)
+// The step's metadata copy from hp on stream s.
+int enqueue_meta_copy(codec *c, const MetaLayout &ml, const int32_t *hp, hipStream_t s)
+{
+    return timed(c, "h2d_meta", (int64_t)ml.total * 4, s, [&] {
+        return hipMemcpyAsync(c->meta_now, hp, ml.total * 4, hipMemcpyHostToDevice, s);
+    });
+}
+
+// The step's kernels on stream s (reading the metadata already copied).
+// Only asynchronous calls and no memset nodes, so that a graph can capture it.
+int enqueue_kernels(codec *c, int B, int F, const MetaLayout &ml, float *pcm, hipStream_t s)
 {
     const codec_cfg &g = c->cfg;
     const StepMeta &m = ml.m;
-    int rc = timed(c, "h2d_meta", (int64_t)ml.total * 4, s, [&] {
-        return hipMemcpyAsync(c->meta_dev, hp, ml.total * 4, hipMemcpyHostToDevice, s);
-    });
-    if (rc)
-        return rc;
+    int rc = CODEC_OK;
 
-    // ---- device work ----
     // the gather and the halo fill of every layer share one launch
     rc = timed(c, "rvq_gather", F, s, [&] {
         return launch_rvq_gather_fill(c->cb, c->cb_dtype, m.codes, F, g.K, g.E, g.d_cb, c->z,
@@ -803,6 +843,17 @@ int enqueue_device(codec *c, int B, int F, const MetaLayout &ml, const int32_t *
     return CODEC_OK;
 }
 
+void graph_free(codec::GraphEntry &e)
+{
+    if (e.done)
+        (void)hipEventSynchronize(e.done);
+    if (e.exec)
+        (void)hipGraphExecDestroy(e.exec);
+    if (e.done)
+        (void)hipEventDestroy(e.done);
+    e = codec::GraphEntry{};
+}
+
 // Host bookkeeping of a step that has been enqueued.
 void step_done(codec *c, int B, const int *slots, const int32_t *n)
 {
@@ -824,10 +875,12 @@ int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int3
     HIPCHK(c, hipEventSynchronize(c->pin_ev[pi]));  // the copy that last read this buffer is done
     int32_t *hp = (int32_t *)c->pinned[pi];
     MetaLayout ml = fill_meta(c, hp, B, slots, n, codes, codes_on_device);
-    int rc = enqueue_device(c, B, F, ml, hp, pcm, s);
+    int rc = enqueue_meta_copy(c, ml, hp, s);
     if (rc)
         return rc;
     HIPCHK(c, hipEventRecord(c->pin_ev[pi], s));
+    if ((rc = enqueue_kernels(c, B, F, ml, pcm, s)))
+        return rc;
     step_done(c, B, slots, n);
     return CODEC_OK;
 }
@@ -883,7 +936,7 @@ int check_cfg(const codec_cfg *g, int *ch, int *hop)
     if (g->d_cb % gran)
         return set_err(nullptr, CODEC_EINVAL, "cfg: d_cb=%d is not a multiple of %d", g->d_cb,
                        gran);
-    if ((int64_t)g->max_frames_per_call * *hop >= (int64_t)1 << 31)
+    if ((int64_t)(g->max_frames_per_call + kGraphPadMax) * *hop >= (int64_t)1 << 31)
         return set_err(nullptr, CODEC_EINVAL, "cfg: max_frames_per_call * hop overflows int32");
     return CODEC_OK;
 }
@@ -954,6 +1007,54 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
             if (!known.count(weights[i].name))
                 return set_err(nullptr, CODEC_EINVAL, "weights: unknown parameter '%s'",
                                weights[i].name);
+    }
+
+    // bf16 weights run as fp16 MFMA operands: a weight beyond fp16's finite
+    // range, or codebook entries whose K-term sum could exceed it (the RVQ sum
+    // is stored in fp16), cannot be represented; reject them here
+    if (cfg->weight_dtype == CODEC_DTYPE_BF16) {
+        const float kF16Max = 65504.f;
+        auto bf16 = [](uint16_t b) {
+            uint32_t u = (uint32_t)b << 16;
+            float f;
+            memcpy(&f, &u, 4);
+            return f;
+        };
+        std::vector<float> cb_sum((size_t)cfg->d_cb, 0.f);
+        for (const ParamSpec &p : specs) {
+            const codec_tensor &t = weights[by_name[p.name]];
+            int64_t nel = 1;
+            for (auto v : p.shape)
+                nel *= v;
+            const uint16_t *b = (const uint16_t *)t.host_data;
+            const bool codebook = p.name.rfind("rvq.codebook.", 0) == 0;
+            const bool operand = p.name.size() > 7 &&
+                                 p.name.compare(p.name.size() - 7, 7, ".weight") == 0 &&
+                                 p.name.find(".ln") == std::string::npos;
+            if (codebook) {
+                std::vector<float> mx((size_t)cfg->d_cb, 0.f);
+                for (int64_t i = 0; i < nel; i++) {
+                    const float v = std::fabs(bf16(b[i]));
+                    float &m = mx[(size_t)(i % cfg->d_cb)];
+                    m = std::isnan(v) || v > m ? v : m;
+                }
+                for (int d = 0; d < cfg->d_cb; d++)
+                    cb_sum[(size_t)d] += mx[(size_t)d];
+            } else if (operand) {
+                for (int64_t i = 0; i < nel; i++)
+                    if (!(std::fabs(bf16(b[i])) <= kF16Max))
+                        return set_err(nullptr, CODEC_EINVAL,
+                                       "weights: '%s'[%lld] = %g is outside the fp16 range of "
+                                       "the compute operands (|w| <= 65504)",
+                                       p.name.c_str(), (long long)i, (double)bf16(b[i]));
+            }
+        }
+        for (int d = 0; d < cfg->d_cb; d++)
+            if (!(cb_sum[(size_t)d] <= kF16Max))
+                return set_err(nullptr, CODEC_EINVAL,
+                               "weights: codebook column %d can sum to %g over the %d codebooks, "
+                               "beyond the fp16 range of the stored RVQ sum (65504)",
+                               d, (double)cb_sum[(size_t)d], cfg->K);
     }
 
     int dev = 0;
@@ -1093,8 +1194,12 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
         return cleanup_fail(rc);
     c->out_b = W("dec.out.conv.bias")[0];
 
-    // ---- workspace for max_frames_per_call frames of max_streams streams ----
-    const size_t F = (size_t)c->maxF, B = (size_t)c->maxB, es = (size_t)c->esz;
+    // ---- workspace for max_frames_per_call frames of max_streams streams,
+    // plus a graph step's pad frames and pad stream ----
+    c->allocF = c->maxF + kGraphPadMax;
+    c->allocB = c->maxB + 1;
+    c->pad_slot = c->maxB;
+    const size_t F = (size_t)c->allocF, B = (size_t)c->allocB, es = (size_t)c->esz;
     int64_t *ws = &c->workspace_bytes;
     if ((rc = dev_alloc(c, &c->z, F * g.d_cb * es, ws)))
         return cleanup_fail(rc);
@@ -1182,7 +1287,7 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
         if (!skip)
             sv.l[sv.n++] = t.l[k];
     }
-    if ((rc = dev_alloc(c, &c->state, (size_t)c->maxB * off * es, ws)))
+    if ((rc = dev_alloc(c, &c->state, (size_t)c->allocB * off * es, ws)))
         return cleanup_fail(rc);
 
     // ---- step metadata: device buffer + two pinned staging buffers ----
@@ -1207,8 +1312,11 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
         }
     }
 
-    c->slot_pos.assign(c->maxB, 0);
-    c->slot_fresh.assign(c->maxB, 1);
+    c->slot_pos.assign(c->allocB, 0);
+    c->slot_fresh.assign(c->allocB, 1);
+    c->partial_now = c->splitk_ws;
+    c->partial_cap_now = c->splitk_cap;
+    c->meta_now = c->meta_dev;
     for (int i = c->maxB - 1; i >= 0; i--)
         c->free_slots.push_back(i);
     *out = c;
@@ -1235,14 +1343,7 @@ int codec_close(codec_t *c)
     if (c->cap_stream)
         (void)hipStreamDestroy(c->cap_stream);
     for (auto &kv : c->graphs)
-        for (int i = 0; i < 2; i++) {
-            if (kv.second.exec[i])
-                (void)hipGraphExecDestroy(kv.second.exec[i]);
-            if (kv.second.done[i])
-                (void)hipEventDestroy(kv.second.done[i]);
-            if (kv.second.pinned[i])
-                (void)hipHostFree(kv.second.pinned[i]);
-        }
+        graph_free(kv.second);
     for (void *p : c->allocs)
         (void)hipFree(p);
     delete c;
@@ -1268,6 +1369,8 @@ int codec_info(const codec_t *c, codec_info_t *o)
         (c->cfg.tf_layers ? (int64_t)2 * c->cfg.tf_layers * (c->cfg.tf_window - 1) * c->dm * 4 : 0);
     o->weight_bytes = c->weight_bytes;
     o->workspace_bytes = c->workspace_bytes;
+    o->graph_captures = c->graph_captures;
+    o->graph_replays = c->graph_replays;
     return CODEC_OK;
 }
 
@@ -1389,19 +1492,17 @@ int decode_chunk_device(codec_t *c, int32_t B, const int32_t *ids, const int32_t
 
 #define SNRVQ_MAX_GRAPHS 64
 
-static void graph_free(codec *c, codec::GraphEntry &e)
+// Frames a graph step of F frames is captured for: the next power of two up
+// to kGraphPadMax frames, then the next multiple of kGraphPadMax.
+static int graph_bucket(int F)
 {
-    for (int i = 0; i < 2; i++) {
-        if (e.done[i])
-            (void)hipEventSynchronize(e.done[i]);
-        if (e.exec[i])
-            (void)hipGraphExecDestroy(e.exec[i]);
-        if (e.done[i])
-            (void)hipEventDestroy(e.done[i]);
-        if (e.pinned[i])
-            (void)hipHostFree(e.pinned[i]);
+    if (F <= kGraphPadMax) {
+        int b = 1;
+        while (b < F)
+            b <<= 1;
+        return b;
     }
-    (void)c;
+    return (F + kGraphPadMax - 1) / kGraphPadMax * kGraphPadMax;
 }
 
 int decode_chunk_graph(codec_t *c, int32_t B, const int32_t *ids, const int32_t *n,
@@ -1417,41 +1518,51 @@ int decode_chunk_graph(codec_t *c, int32_t B, const int32_t *ids, const int32_t 
     HIPCHK(c, hipSetDevice(c->dev));
     hipStream_t s = (hipStream_t)stream;
     int F = 0;
-    std::vector<int64_t> key;
-    key.reserve((size_t)B + 2);
-    key.push_back(B);
-    for (int b = 0; b < B; b++) {
-        key.push_back(n[b]);
+    for (int b = 0; b < B; b++)
         F += n[b];
+    // the graph's streams: the caller's, then the pad stream if the bucket
+    // has frames to spare (fresh every step: zero state, position 0)
+    const int Fb = graph_bucket(F), pad = Fb - F;
+    std::vector<int> gslots(slots);
+    std::vector<int32_t> gn(n, n + B);
+    if (pad > 0) {
+        gslots.push_back(c->pad_slot);
+        gn.push_back(pad);
+        c->slot_fresh[c->pad_slot] = 1;
+        c->slot_pos[c->pad_slot] = 0;
     }
-    key.push_back((int64_t)(uintptr_t)pcm);
+    const int Bt = (int)gslots.size();
+    const std::pair<int, int> key{Bt, Fb};
     auto it = c->graphs.find(key);
     if (it == c->graphs.end()) {
-        if (c->graphs.size() >= SNRVQ_MAX_GRAPHS) {  // evict the least recently used shape
+        if (c->graphs.size() >= SNRVQ_MAX_GRAPHS) {  // evict the least recently used
             auto lru = c->graphs.begin();
             for (auto jt = c->graphs.begin(); jt != c->graphs.end(); ++jt)
                 if (jt->second.last_use < lru->second.last_use)
                     lru = jt;
-            graph_free(c, lru->second);
+            graph_free(lru->second);
             c->graphs.erase(lru);
         }
         it = c->graphs.emplace(key, codec::GraphEntry{}).first;
     }
     codec::GraphEntry &e = it->second;
     e.last_use = ++c->graph_clock;
-    const int inst = e.next;
-    e.next ^= 1;
-    if (!e.pinned[inst]) {
-        HIPCHK(c, hipHostMalloc(&e.pinned[inst], c->meta_cap * 4, hipHostMallocDefault));
-        HIPCHK(c, hipEventCreateWithFlags(&e.done[inst], hipEventDisableTiming));
-    } else {
-        HIPCHK(c, hipEventSynchronize(e.done[inst]));  // its last replay read the buffer
-    }
-    int32_t *hp = (int32_t *)e.pinned[inst];
-    MetaLayout ml = fill_meta(c, hp, B, slots.data(), n, codes, false);
-    if (!e.exec[inst]) {
+
+    // metadata through the codec's pinned ring, as for an eager step
+    const int pi = c->pin_i;
+    c->pin_i ^= 1;
+    HIPCHK(c, hipEventSynchronize(c->pin_ev[pi]));
+    int32_t *hp = (int32_t *)c->pinned[pi];
+    MetaLayout ml = fill_meta(c, hp, Bt, gslots.data(), gn.data(), codes, false, F, true);
+    if ((rc = enqueue_meta_copy(c, ml, hp, s)))
+        return rc;
+    HIPCHK(c, hipEventRecord(c->pin_ev[pi], s));
+
+    if (!e.exec) {
         // capture on the codec's own stream (the caller's may be the null
-        // stream, which cannot be captured); nothing runs during capture
+        // stream, which cannot be captured); nothing runs during capture.
+        // The PCM goes to the codec's buffer, so the graph does not depend
+        // on the caller's pcm address.
         if (!c->cap_stream)
             HIPCHK(c, hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking));
         hipGraph_t graph = nullptr;
@@ -1462,7 +1573,7 @@ int decode_chunk_graph(codec_t *c, int32_t B, const int32_t *ids, const int32_t 
             return fail(c, CODEC_EHIP, "decode_chunk_graph: capture failed: %s",
                         hipGetErrorString(ce));
         }
-        rc = enqueue_device(c, B, F, ml, hp, pcm, c->cap_stream);
+        rc = enqueue_kernels(c, Bt, Fb, ml, c->pcm_scratch, c->cap_stream);
         ce = hipStreamEndCapture(c->cap_stream, &graph);
         c->capturing = false;
         if (rc) {
@@ -1473,17 +1584,26 @@ int decode_chunk_graph(codec_t *c, int32_t B, const int32_t *ids, const int32_t 
         if (ce != hipSuccess)
             return fail(c, CODEC_EHIP, "decode_chunk_graph: capture failed: %s",
                         hipGetErrorString(ce));
-        ce = hipGraphInstantiate(&e.exec[inst], graph, nullptr, nullptr, 0);
+        ce = hipGraphInstantiate(&e.exec, graph, nullptr, nullptr, 0);
         (void)hipGraphDestroy(graph);
         if (ce != hipSuccess) {
-            e.exec[inst] = nullptr;
+            e.exec = nullptr;
             return fail(c, CODEC_EHIP, "decode_chunk_graph: instantiate failed: %s",
                         hipGetErrorString(ce));
         }
+        HIPCHK(c, hipEventCreateWithFlags(&e.done, hipEventDisableTiming));
+        c->graph_captures++;
+    } else {
+        c->graph_replays++;
     }
-    HIPCHK(c, hipGraphLaunch(e.exec[inst], s));
-    HIPCHK(c, hipEventRecord(e.done[inst], s));
+    HIPCHK(c, hipGraphLaunch(e.exec, s));
+    HIPCHK(c, hipEventRecord(e.done, s));
+    HIPCHK(c, hipMemcpyAsync(pcm, c->pcm_scratch, sizeof(float) * (size_t)F * c->hop,
+                             hipMemcpyDeviceToDevice, s));
     step_done(c, B, slots.data(), n);
+    c->last_meta = ml.m;  // the caller's streams are the first B of the graph's
+    c->lastF = F;
+    c->lastB = B;
     return CODEC_OK;
 }
 
@@ -1533,19 +1653,55 @@ int codec_debug_capture(codec_t *c, int32_t what, float *dst, int64_t capacity,
 {
     if (!c || !dst)
         return set_err(c ? &c->err : nullptr, CODEC_EINVAL, "codec_debug_capture: NULL argument");
-    if (what != CODEC_CAPTURE_LATENT && what != CODEC_CAPTURE_DEC_INPUT)
-        return fail(c, CODEC_EINVAL, "codec_debug_capture: what=%d", what);
     if (c->lastF == 0)
         return fail(c, CODEC_EINVAL, "codec_debug_capture: no decode step yet");
-    int64_t need = (int64_t)c->lastF * c->cfg.d_lat;
+    const void *ext = nullptr;
+    int H = 0, C = 0, rate = 1;
+    bool materialized = true;
+    if (what == CODEC_CAPTURE_LATENT || what == CODEC_CAPTURE_DEC_INPUT) {
+        const bool tf_latent = what == CODEC_CAPTURE_LATENT && c->cfg.tf_layers > 0;
+        ext = tf_latent ? c->u16 : c->u_ext;
+        H = tf_latent ? 0 : 6;
+        C = c->cfg.d_lat;
+    } else if (what >= CODEC_CAPTURE_LAYER0 && what <= CODEC_CAPTURE_LAYER0 + 3 * c->S) {
+        const int t = what - CODEC_CAPTURE_LAYER0, i = t / 3, k = t % 3;
+        if (t == 3 * c->S) {  // the final conv's input
+            ext = c->a_outb;
+            H = 6;
+            C = c->ch[c->S];
+            rate = c->hop;
+            materialized = !c->fuse_T[c->S - 1];
+        } else if (k == 0) {  // stage i's transposed-conv input (written by every path)
+            ext = c->aT[i];
+            H = 1;
+            C = c->ch[i];
+            rate = c->rate[i];
+        } else {  // residual unit k - 1 of stage i
+            ext = k == 1 ? c->a1[i] : c->a2[i];
+            H = k == 1 ? 6 : 18;
+            C = c->ch[i + 1];
+            rate = c->rate[i + 1];
+            materialized = !c->fuse_T[i];
+        }
+    } else {
+        return fail(c, CODEC_EINVAL, "codec_debug_capture: what=%d (0..%d)", what,
+                    CODEC_CAPTURE_LAYER0 + 3 * c->S);
+    }
+    if (!materialized)
+        return fail(c, CODEC_EINVAL,
+                    "codec_debug_capture: layer %d runs inside a fused stage kernel and is never "
+                    "stored; open the codec with CODEC_FLAG_PER_LAYER to capture it",
+                    what);
+    const int64_t need = (int64_t)c->lastF * rate * C;
     if (capacity < need)
         return fail(c, CODEC_EINVAL, "codec_debug_capture: capacity %lld < %lld",
                     (long long)capacity, (long long)need);
+    if (c->lastF > c->allocF || c->lastB > c->allocB)  // the workspace holds the step
+        return fail(c, CODEC_EINVAL, "codec_debug_capture: step of %d frames, %d streams",
+                    c->lastF, c->lastB);
     HIPCHK(c, hipSetDevice(c->dev));
-    const bool tf_latent = what == CODEC_CAPTURE_LATENT && c->cfg.tf_layers > 0;
-    HIPCHK(c, launch_unextend(tf_latent ? c->u16 : c->u_ext, c->dtype, tf_latent ? 0 : 6,
-                              c->cfg.d_lat, 1, c->last_meta.frame_stream, c->lastF, dst,
-                              (hipStream_t)stream));
+    HIPCHK(c, launch_unextend(ext, c->dtype, H, C, rate, c->last_meta.frame_stream,
+                              c->lastF * rate, dst, (hipStream_t)stream));
     return CODEC_OK;
 }
 
@@ -1683,19 +1839,17 @@ int codec_debug_conv_plan(int32_t M, int32_t N, int32_t Cin, int32_t taps, int32
     return CODEC_OK;
 }
 
-int codec_resolve_initial_chunk_frames(int64_t value, int32_t has_value, int32_t steady,
-                                       int32_t default_frames, int32_t *out)
+int codec_initial_chunk_size(int64_t requested, int32_t has_request, int32_t steady,
+                             int32_t fallback, int32_t *out)
 {
     if (!out)
-        return set_err(nullptr, CODEC_EINVAL, "codec_resolve_initial_chunk_frames: NULL out");
-    if (steady <= 0)
-        return set_err(nullptr, CODEC_EINVAL, "steady_chunk_frames must be positive, got %d",
-                       steady);
-    int64_t v = has_value ? value : default_frames;
-    if (v < 0)
-        return set_err(nullptr, CODEC_EINVAL, "initial chunk frames must be >= 0, got %lld",
-                       (long long)v);
-    *out = (int32_t)std::min<int64_t>(v, steady);
+        return set_err(nullptr, CODEC_EINVAL, "codec_initial_chunk_size: NULL out");
+    if (steady < 1)
+        return set_err(nullptr, CODEC_EINVAL, "steady chunk size %d is below one frame", steady);
+    const int64_t frames = has_request ? requested : (int64_t)fallback;
+    if (frames < 0)
+        return set_err(nullptr, CODEC_EINVAL, "chunk size %lld is negative", (long long)frames);
+    *out = frames > steady ? steady : (int32_t)frames;
     return CODEC_OK;
 }
 

@@ -38,7 +38,7 @@ __device__ __forceinline__ float snrvq_snake(float v, float alpha_rev, float inv
     const float s2 = s * s;
     return __builtin_fmaf(s2, inv_alpha, v);
 }
-__device__ __forceinline__ float snrvq_elu(float v) { return v > 0.f ? v : __expf(v) - 1.f; }
+__device__ __forceinline__ float snrvq_elu(float v) { return v > 0.f ? v : expm1f(v); }
 
 // fp32 -> fp16 (round to nearest even) of a materialized fp32 value.  The
 // empty asm keeps the compiler from folding the conversion into the FMA that

@@ -538,16 +538,21 @@ def test_stateless_window_redecode_matches_stateful_c2():
 # --------------------------------------------------------------------------
 # Graph replay (one launch per step for a repeated chunk shape)
 # --------------------------------------------------------------------------
-def test_graph_replay_bitwise_equals_eager():
-    """decode_chunk_graph captures a step per chunk shape and replays it with
-    new codes and state; every replay must equal the eager decode_chunk of the
-    same step bit for bit.  Replays are interleaved with eager work and host
-    synchronisations, shapes change and come back (capture, cache hit)."""
+def test_graph_replay_vs_eager_and_oracle():
+    """decode_chunk_graph runs each step as the graph of its frame bucket
+    (next power of two up to 32 frames), the spare frames on a pad stream.
+    Replays are interleaved with eager decode_chunk steps of the same codes
+    and with host synchronisations; bucket shapes change and come back.  A
+    step whose frame count is a bucket size runs the eager launch sequence
+    exactly: bit for bit the eager PCM.  A padded step may split K
+    differently: within the bound of the eager PCM.  Every graph stream
+    against the oracle's whole-utterance decode."""
     cfg = RI.get_config("c2")
-    c = open_codec(cfg)
+    w = RI.make_weights(cfg)
+    c = open_codec(cfg, w)
     H = c.hop
     B = 4
-    plan = [1, 2, 4, 8, 8, 8, 8, 3, 8, 8, 2, 8, 8]
+    plan = [1, 2, 4, 8, 8, 8, 8, 3, 8, 8, 2, 8, 8, 5, 3]
     T = sum(plan)
     codes = [RI.stream_codes(cfg, b, T, part=7) for b in range(B)]
     ids_g = [c.stream_open() for _ in range(B)]
@@ -555,6 +560,7 @@ def test_graph_replay_bitwise_equals_eager():
     pcm_g = torch.empty(max(plan) * B * H, dtype=torch.float32, device="cuda")
     at = 0
     say("case graph replay: plan", plan)
+    graph_out = [[] for _ in range(B)]
     for k, n in enumerate(plan):
         packed = np.concatenate([cb[at:at + n] for cb in codes])
         c.decode_chunk_graph(ids_g, [n] * B, packed, pcm_g)
@@ -563,8 +569,28 @@ def test_graph_replay_bitwise_equals_eager():
         pcm_e = torch.empty(n * B * H, dtype=torch.float32, device="cuda")
         c.decode_chunk(ids_e, [n] * B, packed, pcm_e)
         ref = pcm_e.cpu().numpy()
-        assert np.array_equal(got, ref), f"step {k} (n={n}): graph replay differs from eager"
+        F = n * B
+        exact = F & (F - 1) == 0  # a bucket size: no pad stream
+        if exact:
+            assert np.array_equal(got, ref), f"step {k} (n={n}): graph differs from eager"
+        for b in range(B):
+            e, _ = rel_err(got[b * n * H:(b + 1) * n * H], ref[b * n * H:(b + 1) * n * H].astype(np.float64))
+            assert e <= tol_for(cfg), f"step {k} stream {b}: graph vs eager {e:.3e}"
+            graph_out[b].append(got[b * n * H:(b + 1) * n * H])
         at += n
+    info = c.get_info()
+    say(f"graphs captured {info.graph_captures}, replays {info.graph_replays}")
+    keys = set()
+    for n in plan:  # (streams incl. the pad stream, bucket frames)
+        F = n * B
+        Fb = 1 << (F - 1).bit_length() if F <= 32 else (F + 31) // 32 * 32
+        keys.add((B + (Fb > F), Fb))
+    assert info.graph_captures == len(keys) and info.graph_replays == len(plan) - len(keys)
+    m = oracle.Model(cfg, w)
+    for b in range(B):
+        e, ac = rel_err(np.concatenate(graph_out[b]), m.decode_full(codes[b]))
+        say(f"graph stream {b} vs oracle: err/peak {e:.3e} AC-rel {ac:.3e}")
+        assert e <= tol_for(cfg)
     c.close()
 
 

@@ -51,17 +51,18 @@ def test_chunk_plan_matches_oracle_policy():
             policy.chunk_plan(total, ramp, steady, initial), (total, ramp, steady, initial)
 
 
-def test_resolve_initial_chunk_frames():
-    assert snr.resolve_initial_chunk_frames(None, 8) == 0
-    assert snr.resolve_initial_chunk_frames(None, 8, 3) == 3
-    assert snr.resolve_initial_chunk_frames("5", 8) == 5
-    assert snr.resolve_initial_chunk_frames(40, 8) == 8
-    with pytest.raises(ValueError):
-        snr.resolve_initial_chunk_frames(3, 0)
-    with pytest.raises(TypeError):
-        snr.resolve_initial_chunk_frames("abc", 8)
-    with pytest.raises(ValueError):
-        snr.resolve_initial_chunk_frames(-1, 8)
+def test_initial_chunk_size_matches_oracle_policy():
+    cases = [(None, 8, 0), (None, 8, 3), (5, 8, 0), (40, 8, 0), (0, 8, 0), (8, 8, 1),
+             (np.int32(7), 4, 0), (3, 1, 0)]
+    for req, steady, fb in cases:
+        assert snr.initial_chunk_size(req, steady, fb) == \
+            policy.initial_chunk_size(req, steady, fb), (req, steady, fb)
+    for req, steady, fb in [(3, 0, 0), (-1, 8, 0), (None, 8, -1)]:
+        with pytest.raises(ValueError):
+            snr.initial_chunk_size(req, steady, fb)
+    for bad in ("5", 2.5, True):
+        with pytest.raises(TypeError):
+            snr.initial_chunk_size(bad, 8)
 
 
 def _bits(cfg, w):

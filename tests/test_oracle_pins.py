@@ -204,9 +204,13 @@ def test_rvq_rejects_out_of_range_code():
 # --------------------------------------------------------------------------
 # Whole decoder on the tiny configuration: independent torch composition
 # --------------------------------------------------------------------------
-def torch_decode_full(cfg, w, codes):
+def torch_decode_full(cfg, w, codes, taps=None):
     """Whole-utterance decode of the network, composed from torch fp64 library
-    ops (conv1d / conv_transpose1d with explicit causal padding)."""
+    ops (conv1d / conv_transpose1d with explicit causal padding).  ``taps``,
+    a dict, receives every conv operand [rows, C] keyed like the oracle's
+    decode_tap (3 i: stage i's transposed-conv input; 3 i + 1 + j: its
+    residual unit j's input; 3 S: the final conv's input)."""
+    taps = {} if taps is None else taps
     T = codes.shape[0]
     W = {k: t64(v) for k, v in w.items()}
     z = sum(W[f"rvq.codebook.{k}"][torch.from_numpy(codes[:, k].astype(np.int64))]
@@ -228,14 +232,19 @@ def torch_decode_full(cfg, w, codes):
     for i, s in enumerate(cfg["strides"]):
         p = f"dec.stage.{i}."
         n = x.shape[-1]
-        x = F.conv_transpose1d(act(x, W[p + "snake.alpha"]), W[p + "convT.weight"],
-                               W[p + "convT.bias"], stride=s)[..., : n * s]
+        a = act(x, W[p + "snake.alpha"])
+        taps[3 * i] = a[0].T.numpy()
+        x = F.conv_transpose1d(a, W[p + "convT.weight"], W[p + "convT.bias"], stride=s)[..., : n * s]
         for j, d in enumerate((1, 3)):
             q = p + f"ru.{j}."
-            h = cconv(act(x, W[q + "snake1.alpha"]), W[q + "conv7.weight"], W[q + "conv7.bias"], d)
+            a = act(x, W[q + "snake1.alpha"])
+            taps[3 * i + 1 + j] = a[0].T.numpy()
+            h = cconv(a, W[q + "conv7.weight"], W[q + "conv7.bias"], d)
             h = F.conv1d(act(h, W[q + "snake2.alpha"]), W[q + "conv1.weight"], W[q + "conv1.bias"])
             x = x + h
-    y = cconv(act(x, W["dec.out.snake.alpha"]), W["dec.out.conv.weight"], W["dec.out.conv.bias"], 1)
+    a = act(x, W["dec.out.snake.alpha"])
+    taps[3 * len(cfg["strides"])] = a[0].T.numpy()
+    y = cconv(a, W["dec.out.conv.weight"], W["dec.out.conv.bias"], 1)
     return y[0, 0].numpy()
 
 
@@ -249,6 +258,51 @@ def test_whole_decoder_c1_matches_torch_composition(act):
     ref = torch_decode_full(cfg, w, codes)
     assert pcm.shape == (cfg["n_frames"] * RI.hop(cfg),)
     np.testing.assert_allclose(pcm, ref, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("act", ["snake", "elu"])
+def test_decoder_taps_match_torch_composition(act):
+    """Every conv operand the oracle can hand out (its layer taps) equals the
+    torch composition's at the same point, and taking a tap leaves the PCM
+    bit for bit unchanged; a streamed decode's taps concatenate to the whole
+    decode's."""
+    cfg = RI.get_config("c1", act=act)
+    w = RI.make_weights(cfg)
+    T = 20
+    codes = RI.stream_codes(cfg, 2, T)
+    m = oracle.Model(cfg, w)
+    ref_taps = {}
+    ref = torch_decode_full(cfg, w, codes, ref_taps)
+    full = m.decode_full(codes)
+    S = len(cfg["strides"])
+    assert sorted(ref_taps) == list(range(3 * S + 1))
+    for tap, want in ref_taps.items():
+        pcm, got = m.stream().decode_tap(codes, tap)
+        assert got.shape == want.shape == oracle.tap_shape(cfg, tap, T)
+        assert np.array_equal(pcm, full)
+        np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+        s = m.stream()
+        parts = [s.decode_tap(codes[a:b], tap)[1] for a, b in ((0, 3), (3, 4), (4, T))]
+        assert np.array_equal(np.concatenate(parts), got)
+    np.testing.assert_allclose(full, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_final_tanh_is_tanh_of_raw_output():
+    """The optional output tanh (off in every workload) maps each raw PCM
+    sample through tanh and nothing else: against numpy's tanh of the raw
+    decode, including a decode whose raw samples reach |x| > 1 (scaled output
+    conv) so that the saturation is exercised."""
+    for scale in (1.0, 1000.0):
+        cfg = RI.get_config("c1")
+        w = dict(RI.make_weights(cfg))
+        w["dec.out.conv.weight"] = w["dec.out.conv.weight"] * np.float32(scale)
+        codes = RI.stream_codes(cfg, 4, 12)
+        raw = oracle.Model(cfg, w).decode_full(codes)
+        sq = oracle.Model(dict(cfg, final_tanh=True), w).decode_full(codes)
+        if scale > 1:
+            assert np.max(np.abs(raw)) > 1.5
+        np.testing.assert_allclose(sq, np.tanh(raw), rtol=4e-16, atol=1e-300)
+        assert not np.array_equal(sq, raw)
 
 
 # --------------------------------------------------------------------------

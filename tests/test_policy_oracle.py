@@ -2,6 +2,7 @@
 import json
 import os
 
+import numpy as np
 import pytest
 
 from oracle import policy
@@ -40,14 +41,21 @@ def test_ramp_entries_clamped_to_steady_and_override():
     assert policy.chunk_plan(20, (1, 2, 4), 8, initial=50) == [8, 2, 4, 6]
 
 
-def test_resolve_initial_chunk_frames():
-    assert policy.resolve_initial_chunk_frames(None, 8) == 0
-    assert policy.resolve_initial_chunk_frames(None, 8, default_frames=3) == 3
-    assert policy.resolve_initial_chunk_frames("5", 8) == 5
-    assert policy.resolve_initial_chunk_frames(40, 8) == 8
+def test_initial_chunk_size():
+    # no request: the fallback; requests above the steady size are capped
+    assert policy.initial_chunk_size(None, 8) == 0
+    assert policy.initial_chunk_size(None, 8, fallback=3) == 3
+    assert policy.initial_chunk_size(5, 8) == 5
+    assert policy.initial_chunk_size(np.int64(6), 8) == 6
+    assert policy.initial_chunk_size(0, 8) == 0
+    assert policy.initial_chunk_size(40, 8) == 8
+    assert policy.initial_chunk_size(8, 8) == 8
     with pytest.raises(ValueError):
-        policy.resolve_initial_chunk_frames(3, 0)
-    with pytest.raises(TypeError):
-        policy.resolve_initial_chunk_frames("abc", 8)
+        policy.initial_chunk_size(3, 0)
     with pytest.raises(ValueError):
-        policy.resolve_initial_chunk_frames(-1, 8)
+        policy.initial_chunk_size(-1, 8)
+    with pytest.raises(ValueError):
+        policy.initial_chunk_size(None, 8, fallback=-2)
+    for bad in ("5", 2.5, True, [1]):
+        with pytest.raises(TypeError):
+            policy.initial_chunk_size(bad, 8)
