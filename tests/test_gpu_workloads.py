@@ -415,15 +415,17 @@ def test_decode_beside_gemm_load(mode):
                     torch.matmul(a, bm)
         outs = [[] for _ in range(B)]
         at = 0
-        for n in plan:
-            packed = np.concatenate([cd[at:at + n] for cd in codes])
-            pcm = torch.empty(B * n * codec.hop, dtype=torch.float32, device="cuda")
-            codec.decode_chunk(ids, [n] * B, packed, pcm, stream=dec)
-            dec.synchronize()
-            host = pcm.cpu().numpy()
-            for b in range(B):
-                outs[b].append(host[b * n * codec.hop:(b + 1) * n * codec.hop])
-            at += n
+        # everything on the decode stream: a copy on the null stream would
+        # wait for the load (CU-masked streams are blocking streams)
+        with torch.cuda.stream(dec):
+            for n in plan:
+                packed = np.concatenate([cd[at:at + n] for cd in codes])
+                pcm = torch.empty(B * n * codec.hop, dtype=torch.float32, device="cuda")
+                codec.decode_chunk(ids, [n] * B, packed, pcm, stream=dec)
+                host = pcm.cpu().numpy()
+                for b in range(B):
+                    outs[b].append(host[b * n * codec.hop:(b + 1) * n * codec.hop])
+                at += n
         busy = not load.query()
         torch.cuda.synchronize()
         for i in ids:
