@@ -214,6 +214,24 @@ int decode_chunk_graph(codec_t *codec, int32_t B, const int32_t *stream_ids,
                        const int32_t *n_frames, const int32_t *codes, float *pcm,
                        int64_t pcm_capacity, codec_hip_stream stream);
 
+/* For callers that cannot allocate memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): decode_chunk_device
+ * with the step's scratch -- its metadata and the split-K partial sums --
+ * taken from a static device array of 32 MiB per GPU (1 MiB of metadata,
+ * 31 MiB of partials) instead of the codec's buffers.  It allocates nothing,
+ * on the device, the host or pinned.  Weights, state slots and the
+ * activation workspace are the codec's, allocated by codec_open.  Arguments,
+ * checks and results are those of decode_chunk_device (within the parity
+ * bound: the smaller partial space can change a layer's K split), plus
+ * CODEC_ETOOBIG when the step's metadata exceeds the 1 MiB region (about
+ * 250,000 frames).  Every codec on a GPU shares that GPU's array, which
+ * keeps the last call's contents: calls that overlap on one GPU (different
+ * codecs or streams without ordering) race and give wrong results.
+ * codec_debug_capture after such a step reads the metadata in the array. */
+int decode_chunk_device_noalloc(codec_t *codec, int32_t B, const int32_t *stream_ids,
+                                const int32_t *n_frames, const int32_t *codes_dev, float *pcm,
+                                int64_t pcm_capacity, codec_hip_stream stream);
+
 /* Waits for the codec's device work and returns through *bad_codes the
  * number of out-of-range codes seen by decode_chunk_device since the last
  * call (then resets it).  CODEC_ERANGE when it is nonzero. */

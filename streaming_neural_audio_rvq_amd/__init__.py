@@ -67,7 +67,7 @@ _lib = None
 
 EXPORTS = ["codec_open", "codec_close", "codec_info", "codec_last_error", "stream_open",
            "stream_close", "stream_prefill", "decode_chunk", "decode_chunk_device",
-           "decode_chunk_graph",
+           "decode_chunk_graph", "decode_chunk_device_noalloc",
            "codec_device_status", "codec_debug_capture", "codec_debug_read_state",
            "codec_profile_enable", "codec_profile_read", "codec_chunk_plan",
            "codec_initial_chunk_size", "codec_debug_conv_plan"]
@@ -97,6 +97,8 @@ def lib():
                                       C.c_void_p, C.c_int64, C.c_void_p]
     L.decode_chunk_graph.argtypes = [C.c_void_p, C.c_int32, _I32P, _I32P, _I32P, C.c_void_p,
                                      C.c_int64, C.c_void_p]
+    L.decode_chunk_device_noalloc.argtypes = [C.c_void_p, C.c_int32, _I32P, _I32P, C.c_void_p,
+                                              C.c_void_p, C.c_int64, C.c_void_p]
     L.codec_device_status.argtypes = [C.c_void_p, C.POINTER(C.c_int64)]
     L.codec_debug_capture.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int64, C.c_void_p]
     L.codec_debug_read_state.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int64,
@@ -263,6 +265,16 @@ class Codec:
                                          C.c_void_p(codes_dev.data_ptr()),
                                          C.c_void_p(pcm.data_ptr()), pcm.numel(),
                                          _stream_handle(stream)), self._h)
+
+    def decode_chunk_device_noalloc(self, stream_ids, n_frames, codes_dev, pcm, stream=None):
+        """decode_chunk_device with its scratch in the library's static device
+        array (allocates nothing)."""
+        ids = _i32(stream_ids)
+        n = _i32(n_frames)
+        _check(lib().decode_chunk_device_noalloc(self._h, len(ids), _ptr(ids), _ptr(n),
+                                                 C.c_void_p(codes_dev.data_ptr()),
+                                                 C.c_void_p(pcm.data_ptr()), pcm.numel(),
+                                                 _stream_handle(stream)), self._h)
 
     def device_status(self) -> int:
         """Number of out-of-range device-resident codes since the last call

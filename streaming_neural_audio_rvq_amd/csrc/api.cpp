@@ -23,6 +23,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <unordered_map>
 #include <unordered_set>
@@ -114,7 +115,8 @@ struct codec {
     float *x = nullptr, *pcm_scratch = nullptr;
     float *splitk_ws = nullptr;  // split-K partial sums
     long splitk_cap = 0;         // floats
-    // buffers of the step being enqueued (the codec's own: above and meta_dev)
+    // buffers of the step being enqueued: the codec's own (above and
+    // meta_dev), or the no-allocation entry point's static scratch
     float *partial_now = nullptr;
     long partial_cap_now = 0;
     void *meta_now = nullptr;
@@ -885,6 +887,42 @@ int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int3
     return CODEC_OK;
 }
 
+// ---- static scratch of decode_chunk_device_noalloc ----
+// One array per GPU the library runs on, held until the process ends: the
+// step metadata in the first SNRVQ_SCRATCH_META_BYTES, the split-K partials
+// after it.  Host code never uses the array's name as an address: the device
+// address of each GPU's copy is looked up once per device (with that device
+// current) and kept in g_scratch_dev.
+constexpr size_t SNRVQ_SCRATCH_BYTES = (size_t)32 << 20;
+constexpr size_t SNRVQ_SCRATCH_META_BYTES = (size_t)1 << 20;
+constexpr int SNRVQ_MAX_DEVICES = 64;
+void *g_scratch_dev[SNRVQ_MAX_DEVICES];
+std::mutex g_scratch_mu;
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[SNRVQ_SCRATCH_BYTES];
+
+namespace {
+
+// Resolves this codec's device's scratch address (once per device).
+int scratch_setup(codec *c)
+{
+    if (c->dev < 0 || c->dev >= SNRVQ_MAX_DEVICES)
+        return fail(c, CODEC_EINVAL, "device %d: the no-allocation scratch covers devices 0..%d",
+                    c->dev, SNRVQ_MAX_DEVICES - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[c->dev])
+        return CODEC_OK;
+    void *ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+        return fail(c, CODEC_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", c->dev,
+                    hipGetErrorString(e));
+    g_scratch_dev[c->dev] = ptr;
+    return CODEC_OK;
+}
+
 int check_cfg(const codec_cfg *g, int *ch, int *hop)
 {
     if (g->K < 1 || g->K > 64 || g->E < 1 || g->d_cb < 1 || g->d_lat < 1)
@@ -1317,6 +1355,8 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
     c->partial_now = c->splitk_ws;
     c->partial_cap_now = c->splitk_cap;
     c->meta_now = c->meta_dev;
+    if ((rc = scratch_setup(c)))
+        return cleanup_fail(rc);
     for (int i = c->maxB - 1; i >= 0; i--)
         c->free_slots.push_back(i);
     *out = c;
@@ -1605,6 +1645,40 @@ int decode_chunk_graph(codec_t *c, int32_t B, const int32_t *ids, const int32_t 
     c->lastF = F;
     c->lastB = B;
     return CODEC_OK;
+}
+
+int decode_chunk_device_noalloc(codec_t *c, int32_t B, const int32_t *ids, const int32_t *n,
+                                const int32_t *codes_dev, float *pcm, int64_t pcm_capacity,
+                                codec_hip_stream stream)
+{
+    if (!c)
+        return set_err(nullptr, CODEC_EINVAL, "decode_chunk_device_noalloc: NULL codec");
+    std::vector<int> slots;
+    int rc = check_step(c, B, ids, n, codes_dev, pcm, pcm_capacity, true, slots);
+    if (rc)
+        return rc;
+    int F = 0;
+    for (int b = 0; b < B; b++)
+        F += n[b];
+    const size_t meta_bytes = meta_offsets(c, B, F, true).total * 4;
+    if (meta_bytes > SNRVQ_SCRATCH_META_BYTES)
+        return fail(c, CODEC_ETOOBIG,
+                    "decode_chunk_device_noalloc: the step's metadata takes %zu bytes, the "
+                    "static scratch holds %zu",
+                    meta_bytes, SNRVQ_SCRATCH_META_BYTES);
+    void *base = c->dev >= 0 && c->dev < SNRVQ_MAX_DEVICES ? g_scratch_dev[c->dev] : nullptr;
+    if (!base)
+        return fail(c, CODEC_EHIP, "decode_chunk_device_noalloc: no scratch on device %d",
+                    c->dev);
+    HIPCHK(c, hipSetDevice(c->dev));
+    c->meta_now = base;
+    c->partial_now = (float *)((char *)base + SNRVQ_SCRATCH_META_BYTES);
+    c->partial_cap_now = (long)((SNRVQ_SCRATCH_BYTES - SNRVQ_SCRATCH_META_BYTES) / sizeof(float));
+    rc = enqueue_step(c, B, slots.data(), n, codes_dev, pcm, (hipStream_t)stream, true);
+    c->meta_now = c->meta_dev;
+    c->partial_now = c->splitk_ws;
+    c->partial_cap_now = c->splitk_cap;
+    return rc;
 }
 
 int codec_device_status(codec_t *c, int64_t *bad)
