@@ -460,6 +460,50 @@ def mfma_summary(args, cfg: dict, out: list, res: dict) -> None:
     out.append("")
 
 
+def cotenant_trace_summary(path: str) -> list:
+    """Decode kernels of a --cotenant run's kernel trace, inside and outside
+    the window in which the GEMM load ran (from the third GEMM, after the two
+    timed alone, to the last one's end): calls and average duration per
+    kernel, and the decode kernels' total time per decode step."""
+    import csv
+    fn = [f for f in os.listdir(path) if f.endswith("kernel_trace.csv")][0]
+    rows = list(csv.DictReader(open(os.path.join(path, fn))))
+    gemm = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
+                  if r["Kernel_Name"].startswith("Cijk_"))
+    if len(gemm) < 3:
+        raise SystemExit("cotenant trace: fewer than three GEMM dispatches")
+    w0, w1 = gemm[2][0], max(e for _, e in gemm[2:])
+    agg = {}
+    steps = {"alone": 0, "beside": 0}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "snrvq" not in name:
+            continue
+        t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        where = "beside" if t0 >= w0 and t1 <= w1 else "alone"
+        if "rvq_gather" in name:
+            steps[where] += 1
+        a = agg.setdefault(name, {"alone": [0, 0], "beside": [0, 0]})
+        a[where][0] += 1
+        a[where][1] += t1 - t0
+    out = [f"Load window: {(w1 - w0) / 1e6:.2f} ms, {len(gemm) - 2} GEMMs. Decode steps: "
+           f"{steps['alone']} outside the window (warm-up, the timed solo pass, prefill "
+           f"included), {steps['beside']} inside it.\n",
+           "| kernel | calls alone | avg us alone | calls beside load | avg us beside load |",
+           "|---|---:|---:|---:|---:|"]
+    tot = {"alone": 0, "beside": 0}
+    for name, a in sorted(agg.items(), key=lambda kv: -kv[1]["beside"][1])[:12]:
+        short = name if len(name) < 80 else name[:77] + "..."
+        cells = []
+        for k in ("alone", "beside"):
+            n, t = a[k]
+            tot[k] += t
+            cells += [str(n), f"{t / n / 1e3:.1f}" if n else "-"]
+        out.append(f"| `{short}` | " + " | ".join(cells) + " |")
+    out.append("")
+    return out
+
+
 def rocprof_summary(args) -> int:
     """Text summary of a rocprofv3 kernel trace of this benchmark, and of two
     counter runs (FETCH_SIZE, WRITE_SIZE) scaled by the same counters of a
@@ -602,6 +646,9 @@ def rocprof_summary(args) -> int:
                    "source matches.\n")
     if args.pmc_mfma:
         mfma_summary(args, cfg, out, res)
+    if args.cotenant_trace:
+        out.append("## Decode kernels alone and beside the GEMM load\n")
+        out += cotenant_trace_summary(args.cotenant_trace)
     out.append("```json\n" + json.dumps(res, indent=1) + "\n```")
     text = "\n".join(out) + "\n"
     if args.rocprof_summary == "-":
@@ -698,6 +745,8 @@ def main() -> int:
     ap.add_argument("--pmc-write", help="rocprofv3 --pmc WRITE_SIZE output directory")
     ap.add_argument("--pmc-mfma", help="rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES "
                     "output directory")
+    ap.add_argument("--cotenant-trace", help="rocprofv3 --kernel-trace output directory of a "
+                    "--cotenant run (summarised with --rocprof-summary)")
     ap.add_argument("--n-cu", type=int, default=256, help="compute units (counter summaries)")
     ap.add_argument("--pmc-steps", type=int, default=2)
     ap.add_argument("--pmc-warmup", type=int, default=1)
