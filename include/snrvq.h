@@ -239,8 +239,11 @@ int codec_device_status(codec_t *codec, int64_t *bad_codes);
 
 /* ---- inspection (tests) -------------------------------------------------- */
 
-#define CODEC_CAPTURE_LATENT 0    /* projected RVQ sum, [sum n][d_lat] */
+#define CODEC_CAPTURE_LATENT 0    /* projected RVQ sum, [sum n][d_lat] (decoders with a
+                                     transformer: without one the projection is folded into
+                                     the input conv and never stored) */
 #define CODEC_CAPTURE_DEC_INPUT 1 /* input of the conv decoder (after the transformer) */
+#define CODEC_CAPTURE_RVQ_SUM 2   /* the gathered codebook sum z, [sum n][d_cb] */
 /* Conv operands of the decoder, in network order (S = n_stages):
  *   CODEC_CAPTURE_LAYER0 + 3 i          stage i's transposed-conv input,
  *                                       activated: [sum n * r_i][C_i]
@@ -252,7 +255,7 @@ int codec_device_status(codec_t *codec, int64_t *bad_codes);
  * a fused stage kernel the residual-unit and final-conv inputs never reach
  * memory: capturing them needs a codec opened with CODEC_FLAG_PER_LAYER
  * (same arithmetic, every layer stored), else CODEC_EINVAL. */
-#define CODEC_CAPTURE_LAYER0 2
+#define CODEC_CAPTURE_LAYER0 3
 
 /* Copies an intermediate of the last decode step (any decode entry point)
  * as float32, packed like the codes: stream after stream, rows of a stream

@@ -21,7 +21,7 @@ CODEC_OK, CODEC_EINVAL, CODEC_ESTREAM, CODEC_EDUP, CODEC_ERANGE = 0, 1, 2, 3, 4
 CODEC_ENOSLOT, CODEC_ETOOBIG, CODEC_ENOMEM, CODEC_EHIP = 5, 6, 7, 8
 DTYPE_F32, DTYPE_BF16, DTYPE_F16 = 0, 1, 2
 ACT = {"snake": 0, "elu": 1}
-CAPTURE_LATENT, CAPTURE_DEC_INPUT, CAPTURE_LAYER0 = 0, 1, 2
+CAPTURE_LATENT, CAPTURE_DEC_INPUT, CAPTURE_RVQ_SUM, CAPTURE_LAYER0 = 0, 1, 2, 3
 FLAG_PER_LAYER = 1
 FLAG_NO_SPLIT_K = 2
 FLAG_TWO_STAGE_BUFFERS = 4

@@ -3,7 +3,7 @@
 //
 // Decode step (all on the caller's stream):
 //   H2D of the packed step metadata (codes, frame->stream map, cu, slots,
-//   fresh flags, positions) from a pinned ring buffer;
+//   fresh flags, positions) from a pinned staging arena;
 //   one launch: the RVQ gather-and-sum of every frame beside the halo fill
 //   (every conv layer's left context, all streams);
 //   projection GEMM -> [windowed transformer] -> input conv -> per stage
@@ -22,8 +22,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <deque>
 #include <map>
 #include <mutex>
+#include <thread>
 #include <string>
 #include <unordered_map>
 #include <unordered_set>
@@ -110,6 +112,13 @@ struct codec {
     void *u16 = nullptr, *a16 = nullptr, *att16 = nullptr, *f16 = nullptr;
     float *h32 = nullptr, *qkv32 = nullptr, *kring = nullptr, *vring = nullptr;
 
+    // Decoders without a transformer fold the projection into the input conv
+    // (fold): the gather writes z' = [z, 1, 0...] rows of dz values into the
+    // extended buffer z, and the input conv's weights are W_in composed with
+    // [W_p | b_p] (computed at open).  Otherwise z is the packed RVQ sum
+    // (dz = d_cb) and the projection runs as its own GEMM into u_ext / u16.
+    bool fold = false;
+    int dz = 0;
     void *z = nullptr, *u_ext = nullptr, *aT[CODEC_MAX_STAGES]{}, *a1[CODEC_MAX_STAGES]{},
          *a2[CODEC_MAX_STAGES]{}, *h = nullptr, *a_outb = nullptr;
     float *x = nullptr, *pcm_scratch = nullptr;
@@ -134,7 +143,19 @@ struct codec {
     void *meta_dev = nullptr;
     size_t meta_cap = 0;  // int32 elements
     unsigned long long *bad_codes = nullptr;  // device counter (device-resident codes)
-    void *pinned[2]{};
+    // Pinned staging of the step metadata: an arena used as a ring.  Each
+    // step takes the next span of it, and an event recorded after the step's
+    // launches releases the span; the host waits only when the arena (or the
+    // event pool) is full, so it can queue many steps ahead of the device
+    // and a host-side pause does not leave the device idle.
+    char *arena = nullptr;
+    size_t arena_cap = 0, arena_head = 0;
+    struct Span {
+        size_t begin, end;
+        hipEvent_t ev;
+    };
+    std::deque<Span> inflight;          // oldest first
+    std::vector<hipEvent_t> ev_free;    // preallocated at open
     // Step graphs (decode_chunk_graph), keyed by (streams in the graph, frames
     // in the graph): a step of F frames runs as a graph of the next bucket of
     // Fb >= F frames, the difference decoded by the pad stream (slot pad_slot,
@@ -153,8 +174,6 @@ struct codec {
     hipStream_t cap_stream = nullptr;  // graphs are captured here, launched on the caller's
     int pad_slot = 0;                  // state slot of the graph pad stream (max_streams)
     int allocF = 0, allocB = 0;        // frames and streams the workspace holds
-    hipEvent_t pin_ev[2]{};
-    int pin_i = 0;
     StepMeta last_meta{};
     int lastF = 0, lastB = 0;
 
@@ -359,6 +378,58 @@ std::vector<float> pack_convT(const std::vector<float> &W, int Ci, int Co, int s
                 o[(n * 2 + 1) * Ci + c] = W[((size_t)c * Co + oc) * k + r];
             }
     return o;
+}
+
+// Input conv composed with the projection, for decoders whose projection
+// feeds the input conv directly.  The conv of u = W_p z + b_p over a zero
+// left context equals, tap by tap, a conv of z' = [z, 1, 0...] (zero left
+// context too: the 1 is absent before the stream's first frame, exactly
+// where the bias b_p is) with weights W_in[o][:, tap] [W_p | b_p]:
+//   Wc[o][tap dz + c] = sum_m W_in[o][m][tap] W'[m][c],
+//   W'[m][c] = W_p[m][c] (c < d_cb), b_p[m] (c = d_cb), 0 (c > d_cb).
+// Summed in fp64 over m ascending, then rounded once to fp32.  Packed K-major
+// ([o][tap][c]) for the implicit GEMM.  Rows split over host threads.
+std::vector<float> fold_projection(const std::vector<float> &Win /*[Co][Dl][7]*/,
+                                   const std::vector<float> &Wp /*[Dl][Dcb]*/,
+                                   const std::vector<float> &bp /*[Dl]*/, int Co, int Dl, int Dcb,
+                                   int dz)
+{
+    std::vector<double> wpx((size_t)Dl * dz, 0.0);
+    for (int m = 0; m < Dl; m++) {
+        for (int cc = 0; cc < Dcb; cc++)
+            wpx[(size_t)m * dz + cc] = Wp[(size_t)m * Dcb + cc];
+        wpx[(size_t)m * dz + Dcb] = bp[m];
+    }
+    std::vector<float> out((size_t)Co * 7 * dz);
+    auto rows = [&](int o0, int o1) {
+        std::vector<double> acc((size_t)7 * dz);
+        for (int o = o0; o < o1; o++) {
+            std::fill(acc.begin(), acc.end(), 0.0);
+            for (int m = 0; m < Dl; m++) {
+                const double *wr = wpx.data() + (size_t)m * dz;
+                for (int tap = 0; tap < 7; tap++) {
+                    const double w = Win[((size_t)o * Dl + m) * 7 + tap];
+                    double *ar = acc.data() + (size_t)tap * dz;
+                    for (int cc = 0; cc <= Dcb; cc++)
+                        ar[cc] += w * wr[cc];
+                }
+            }
+            for (size_t k = 0; k < acc.size(); k++)
+                out[(size_t)o * 7 * dz + k] = (float)acc[k];
+        }
+    };
+    unsigned nt = std::thread::hardware_concurrency();
+    nt = nt < 1 ? 1 : (nt > 16 ? 16 : nt);
+    std::vector<std::thread> th;
+    const int per = (Co + (int)nt - 1) / (int)nt;
+    for (unsigned t = 0; t < nt; t++) {
+        const int o0 = (int)t * per, o1 = std::min(Co, o0 + per);
+        if (o0 < o1)
+            th.emplace_back(rows, o0, o1);
+    }
+    for (auto &x : th)
+        x.join();
+    return out;
 }
 
 int make_lin(codec *c, const std::vector<float> &packed, const std::vector<float> &bias, int N,
@@ -725,21 +796,25 @@ int enqueue_kernels(codec *c, int B, int F, const MetaLayout &ml, float *pcm, hi
 
     // the gather and the halo fill of every layer share one launch
     rc = timed(c, "rvq_gather", F, s, [&] {
-        return launch_rvq_gather_fill(c->cb, c->cb_dtype, m.codes, F, g.K, g.E, g.d_cb, c->z,
-                                      c->dtype, c->bad_codes, c->halo, c->state, m, B, s);
+        return launch_rvq_gather_fill(c->cb, c->cb_dtype, m.codes, F, g.K, g.E, g.d_cb, c->dz,
+                                      c->fold ? 6 : 0, c->fold ? 1 : 0, c->z, c->dtype,
+                                      c->bad_codes, c->halo, c->state, m, B, s);
     });
     if (rc)
         return rc;
 
-    ConvArgs a = conv_args(c, c->proj, c->z, 0, 1, F, m);
-    a.out16 = g.tf_layers ? c->u16 : c->u_ext;
-    a.out_H = g.tf_layers ? 0 : 6;
-    if ((rc = run_conv(c, "proj", a, s)))
-        return rc;
+    ConvArgs a;
+    if (!c->fold) {
+        a = conv_args(c, c->proj, c->z, 0, 1, F, m);
+        a.out16 = g.tf_layers ? c->u16 : c->u_ext;
+        a.out_H = g.tf_layers ? 0 : 6;
+        if ((rc = run_conv(c, "proj", a, s)))
+            return rc;
+    }
     if (g.tf_layers && (rc = enqueue_transformer(c, B, F, m, s)))
         return rc;
 
-    a = conv_args(c, c->in_conv, c->u_ext, 6, 1, F, m);
+    a = conv_args(c, c->in_conv, c->fold ? c->z : c->u_ext, 6, 1, F, m);
     a.out16 = c->aT[0];
     a.out_H = 1;
     set_act(c, a, c->a_stage[0]);
@@ -865,23 +940,83 @@ void step_done(codec *c, int B, const int *slots, const int32_t *n)
     }
 }
 
+// Waits for (and releases) the oldest in-flight span of the staging arena.
+int arena_retire_oldest(codec *c)
+{
+    const codec::Span sp = c->inflight.front();
+    c->inflight.pop_front();
+    c->ev_free.push_back(sp.ev);
+    HIPCHK(c, hipEventSynchronize(sp.ev));
+    return CODEC_OK;
+}
+
+// A span of `bytes` of the staging arena for the next step's metadata (the
+// arena holds the largest step several times over).  Spans are taken in ring
+// order; the in-flight spans that the new one overlaps are waited for first.
+int arena_take(codec *c, size_t bytes, int32_t **out)
+{
+    bytes = (bytes + 255) & ~(size_t)255;
+    if (bytes > c->arena_cap)
+        return fail(c, CODEC_ETOOBIG, "step metadata of %zu bytes exceeds the staging arena",
+                    bytes);
+    // The in-flight spans form one circular run ending at the head, oldest
+    // first, so the spans a new span overlaps are always the oldest ones --
+    // except when wrapping to 0 while the run itself wraps: its oldest spans
+    // then lie in [head, cap), which this lap gives up, and are retired first.
+    const size_t at = c->arena_head + bytes <= c->arena_cap ? c->arena_head : 0;
+    if (at == 0 && c->arena_head > 0)
+        while (!c->inflight.empty() && c->inflight.front().begin >= c->arena_head) {
+            int rc = arena_retire_oldest(c);
+            if (rc)
+                return rc;
+        }
+    while (!c->inflight.empty()) {
+        const codec::Span &sp = c->inflight.front();
+        const bool overlap = sp.begin < at + bytes && at < sp.end;
+        if (!overlap && !c->ev_free.empty())
+            break;
+        int rc = arena_retire_oldest(c);
+        if (rc)
+            return rc;
+    }
+    *out = (int32_t *)(c->arena + at);
+    c->arena_head = at + bytes;
+    return CODEC_OK;
+}
+
+// Marks the span just taken as in flight until the work enqueued so far on s
+// is done.  Recorded after the step's last launch (not right after the copy
+// that reads the span): the record also hands the step's launches to the
+// device, so a later wait on it never finds them still queued on the host.
+int arena_commit(codec *c, const int32_t *hp, size_t bytes, hipStream_t s)
+{
+    bytes = (bytes + 255) & ~(size_t)255;
+    hipEvent_t ev = c->ev_free.back();
+    HIPCHK(c, hipEventRecord(ev, s));
+    c->ev_free.pop_back();
+    const size_t begin = (size_t)((const char *)hp - c->arena);
+    c->inflight.push_back({begin, begin + bytes, ev});
+    return CODEC_OK;
+}
+
 int enqueue_step(codec *c, int B, const int *slots, const int32_t *n, const int32_t *codes,
                  float *pcm, hipStream_t s, bool codes_on_device = false)
 {
     int F = 0;
     for (int b = 0; b < B; b++)
         F += n[b];
-    // batch assembly into the pinned ring, one H2D copy
-    int pi = c->pin_i;
-    c->pin_i ^= 1;
-    HIPCHK(c, hipEventSynchronize(c->pin_ev[pi]));  // the copy that last read this buffer is done
-    int32_t *hp = (int32_t *)c->pinned[pi];
-    MetaLayout ml = fill_meta(c, hp, B, slots, n, codes, codes_on_device);
-    int rc = enqueue_meta_copy(c, ml, hp, s);
+    // batch assembly into the pinned staging arena, one H2D copy
+    const size_t bytes = meta_offsets(c, B, F, codes_on_device).total * 4;
+    int32_t *hp = nullptr;
+    int rc = arena_take(c, bytes, &hp);
     if (rc)
         return rc;
-    HIPCHK(c, hipEventRecord(c->pin_ev[pi], s));
+    MetaLayout ml = fill_meta(c, hp, B, slots, n, codes, codes_on_device);
+    if ((rc = enqueue_meta_copy(c, ml, hp, s)))
+        return rc;
     if ((rc = enqueue_kernels(c, B, F, ml, pcm, s)))
+        return rc;
+    if ((rc = arena_commit(c, hp, bytes, s)))
         return rc;
     step_done(c, B, slots, n);
     return CODEC_OK;
@@ -1162,7 +1297,11 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
         }
     }
     // ---- dense layers, repacked K-major for the implicit GEMM ----
-    if ((rc = make_lin(c, W("rvq.proj.weight"), W("rvq.proj.bias"), g.d_lat, g.d_lat, g.d_cb, 1,
+    c->fold = g.tf_layers == 0;
+    c->dz = c->fold ? (g.d_cb + 1 + (c->dtype ? 63 : 15)) / (c->dtype ? 64 : 16) * (c->dtype ? 64 : 16)
+                    : g.d_cb;
+    if (!c->fold &&
+        (rc = make_lin(c, W("rvq.proj.weight"), W("rvq.proj.bias"), g.d_lat, g.d_lat, g.d_cb, 1,
                        1, 1, &c->proj)))
         return cleanup_fail(rc);
     if (g.tf_layers) {
@@ -1199,9 +1338,18 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
             return cleanup_fail(rc);
         HIPCHK(c, hipMemcpy(c->inv_freq, inv.data(), inv.size() * 8, hipMemcpyHostToDevice));
     }
-    if ((rc = make_lin(c, pack_conv(W("dec.in_conv.weight"), ch[0], g.d_lat, 7),
-                       W("dec.in_conv.bias"), ch[0], ch[0], g.d_lat, 7, 1, 1, &c->in_conv)))
+    if (c->fold) {
+        std::vector<float> wc =
+            fold_projection(W("dec.in_conv.weight"), W("rvq.proj.weight"), W("rvq.proj.bias"),
+                            ch[0], g.d_lat, g.d_cb, c->dz);
+        if ((rc = make_lin(c, wc, W("dec.in_conv.bias"), ch[0], ch[0], c->dz, 7, 1, 1,
+                           &c->in_conv)))
+            return cleanup_fail(rc);
+    } else if ((rc = make_lin(c, pack_conv(W("dec.in_conv.weight"), ch[0], g.d_lat, 7),
+                              W("dec.in_conv.bias"), ch[0], ch[0], g.d_lat, 7, 1, 1,
+                              &c->in_conv))) {
         return cleanup_fail(rc);
+    }
     for (int i = 0; i < c->S; i++) {
         int ci = ch[i], co = ch[i + 1], s = g.strides[i];
         snprintf(nm, sizeof nm, "dec.stage.%d.snake.alpha", i);
@@ -1239,10 +1387,15 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
     c->pad_slot = c->maxB;
     const size_t F = (size_t)c->allocF, B = (size_t)c->allocB, es = (size_t)c->esz;
     int64_t *ws = &c->workspace_bytes;
-    if ((rc = dev_alloc(c, &c->z, F * g.d_cb * es, ws)))
-        return cleanup_fail(rc);
-    if ((rc = dev_alloc(c, &c->u_ext, (B * 6 + F) * g.d_lat * es, ws)))
-        return cleanup_fail(rc);
+    if (c->fold) {  // extended rows of dz values: the input conv's operand
+        if ((rc = dev_alloc(c, &c->z, (B * 6 + F) * c->dz * es, ws)))
+            return cleanup_fail(rc);
+    } else {
+        if ((rc = dev_alloc(c, &c->z, F * g.d_cb * es, ws)))
+            return cleanup_fail(rc);
+        if ((rc = dev_alloc(c, &c->u_ext, (B * 6 + F) * g.d_lat * es, ws)))
+            return cleanup_fail(rc);
+    }
     size_t hmax = 0;
     for (int i = 0; i < c->S; i++) {
         size_t ro = (size_t)c->rate[i + 1], co = (size_t)ch[i + 1];
@@ -1291,7 +1444,10 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
         L.state_off = off;
         off += (int64_t)H * C;
     };
-    add(c->u_ext, 6, g.d_lat, 1);
+    if (c->fold)
+        add(c->z, 6, c->dz, 1);
+    else
+        add(c->u_ext, 6, g.d_lat, 1);
     for (int i = 0; i < c->S; i++) {
         add(c->aT[i], 1, ch[i], c->rate[i]);
         c->off_a1[i] = off;
@@ -1328,7 +1484,7 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
     if ((rc = dev_alloc(c, &c->state, (size_t)c->allocB * off * es, ws)))
         return cleanup_fail(rc);
 
-    // ---- step metadata: device buffer + two pinned staging buffers ----
+    // ---- step metadata: device buffer + pinned staging arena ----
     c->meta_cap = round4(F * g.K) + round4(F) + round4(B + 1) + 3 * round4(B) +
                   CODEC_MAX_STAGES * round4(B + 1) + 4;
     if ((rc = dev_alloc(c, &c->meta_dev, c->meta_cap * 4, ws)))
@@ -1336,17 +1492,25 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
     if ((rc = dev_alloc(c, (void **)&c->bad_codes, sizeof(unsigned long long), ws)))
         return cleanup_fail(rc);
     HIPCHK(c, hipMemset(c->bad_codes, 0, sizeof(unsigned long long)));
-    for (int i = 0; i < 2; i++) {
-        hipError_t e = hipHostMalloc(&c->pinned[i], c->meta_cap * 4, hipHostMallocDefault);
+    // staging arena: the largest step's metadata 16 times over, at least
+    // 16 MiB; events for up to 1024 steps in flight
+    c->arena_cap = std::max<size_t>((size_t)16 << 20, 16 * ((c->meta_cap * 4 + 255) & ~(size_t)255));
+    {
+        hipError_t e = hipHostMalloc((void **)&c->arena, c->arena_cap, hipHostMallocDefault);
         if (e != hipSuccess) {
-            c->pinned[i] = nullptr;
-            fail(c, CODEC_ENOMEM, "hipHostMalloc: %s", hipGetErrorString(e));
+            c->arena = nullptr;
+            fail(c, CODEC_ENOMEM, "hipHostMalloc of the %zu-byte staging arena: %s",
+                 c->arena_cap, hipGetErrorString(e));
             return cleanup_fail(CODEC_ENOMEM);
         }
-        e = hipEventCreateWithFlags(&c->pin_ev[i], hipEventDisableTiming);
-        if (e != hipSuccess) {
-            fail(c, CODEC_EHIP, "hipEventCreate: %s", hipGetErrorString(e));
-            return cleanup_fail(CODEC_EHIP);
+        for (int i = 0; i < 1024; i++) {
+            hipEvent_t ev = nullptr;
+            e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+            if (e != hipSuccess) {
+                fail(c, CODEC_EHIP, "hipEventCreate: %s", hipGetErrorString(e));
+                return cleanup_fail(CODEC_EHIP);
+            }
+            c->ev_free.push_back(ev);
         }
     }
 
@@ -1374,12 +1538,12 @@ int codec_close(codec_t *c)
     }
     for (auto e : c->ev_pool)
         (void)hipEventDestroy(e);
-    for (int i = 0; i < 2; i++) {
-        if (c->pin_ev[i])
-            (void)hipEventDestroy(c->pin_ev[i]);
-        if (c->pinned[i])
-            (void)hipHostFree(c->pinned[i]);
-    }
+    for (auto &sp : c->inflight)
+        (void)hipEventDestroy(sp.ev);
+    for (auto e : c->ev_free)
+        (void)hipEventDestroy(e);
+    if (c->arena)
+        (void)hipHostFree(c->arena);
     if (c->cap_stream)
         (void)hipStreamDestroy(c->cap_stream);
     for (auto &kv : c->graphs)
@@ -1588,15 +1752,14 @@ int decode_chunk_graph(codec_t *c, int32_t B, const int32_t *ids, const int32_t 
     codec::GraphEntry &e = it->second;
     e.last_use = ++c->graph_clock;
 
-    // metadata through the codec's pinned ring, as for an eager step
-    const int pi = c->pin_i;
-    c->pin_i ^= 1;
-    HIPCHK(c, hipEventSynchronize(c->pin_ev[pi]));
-    int32_t *hp = (int32_t *)c->pinned[pi];
+    // metadata through the codec's pinned staging arena, as for an eager step
+    const size_t meta_bytes = meta_offsets(c, Bt, Fb, false).total * 4;
+    int32_t *hp = nullptr;
+    if ((rc = arena_take(c, meta_bytes, &hp)))
+        return rc;
     MetaLayout ml = fill_meta(c, hp, Bt, gslots.data(), gn.data(), codes, false, F, true);
     if ((rc = enqueue_meta_copy(c, ml, hp, s)))
         return rc;
-    HIPCHK(c, hipEventRecord(c->pin_ev[pi], s));
 
     if (!e.exec) {
         // capture on the codec's own stream (the caller's may be the null
@@ -1640,6 +1803,8 @@ int decode_chunk_graph(codec_t *c, int32_t B, const int32_t *ids, const int32_t 
     HIPCHK(c, hipEventRecord(e.done, s));
     HIPCHK(c, hipMemcpyAsync(pcm, c->pcm_scratch, sizeof(float) * (size_t)F * c->hop,
                              hipMemcpyDeviceToDevice, s));
+    if ((rc = arena_commit(c, hp, meta_bytes, s)))
+        return rc;
     step_done(c, B, slots.data(), n);
     c->last_meta = ml.m;  // the caller's streams are the first B of the graph's
     c->lastF = F;
@@ -1732,11 +1897,22 @@ int codec_debug_capture(codec_t *c, int32_t what, float *dst, int64_t capacity,
     const void *ext = nullptr;
     int H = 0, C = 0, rate = 1;
     bool materialized = true;
+    int ld = 0;  // row pitch of the source, 0: C
     if (what == CODEC_CAPTURE_LATENT || what == CODEC_CAPTURE_DEC_INPUT) {
+        if (c->fold)
+            return fail(c, CODEC_EINVAL,
+                        "codec_debug_capture: without a transformer the projection is folded "
+                        "into the input conv and the latent is never stored; capture "
+                        "CODEC_CAPTURE_RVQ_SUM");
         const bool tf_latent = what == CODEC_CAPTURE_LATENT && c->cfg.tf_layers > 0;
         ext = tf_latent ? c->u16 : c->u_ext;
         H = tf_latent ? 0 : 6;
         C = c->cfg.d_lat;
+    } else if (what == CODEC_CAPTURE_RVQ_SUM) {
+        ext = c->z;
+        H = c->fold ? 6 : 0;
+        ld = c->dz;
+        C = c->cfg.d_cb;
     } else if (what >= CODEC_CAPTURE_LAYER0 && what <= CODEC_CAPTURE_LAYER0 + 3 * c->S) {
         const int t = what - CODEC_CAPTURE_LAYER0, i = t / 3, k = t % 3;
         if (t == 3 * c->S) {  // the final conv's input
@@ -1774,7 +1950,7 @@ int codec_debug_capture(codec_t *c, int32_t what, float *dst, int64_t capacity,
         return fail(c, CODEC_EINVAL, "codec_debug_capture: step of %d frames, %d streams",
                     c->lastF, c->lastB);
     HIPCHK(c, hipSetDevice(c->dev));
-    HIPCHK(c, launch_unextend(ext, c->dtype, H, C, rate, c->last_meta.frame_stream,
+    HIPCHK(c, launch_unextend(ext, c->dtype, H, ld ? ld : C, C, rate, c->last_meta.frame_stream,
                               c->lastF * rate, dst, (hipStream_t)stream));
     return CODEC_OK;
 }

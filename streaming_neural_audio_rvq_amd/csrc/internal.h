@@ -147,23 +147,27 @@ const char *conv_gemm_tile_name(int dtype, int tile);
 hipError_t launch_halo_save(const HaloTable &t, void *state, const StepMeta &m, int B,
                             hipStream_t st);
 
-// z[f][:] = sum_k cb[k][codes[f][k]][:] (cb is one [K][E][d_cb] array),
-// written in the compute type.  cb_dtype: 0 fp32 tables, 1 bf16 tables.
-// out_dtype: 0 fp32, 1 fp16.  Codes outside [0, E) are counted in *bad and
-// read as 0.  The same launch fills the halo rows of every layer of table t
-// from the streams' slots (zeros for fresh streams): the two are independent.
+// z[f][0, d_cb) = sum_k cb[k][codes[f][k]][:] (cb is one [K][E][d_cb] array),
+// written in the compute type as rows of out_ld values: with `one`, value
+// d_cb is 1 and the rest of the row zero (the constant input of a folded
+// input conv).  out_H > 0 writes the rows into an extended buffer with out_H
+// halo rows per stream.  cb_dtype: 0 fp32 tables, 1 bf16 tables.  out_dtype:
+// 0 fp32, 1 fp16.  Codes outside [0, E) are counted in *bad and read as 0.
+// The same launch fills the halo rows of every layer of table t from the
+// streams' slots (zeros for fresh streams): the two are independent.
 hipError_t launch_rvq_gather_fill(const void *cb, int cb_dtype, const int32_t *codes, int F,
-                                  int K, int E, int d_cb, void *z, int out_dtype,
-                                  unsigned long long *bad, const HaloTable &t, void *state,
-                                  const StepMeta &m, int B, hipStream_t st);
+                                  int K, int E, int d_cb, int out_ld, int out_H, int one, void *z,
+                                  int out_dtype, unsigned long long *bad, const HaloTable &t,
+                                  void *state, const StepMeta &m, int B, hipStream_t st);
 
 // pcm[m] = b + sum_{j, c} w[c][j] A_ext[row(m) - (6 - j), c], m < M (k = 7, Cout = 1).
 hipError_t launch_final_conv(const void *A, int dtype, int A_H, int C, int rate,
                              const float *w /*[C][7]*/, float b, int final_tanh,
                              const int32_t *frame_stream, int M, float *pcm, hipStream_t st);
 
-// Copies packed rows out of an extended buffer as fp32 [M][C].
-hipError_t launch_unextend(const void *ext, int dtype, int H, int C, int rate,
+// Copies the first C values of packed rows out of an extended buffer (rows
+// of ld values, H halo rows per stream) as fp32 [M][C].
+hipError_t launch_unextend(const void *ext, int dtype, int H, int ld, int C, int rate,
                            const int32_t *frame_stream, int M, float *dst, hipStream_t st);
 
 // ---- fused upsample stage (kernels_stage.hip), fp16 operands only ----

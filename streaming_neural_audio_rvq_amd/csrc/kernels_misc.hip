@@ -15,25 +15,8 @@ namespace {
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-
-// Copies the slot's H rows of halo layer `layer` into the halo of stream b
-// (zeros for a fresh stream); one work-group.
-__device__ __forceinline__ void halo_fill_one(const HaloTable &t, int layer, int b,
-                                              const char *state, const int32_t *cu,
-                                              const int32_t *slot, const int32_t *fresh)
-{
-    const HaloLayer &L = t.l[layer];
-    const long row_bytes = (long)L.C * t.elem_bytes;
-    const long bytes = (long)L.H * row_bytes;
-    char *dst = (char *)L.ext + ((long)b * L.H + (long)cu[b] * L.rate) * row_bytes;
-    const char *src = state + ((long)slot[b] * t.slot_elems + L.state_off) * t.elem_bytes;
-    const bool zero = fresh[b] != 0;
-    for (long i = (long)threadIdx.x * 16; i < bytes; i += 256 * 16) {
-        u4 v = zero ? u4{0u, 0u, 0u, 0u} : *(const u4 *)(src + i);
-        *(u4 *)(dst + i) = v;
-    }
-}
 
 // blockIdx.x = batch index b, blockIdx.y = halo layer.
 __global__ __launch_bounds__(256) void halo_save_kernel(HaloTable t, char *state,
@@ -42,94 +25,140 @@ __global__ __launch_bounds__(256) void halo_save_kernel(HaloTable t, char *state
     halo_save_one(t, blockIdx.y, blockIdx.x, state, cu, slot, threadIdx.x, 256);
 }
 
-typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void load4(const uint16_t *p, float *v)
+// 8 consecutive table values as fp32 (bf16 -> fp32 is exact: the bits move to
+// the top half).
+__device__ __forceinline__ void load8(const uint16_t *p, float *v)
 {
-    // bf16 -> fp32 is exact: the bits move to the top half
-    u2 w = *(const u2 *)p;
+    const u4 w = *(const u4 *)p;
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
+    for (int i = 0; i < 4; i++) {
         v[2 * i] = __uint_as_float(w[i] << 16);
         v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
 }
-__device__ __forceinline__ void load4(const float *p, float *v)
+__device__ __forceinline__ void load8(const float *p, float *v)
 {
-    f4 a = *(const f4 *)p;
+    const f4 a = *(const f4 *)p, b = *(const f4 *)(p + 4);
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 4; i++) {
         v[i] = a[i];
+        v[4 + i] = b[i];
+    }
 }
-__device__ __forceinline__ void store4(half_t *p, const float *v)
+__device__ __forceinline__ void store8(half_t *p, const float *v)
 {
-    *(h4 *)p = h4{snrvq_f16(v[0]), snrvq_f16(v[1]), snrvq_f16(v[2]), snrvq_f16(v[3])};
+    h8 h;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        h[i] = snrvq_f16(v[i]);
+    *(h8 *)p = h;
 }
-__device__ __forceinline__ void store4(float *p, const float *v)
+__device__ __forceinline__ void store8(float *p, const float *v)
 {
     *(f4 *)p = f4{v[0], v[1], v[2], v[3]};
+    *(f4 *)(p + 4) = f4{v[4], v[5], v[6], v[7]};
 }
 
-// One thread owns 4 consecutive latent values of one frame and sums the K
-// selected codebook rows in codebook order, in fp32.  The codebooks are one
-// contiguous [K][E][d_cb] array.  Codebooks are taken 8 at a time: their
-// codes, then their rows are loaded before any is added, so a thread has up to
-// 8 row loads in flight instead of one.
+// One thread owns 8 consecutive values of one frame's output row and sums
+// the K selected codebook rows in codebook order, in fp32.  The codebooks are
+// one contiguous [K][E][d_cb] array.  Codebooks are taken 16 at a time: all
+// 16 codes are loaded, then all 16 rows, before any is added, so a step of up
+// to 16 codebooks costs two dependent memory round trips (codes, rows).  The output row is out_ld wide:
+// channels [0, d_cb) take the sum; with `one` set channel d_cb is 1 (the
+// constant input that carries the projection bias through a folded input
+// conv) and the rest zero.  out_H > 0: rows go to the extended buffer (stream
+// b's frame f at row (b + 1) out_H + f).
 template <typename CB, typename OUT>
 __device__ __forceinline__ void rvq_gather_body(int blk, const CB *cb, const int32_t *codes, int F,
-                                                int K, int E, int d_cb, OUT *z,
+                                                int K, int E, int d_cb, int out_ld, int out_H,
+                                                bool one, const int32_t *frame_stream, OUT *z,
                                                 unsigned long long *bad)
 {
-    const int per_frame = d_cb / 4;
-    long g = (long)blk * 256 + threadIdx.x;
-    long f = g / per_frame;
+    const int per_frame = out_ld / 8;
+    const long g = (long)blk * 256 + threadIdx.x;
+    const long f = g / per_frame;
     if (f >= F)
         return;
-    int d = (int)(g - f * per_frame) * 4;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    const int32_t *cf = codes + f * K;
-    for (int k0 = 0; k0 < K; k0 += 8) {
-        int e[8];
+    const int d = (int)(g - f * per_frame) * 8;
+    const long row = out_H ? (long)(frame_stream[f] + 1) * out_H + f : f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (d >= d_cb) {  // the constant channel and the zero padding
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
+        for (int i = 0; i < 8; i++)
+            acc[i] = one && d + i == d_cb ? 1.f : 0.f;
+        store8(z + row * out_ld + d, acc);
+        return;
+    }
+    const int32_t *cf = codes + f * K;
+    constexpr int KB = 16;
+    for (int k0 = 0; k0 < K; k0 += KB) {
+        int e[KB];
+#pragma unroll
+        for (int j = 0; j < KB; j++)
             e[j] = k0 + j < K ? cf[k0 + j] : 0;
+#pragma unroll
+        for (int j = 0; j < KB; j++)
             if ((unsigned)e[j] >= (unsigned)E) {  // only reachable with device-resident codes
-                if (d == 0)
+                if (d == 0 && k0 + j < K)
                     atomicAdd(bad, 1ull);
                 e[j] = 0;
             }
-        }
-        float v[8][4];
+        float v[KB][8];
 #pragma unroll
-        for (int j = 0; j < 8; j++)
+        for (int j = 0; j < KB; j++)
             if (k0 + j < K)
-                load4(cb + ((long)(k0 + j) * E + e[j]) * d_cb + d, v[j]);
+                load8(cb + ((long)(k0 + j) * E + e[j]) * d_cb + d, v[j]);
 #pragma unroll
-        for (int j = 0; j < 8; j++)
+        for (int j = 0; j < KB; j++)
             if (k0 + j < K)
 #pragma unroll
-                for (int i = 0; i < 4; i++)
+                for (int i = 0; i < 8; i++)
                     acc[i] += v[j][i];
     }
-    store4(z + f * d_cb + d, acc);
+    store8(z + row * out_ld + d, acc);
 }
 
 // The step's first launch: the gather in work-groups [0, gblocks), the halo
-// fill of every (layer, stream) pair in the rest.  The two are independent,
-// so one launch runs them side by side instead of one after the other.
+// fill of every layer and stream in the rest.  The two are independent, so
+// one launch runs them side by side.  The fill is flat over (layer, stream,
+// 16-byte chunk), each thread copying FILL_PER chunks (zeros for a fresh
+// stream).
+constexpr int FILL_PER = 4;
 template <typename CB, typename OUT>
 __global__ __launch_bounds__(256) void rvq_gather_fill_kernel(
-    const CB *cb, const int32_t *codes, int F, int K, int E, int d_cb, OUT *z,
-    unsigned long long *bad, int gblocks, HaloTable t, const char *state, const int32_t *cu,
-    const int32_t *slot, const int32_t *fresh, int B)
+    const CB *cb, const int32_t *codes, int F, int K, int E, int d_cb, int out_ld, int out_H,
+    int one, OUT *z, unsigned long long *bad, int gblocks, HaloTable t, const char *state,
+    const int32_t *frame_stream, const int32_t *cu, const int32_t *slot, const int32_t *fresh,
+    int B)
 {
     const int blk = blockIdx.x;
     if (blk < gblocks) {
-        rvq_gather_body(blk, cb, codes, F, K, E, d_cb, z, bad);
+        rvq_gather_body(blk, cb, codes, F, K, E, d_cb, out_ld, out_H, one != 0, frame_stream, z,
+                        bad);
         return;
     }
-    const int j = blk - gblocks;
-    halo_fill_one(t, j / B, j % B, state, cu, slot, fresh);
+    // consecutive threads take consecutive chunks (one 16-byte chunk per
+    // thread per pass: every wave access is one contiguous 1 KB run)
+#pragma unroll
+    for (int q = 0; q < FILL_PER; q++) {
+        int i = ((blk - gblocks) * FILL_PER + q) * 256 + (int)threadIdx.x;
+        for (int l = 0; l < t.n; l++) {
+            const HaloLayer &L = t.l[l];
+            const int cpr = L.C * t.elem_bytes / 16;  // chunks per row
+            const int per_stream = L.H * cpr;
+            if (i >= per_stream * B) {
+                i -= per_stream * B;
+                continue;
+            }
+            const int b = i / per_stream;
+            const int k = i - b * per_stream;
+            char *dst = (char *)L.ext + (((long)b * L.H + (long)cu[b] * L.rate) * cpr + k) * 16;
+            const char *src =
+                state + ((long)slot[b] * t.slot_elems + L.state_off) * t.elem_bytes + (long)k * 16;
+            *(u4 *)dst = fresh[b] ? u4{0u, 0u, 0u, 0u} : *(const u4 *)src;
+            break;
+        }
+    }
 }
 
 // fp32 final conv: pcm[m] = b + sum_j sum_c w[j][c] A[row(m) - (6 - j)][c],
@@ -215,9 +244,9 @@ __global__ __launch_bounds__(256) void final_conv_mfma_kernel(const half_t *A, i
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void unextend_kernel(const T *ext, int H, int C, int rate,
-                                                       const int32_t *frame_stream, int M,
-                                                       float *dst)
+__global__ __launch_bounds__(256) void unextend_kernel(const T *ext, int H, int ld, int C,
+                                                       int rate, const int32_t *frame_stream,
+                                                       int M, float *dst)
 {
     long g = (long)blockIdx.x * 256 + threadIdx.x;
     long total = (long)M * C;
@@ -226,7 +255,7 @@ __global__ __launch_bounds__(256) void unextend_kernel(const T *ext, int H, int 
     long m = g / C;
     int c = (int)(g - m * C);
     int b = frame_stream[m / rate];
-    dst[g] = (float)ext[((long)(b + 1) * H + m) * C + c];
+    dst[g] = (float)ext[((long)(b + 1) * H + m) * ld + c];
 }
 
 }  // namespace
@@ -242,32 +271,40 @@ hipError_t launch_halo_save(const HaloTable &t, void *state, const StepMeta &m, 
 }
 
 hipError_t launch_rvq_gather_fill(const void *cb, int cb_dtype, const int32_t *codes, int F,
-                                  int K, int E, int d_cb, void *z, int out_dtype,
-                                  unsigned long long *bad, const HaloTable &t, void *state,
-                                  const StepMeta &m, int B, hipStream_t st)
+                                  int K, int E, int d_cb, int out_ld, int out_H, int one, void *z,
+                                  int out_dtype, unsigned long long *bad, const HaloTable &t,
+                                  void *state, const StepMeta &m, int B, hipStream_t st)
 {
     if (F <= 0 || B <= 0)
         return hipSuccess;
-    const long threads = (long)F * (d_cb / 4);
+    if (out_ld % 8 || d_cb % 8 || out_ld < d_cb + (one ? 1 : 0))
+        return hipErrorInvalidValue;
+    const long threads = (long)F * (out_ld / 8);
     const int gblocks = (int)((threads + 255) / 256);
-    const dim3 grid((unsigned)(gblocks + (long)t.n * B));
+    long chunks = 0;
+    for (int l = 0; l < t.n; l++) {
+        if ((long)t.l[l].C * t.elem_bytes % 16)
+            return hipErrorInvalidValue;
+        chunks += (long)B * t.l[l].H * t.l[l].C * t.elem_bytes / 16;
+    }
+    if (chunks >= (1L << 30))  // the fill indexes chunks in 32 bits
+        return hipErrorInvalidValue;
+    const long fblocks = (chunks + 256L * FILL_PER - 1) / (256L * FILL_PER);
+    const dim3 grid((unsigned)(gblocks + fblocks));
     const char *sp = (const char *)state;
+#define SNRVQ_GATHER(CBT, OT)                                                                      \
+    hipLaunchKernelGGL((rvq_gather_fill_kernel<CBT, OT>), grid, dim3(256), 0, st,                  \
+                       (const CBT *)cb, codes, F, K, E, d_cb, out_ld, out_H, one, (OT *)z, bad,    \
+                       gblocks, t, sp, m.frame_stream, m.cu, m.slot, m.fresh, B)
     if (cb_dtype == 1 && out_dtype == 1)
-        hipLaunchKernelGGL((rvq_gather_fill_kernel<uint16_t, half_t>), grid, dim3(256), 0, st,
-                           (const uint16_t *)cb, codes, F, K, E, d_cb, (half_t *)z, bad, gblocks,
-                           t, sp, m.cu, m.slot, m.fresh, B);
+        SNRVQ_GATHER(uint16_t, half_t);
     else if (cb_dtype == 0 && out_dtype == 0)
-        hipLaunchKernelGGL((rvq_gather_fill_kernel<float, float>), grid, dim3(256), 0, st,
-                           (const float *)cb, codes, F, K, E, d_cb, (float *)z, bad, gblocks, t,
-                           sp, m.cu, m.slot, m.fresh, B);
+        SNRVQ_GATHER(float, float);
     else if (cb_dtype == 1 && out_dtype == 0)
-        hipLaunchKernelGGL((rvq_gather_fill_kernel<uint16_t, float>), grid, dim3(256), 0, st,
-                           (const uint16_t *)cb, codes, F, K, E, d_cb, (float *)z, bad, gblocks,
-                           t, sp, m.cu, m.slot, m.fresh, B);
+        SNRVQ_GATHER(uint16_t, float);
     else
-        hipLaunchKernelGGL((rvq_gather_fill_kernel<float, half_t>), grid, dim3(256), 0, st,
-                           (const float *)cb, codes, F, K, E, d_cb, (half_t *)z, bad, gblocks, t,
-                           sp, m.cu, m.slot, m.fresh, B);
+        SNRVQ_GATHER(float, half_t);
+#undef SNRVQ_GATHER
     return hipGetLastError();
 }
 
@@ -293,7 +330,7 @@ hipError_t launch_final_conv(const void *A, int dtype, int A_H, int C, int rate,
     return hipGetLastError();
 }
 
-hipError_t launch_unextend(const void *ext, int dtype, int H, int C, int rate,
+hipError_t launch_unextend(const void *ext, int dtype, int H, int ld, int C, int rate,
                            const int32_t *frame_stream, int M, float *dst, hipStream_t st)
 {
     long total = (long)M * C;
@@ -302,10 +339,10 @@ hipError_t launch_unextend(const void *ext, int dtype, int H, int C, int rate,
     dim3 grid((unsigned)((total + 255) / 256));
     if (dtype)
         hipLaunchKernelGGL(unextend_kernel<half_t>, grid, dim3(256), 0, st, (const half_t *)ext, H,
-                           C, rate, frame_stream, M, dst);
+                           ld, C, rate, frame_stream, M, dst);
     else
-        hipLaunchKernelGGL(unextend_kernel<float>, grid, dim3(256), 0, st, (const float *)ext, H, C,
-                           rate, frame_stream, M, dst);
+        hipLaunchKernelGGL(unextend_kernel<float>, grid, dim3(256), 0, st, (const float *)ext, H,
+                           ld, C, rate, frame_stream, M, dst);
     return hipGetLastError();
 }
 

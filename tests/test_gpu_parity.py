@@ -78,23 +78,40 @@ def test_c1_fp32_streamed_and_full_vs_oracle():
     assert e_s <= 1e-5 and e_f <= 1e-5 and e_sf <= 1e-5
 
 
-@pytest.mark.parametrize("name", ["c1", "c2"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
 def test_index_probe_gather_bit_exact(name):
-    cfg = RI.get_config(name)
+    """Codebook indexing, bit for bit: integer probe tables (sums exact in
+    fp16 and fp32) gathered for three ragged streams; the captured RVQ sum
+    equals the oracle's.  The Fish-shaped decoder (projection not folded)
+    also hands out the projected latent, with an identity projection equal
+    to the oracle's bit for bit too; the others fold the projection into the
+    input conv and refuse that capture."""
+    cfg = RI.get_config(name, max_streams=8, max_frames_per_call=64) if name == "c3" \
+        else RI.get_config(name)
     say("case index probe", name)
     w = RI.index_probe_weights(cfg)
     m = oracle.Model(cfg, w)
-    codes = np.concatenate([RI.stream_codes(cfg, b, 5 + 3 * b) for b in range(3)])
     n = [5, 8, 11]
-    _, u_ref, _ = m.stream().decode(codes, capture=True)  # rows are independent per frame
+    codes = np.concatenate([RI.stream_codes(cfg, b, n[b]) for b in range(3)])
+    z_ref = m.rvq_sum(codes)
+    assert np.array_equal(z_ref, np.round(z_ref))  # integer sums, exact everywhere
     c = open_codec(cfg, w)
     ids = [c.stream_open() for _ in n]
     pcm = torch.empty(sum(n) * c.hop, dtype=torch.float32, device="cuda")
     c.decode_chunk(ids, n, codes, pcm)
-    cap = torch.empty(sum(n) * cfg["d_lat"], dtype=torch.float32, device="cuda")
-    c.debug_capture(snr.CAPTURE_LATENT, cap)
-    got = cap.cpu().numpy().reshape(sum(n), cfg["d_lat"]).astype(np.float64)
-    assert np.array_equal(got, u_ref)
+    cap = torch.empty(sum(n) * cfg["d_cb"], dtype=torch.float32, device="cuda")
+    c.debug_capture(snr.CAPTURE_RVQ_SUM, cap)
+    got = cap.cpu().numpy().reshape(sum(n), cfg["d_cb"]).astype(np.float64)
+    assert np.array_equal(got, z_ref)
+    lat = torch.empty(sum(n) * cfg["d_lat"], dtype=torch.float32, device="cuda")
+    if cfg["tf_layers"]:
+        _, u_ref, _ = m.stream().decode(codes, capture=True)  # rows are independent per frame
+        c.debug_capture(snr.CAPTURE_LATENT, lat)
+        got = lat.cpu().numpy().reshape(sum(n), cfg["d_lat"]).astype(np.float64)
+        assert np.array_equal(got, u_ref)
+    else:
+        with pytest.raises(snr.CodecError):
+            c.debug_capture(snr.CAPTURE_LATENT, lat)
 
 
 def test_c2_streamed_ramp_vs_oracle_and_full():
