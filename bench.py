@@ -86,7 +86,12 @@ def layer_model(cfg: dict) -> dict:
             # conv's, each stage input's, and the residual-unit inputs of the
             # stages without a fused kernel (widths above 64 channels)
             fused = [es == 2 and cfg["act"] == "snake" and ch[k + 1] <= 64 for k in range(S)]
-            per_stream = 6 * dl + sum(ch[:S]) + sum(24 * ch[k + 1] for k in range(S)
+            # the input conv's operand: the latent, or (projection folded into
+            # the input conv, decoders without a transformer) [z, 1, 0...]
+            # padded to a multiple of the 64-deep (fp16) / 16-deep K stage
+            gran = 64 if es == 2 else 16
+            d_in = dl if cfg["tf_layers"] else (dcb + 1 + gran - 1) // gran * gran
+            per_stream = 6 * d_in + sum(ch[:S]) + sum(24 * ch[k + 1] for k in range(S)
                                                        if not fused[k])
             wpl += 2 * es * per_stream * cfg["n_streams"]
         else:
@@ -214,6 +219,66 @@ def make_workload(name: str, cfg: dict, codec, total_steps: int, stream,
     else:
         raise SystemExit(f"bench.py: no workload for config {name!r}")
     return {"steps": steps, "desc": f"{name}: {WORKLOADS[name]}", "streams": Bn}
+
+
+def blas_reference(torch, cfg: dict, F: int, reps: int = 20) -> dict:
+    """The decoder's contractions at F frames per step as plain dense fp16
+    GEMMs on the vendor library (torch.mm -> hipBLASLt): no implicit im2col, no
+    activation, no residual, no streaming state -- a calibration of what a
+    tuned library reaches on these shapes, per launch class of this library
+    (a class's GEMMs summed), plus one 8192^3 GEMM."""
+    import rvq_inputs as RI
+    ch = RI.channels(cfg)
+    r = [1]
+    for st in cfg["strides"]:
+        r.append(r[-1] * st)
+    dcb, dl = cfg["d_cb"], cfg["d_lat"]
+    d_in = dl if cfg["tf_layers"] else (dcb + 1 + 63) // 64 * 64
+    classes = {"in_conv": [(F, ch[0], 7 * d_in)]}
+    S = len(cfg["strides"])
+    for i, s in enumerate(cfg["strides"]):
+        ci, co = ch[i], ch[i + 1]
+        convT = (F * r[i], s * co, 2 * ci)
+        conv7 = (F * r[i + 1], co, 7 * co)
+        conv1 = (F * r[i + 1], co, co)
+        if co <= 64:  # one fused kernel per stage
+            g = [convT, conv7, conv1, conv7, conv1]
+            if i == S - 1:
+                g.append((F * r[S], 1, 7 * co))
+            classes[f"s{i}.fused"] = g
+        else:
+            classes[f"s{i}.convT"] = [convT]
+            for j in range(2):
+                classes[f"s{i}.ru{j}.conv7"] = [conv7]
+                classes[f"s{i}.ru{j}.conv1"] = [conv1]
+    classes["square 8192"] = [(8192, 8192, 8192)]
+    timed = {}
+    out = {}
+    for cls, gemms in classes.items():
+        us = flop = 0.0
+        for (M, N, K) in gemms:
+            key = (M, N, K)
+            if key not in timed:
+                a = torch.randn(M, K, dtype=torch.float16, device="cuda:0")
+                b = torch.randn(N, K, dtype=torch.float16, device="cuda:0")
+                for _ in range(3):
+                    torch.mm(a, b.t())
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(reps):
+                    torch.mm(a, b.t())
+                e1.record()
+                torch.cuda.synchronize()
+                timed[key] = 1e3 * e0.elapsed_time(e1) / reps
+                del a, b
+            us += timed[key]
+            flop += 2.0 * M * N * K
+        out[cls] = {"gemms": [list(g) for g in gemms], "blas_us": round(us, 2),
+                    "tflops": round(flop / us / 1e6, 1),
+                    "frac": round(flop / us / 1e6 / PEAK_F16_TFLOPS, 4)}
+    return out
 
 
 def cpu_baseline(name: str, cfg: dict, weights: dict, budget_s: float) -> dict:
@@ -728,6 +793,9 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true",
                     help="run every step through decode_chunk_graph (host codes, one graph "
                          "launch per step, captured once per frame bucket)")
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="also time the decoder's contractions as plain dense fp16 GEMMs on the "
+                         "vendor library (torch.mm) at the workload's mean frames per step")
     ap.add_argument("--stateless", action="store_true",
                     help="comparison: decode every chunk again from zero state with up to 16 "
                          "left frames (the pages' stateless variant) instead of carrying state")
@@ -974,6 +1042,11 @@ def main() -> int:
         out["graph_latency"] = glat
     if graph_info:
         out["graphs"] = graph_info
+    if args.blas_reference:
+        out["blas_reference"] = blas_reference(torch, cfg, int(round(frames / args.steps)))
+        for k, v in out["blas_reference"].items():
+            if k in kernels:
+                v["library_us"] = round(kernels[k]["avg_us"], 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.config, cfg, w, args.cpu_baseline_seconds)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 2)
