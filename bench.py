@@ -47,7 +47,13 @@ def layer_model(cfg: dict) -> dict:
     m = {}
     m["rvq_gather"] = dict(fpr=K * dcb, bpr=K * dcb * 2 + K * 4 + dcb * es, wpl=0)
     m["proj"] = dict(fpr=2 * dl * dcb, bpr=es * (dcb + dl), wpl=es * dl * dcb)
-    m["in_conv"] = dict(fpr=2 * ch[0] * 7 * dl, bpr=es * (dl + ch[0]), wpl=es * ch[0] * 7 * dl)
+    # the input conv reads the latent, or (projection folded into it, decoders
+    # without a transformer) [z, 1, 0...] padded to a multiple of the K stage
+    # (64 deep for fp16, 16 for fp32)
+    gran = 64 if es == 2 else 16
+    d_in = dl if cfg["tf_layers"] else (dcb + 1 + gran - 1) // gran * gran
+    m["in_conv"] = dict(fpr=2 * ch[0] * 7 * dl, bpr=es * (d_in + ch[0]),
+                        wpl=es * ch[0] * 7 * d_in)
     for i, s in enumerate(cfg["strides"]):
         ci, co = ch[i], ch[i + 1]
         m[f"s{i}.convT"] = dict(fpr=2 * s * co * 2 * ci, bpr=es * ci + s * co * (4 + es),
@@ -86,11 +92,6 @@ def layer_model(cfg: dict) -> dict:
             # conv's, each stage input's, and the residual-unit inputs of the
             # stages without a fused kernel (widths above 64 channels)
             fused = [es == 2 and cfg["act"] == "snake" and ch[k + 1] <= 64 for k in range(S)]
-            # the input conv's operand: the latent, or (projection folded into
-            # the input conv, decoders without a transformer) [z, 1, 0...]
-            # padded to a multiple of the 64-deep (fp16) / 16-deep K stage
-            gran = 64 if es == 2 else 16
-            d_in = dl if cfg["tf_layers"] else (dcb + 1 + gran - 1) // gran * gran
             per_stream = 6 * d_in + sum(ch[:S]) + sum(24 * ch[k + 1] for k in range(S)
                                                        if not fused[k])
             wpl += 2 * es * per_stream * cfg["n_streams"]
@@ -453,6 +454,68 @@ def kernel_class(name: str, cfg: dict) -> str:
     return ""
 
 
+def launch_sequence(cfg: dict) -> list:
+    """Launch classes of one decode call of a decoder without a transformer,
+    in the order the library enqueues them (split-K reductions and runtime
+    copies aside): the gather, the input conv (the projection folded in), then
+    per stage either its fused kernel or the ConvT and the residual units (one
+    launch each at 128 channels, two below)."""
+    import rvq_inputs as RI
+    if cfg["tf_layers"]:
+        raise SystemExit("launch_sequence: decoders without a transformer only")
+    ch = RI.channels(cfg)
+    es = 2 if cfg["weight_dtype"] == "bf16" else 4
+    seq = ["rvq_gather", "in_conv"]
+    for i in range(len(cfg["strides"])):
+        if es == 2 and cfg["act"] == "snake" and ch[i + 1] <= 64:
+            seq.append(f"s{i}.fused")
+            continue
+        seq.append(f"s{i}.convT")
+        for j in range(2):
+            if es == 2 and ch[i + 1] == 128:
+                seq.append(f"s{i}.ru{j}")
+            else:
+                seq += [f"s{i}.ru{j}.conv7", f"s{i}.ru{j}.conv1"]
+    return seq
+
+
+def label_dispatches(rows: list, cfg: dict) -> list:
+    """(class, row) for the library's dispatches of whole decode calls: each
+    call opens with its gather launch; a split-K reduction is counted with the
+    launch it completes; runtime copies are left out."""
+    seq = launch_sequence(cfg)
+    out, pos = [], None
+    for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
+        name = r["Kernel_Name"]
+        if "snrvq" not in name:
+            continue
+        if "rvq_gather" in name:
+            pos = 0
+        elif pos is None:
+            continue
+        elif "splitk_reduce" in name:
+            out.append((out[-1][0], r))
+            continue
+        else:
+            pos += 1
+        if pos >= len(seq):
+            raise SystemExit("label_dispatches: more launches in a call than the sequence")
+        want = kernel_class(name, cfg)
+        if want and want != seq[pos]:
+            raise SystemExit(f"label_dispatches: launch {pos} is {want}, expected {seq[pos]}")
+        out.append((seq[pos], r))
+    return out
+
+
+def calls_per_step(name: str, cfg: dict) -> int:
+    """Decode calls one step of the workload makes: the offline workload
+    groups its utterances into several calls, the streaming ones make one."""
+    if name != "c5":
+        return 1
+    import rvq_inputs as RI
+    return len(group_calls(RI.c5_lengths(cfg), None, cfg["max_frames_per_call"]))
+
+
 def _steady(rows: list, n_steps: int) -> list:
     """Dispatches of the decode steps: the last n_steps decode calls, each
     opened by its gather launch (the first kernel of every call), and
@@ -587,7 +650,8 @@ def rocprof_summary(args) -> int:
     if args.kt:
         rows = list(csv.DictReader(open(os.path.join(args.kt, "kt_kernel_trace.csv"))))
         idx = step_indices(args.kt_warmup, args.kt_steps, True)
-        st = _steady(rows, len(idx))
+        cps = calls_per_step(args.config, cfg)
+        st = _steady(rows, len(idx) * cps)
         agg = {}
         for r in st:
             d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
@@ -622,6 +686,22 @@ def rocprof_summary(args) -> int:
                     out.append(f"| {cls} | {v['avg_us']:.1f} | {ks[cls]['avg_us']:.1f} |")
             res["bench_value"] = rec.get("value")
             out.append(f"\nThat run's throughput under the tracer: {rec.get('value')} frames/s.\n")
+            if ks:
+                tot_k = sum(v["ms_total"] for v in ks.values())
+                out.append("Every launch class of the library over that profiled pass "
+                           "(HIP events around each launch):\n")
+                out.append("| class | launches | avg us | total ms | % |")
+                out.append("|---|---:|---:|---:|---:|")
+                for cls, v in sorted(ks.items(), key=lambda kv: -kv[1]["ms_total"]):
+                    out.append(f"| {cls} | {v['launches']} | {v['avg_us']:.1f} | "
+                               f"{v['ms_total']:.3f} | {100 * v['ms_total'] / tot_k:.1f} |")
+                tf = sum(v["ms_total"] for c, v in ks.items() if c.startswith("tf."))
+                if tf:
+                    res["transformer_share"] = round(tf / tot_k, 4)
+                    out.append(f"\nThe transformer's launches (tf.*) take {100 * tf / tot_k:.1f}% "
+                               "of the library's kernel time.\n")
+                else:
+                    out.append("")
         stats = os.path.join(args.kt, "kt_kernel_stats.csv")
         if os.path.exists(stats):
             srows = list(csv.DictReader(open(stats)))[:8]
@@ -687,7 +767,43 @@ def rocprof_summary(args) -> int:
             out.append(f"| {cls} | {n} | {c['units']} | {f:.1f} | {w:.1f} | {f + w:.1f} | "
                        f"{alg:.1f} |")
             res["traffic"][cls] = {"bytes_per_unit": round(f + w, 3)}
+        # every launch class, by launch order within each call
+        by_cls = {}
+        for tag, path in (("FETCH_SIZE", args.pmc_fetch), ("WRITE_SIZE", args.pmc_write)):
+            fn = [f for f in os.listdir(path) if f.endswith("counter_collection.csv")][0]
+            rows = [r for r in csv.DictReader(open(os.path.join(path, fn)))
+                    if r["Counter_Name"] == tag]
+            factor = res[f"{tag}_factor"]
+            for cls, r in label_dispatches(_steady(rows, len(idx)), cfg):
+                c = by_cls.setdefault(cls, {"FETCH_SIZE": 0.0, "WRITE_SIZE": 0.0, "ns": 0})
+                c[tag] += float(r["Counter_Value"]) * 1024.0 * factor
+                if tag == "FETCH_SIZE":
+                    c["ns"] += int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
         nsteps = len(idx)
+        mean_f = sum(frames) / nsteps
+        out.append(f"\nEvery launch class, per step ({mean_f:.0f} frames), against the bytes "
+                   "it must move (its operands, outputs and weights once):\n")
+        out.append("| class | fetch MB | write MB | total MB | algorithmic MB | ratio | "
+                   "GB/s over its own time |")
+        out.append("|---|---:|---:|---:|---:|---:|---:|")
+        res["traffic_by_class"] = {}
+        for cls in launch_sequence(cfg):
+            if cls not in by_cls:
+                continue
+            c = by_cls[cls]
+            f, w = c["FETCH_SIZE"] / nsteps, c["WRITE_SIZE"] / nsteps
+            # the unit rows of a class: frames, a ConvT's input rows, else the
+            # stage's output rows
+            i = 0 if cls in ("rvq_gather", "in_conv") else int(cls[1:cls.index(".")]) + (
+                0 if cls.endswith(".convT") else 1)
+            alg = mean_f * rate[i] * lm[cls]["bpr"] + lm[cls]["wpl"] if cls in lm else None
+            t = c["ns"] * 1e-9 / nsteps
+            out.append(f"| {cls} | {f / 1e6:.1f} | {w / 1e6:.1f} | {(f + w) / 1e6:.1f} | "
+                       + (f"{alg / 1e6:.1f} | {(f + w) / alg:.2f} | " if alg else "| | ")
+                       + f"{(f + w) / t / 1e9:.0f} |")
+            res["traffic_by_class"][cls] = {"bytes_per_step": round(f + w),
+                                            "algorithmic_bytes_per_step":
+                                                round(alg) if alg else None}
         step_b = (whole["FETCH_SIZE"] + whole["WRITE_SIZE"]) / nsteps
         step_s = whole["kernel_ns"] * 1e-9 / nsteps
         out.append(f"\nWhole decode step (every dispatch of the {nsteps} counted steps, "
