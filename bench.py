@@ -527,6 +527,42 @@ def _steady(rows: list, n_steps: int) -> list:
     return [r for r in rows if int(r["Dispatch_Id"]) >= first]
 
 
+def counter_table(path: str, args, cfg: dict, out: list, res: dict) -> None:
+    """Per launch class, the counters of one rocprofv3 --pmc run over the
+    decode steps, summed over each class's dispatches and divided by the
+    steps; the classes' kernel time beside them."""
+    import csv
+    fn = [f for f in os.listdir(path) if f.endswith("counter_collection.csv")][0]
+    disp = {}
+    for r in csv.DictReader(open(os.path.join(path, fn))):
+        d = disp.setdefault(int(r["Dispatch_Id"]), {
+            "Kernel_Name": r["Kernel_Name"], "Dispatch_Id": r["Dispatch_Id"],
+            "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), "c": {}})
+        d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    idx = step_indices(args.pmc_warmup, args.pmc_steps, False)
+    names = sorted({k for d in disp.values() for k in d["c"]})
+    agg = {}
+    for cls, d in label_dispatches(_steady(list(disp.values()), len(idx)), cfg):
+        a = agg.setdefault(cls, {"ns": 0, **{k: 0.0 for k in names}})
+        a["ns"] += d["ns"]
+        for k, v in d["c"].items():
+            a[k] += v
+    n = len(idx)
+    out.append(f"## Counters per launch class ({', '.join(names)}), per step\n")
+    out.append("| class | us | " + " | ".join(names) + " |")
+    out.append("|---|---:|" + "---:|" * len(names))
+    tab = res.setdefault("counters", {})
+    for cls in launch_sequence(cfg):
+        if cls not in agg:
+            continue
+        a = agg[cls]
+        out.append(f"| {cls} | {a['ns'] / n / 1e3:.1f} | " +
+                   " | ".join(f"{a[k] / n:.4g}" for k in names) + " |")
+        t = tab.setdefault(cls, {"us": round(a["ns"] / n / 1e3, 2)})
+        t.update({k: a[k] / n for k in names})
+    out.append("")
+
+
 def mfma_summary(args, cfg: dict, out: list, res: dict) -> None:
     """Matrix-core use over the decode steps of a counter run with
     SQ_INSTS_MFMA and SQ_VALU_MFMA_BUSY_CYCLES: MFMA instructions (every one a
@@ -828,6 +864,8 @@ def rocprof_summary(args) -> int:
                    "source matches.\n")
     if args.pmc_mfma:
         mfma_summary(args, cfg, out, res)
+    for path in args.pmc_any or []:
+        counter_table(path, args, cfg, out, res)
     if args.cotenant_trace:
         out.append("## Decode kernels alone and beside the GEMM load\n")
         out += cotenant_trace_summary(args.cotenant_trace)
@@ -928,6 +966,9 @@ def main() -> int:
     ap.add_argument("--kt-warmup", type=int, default=2)
     ap.add_argument("--pmc-fetch", help="rocprofv3 --pmc FETCH_SIZE output directory")
     ap.add_argument("--pmc-write", help="rocprofv3 --pmc WRITE_SIZE output directory")
+    ap.add_argument("--pmc-any", action="append",
+                    help="rocprofv3 --pmc output directory of any counters: a per-class table "
+                         "over the decode steps (repeatable)")
     ap.add_argument("--pmc-mfma", help="rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES "
                     "output directory")
     ap.add_argument("--cotenant-trace", help="rocprofv3 --kernel-trace output directory of a "

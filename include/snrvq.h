@@ -103,9 +103,13 @@ typedef struct {
  * never split a contraction over K (a split sums partials in another order,
  * so without splits every tile choice gives bit-identical output).
  * TWO_STAGE_BUFFERS: only tiles that double-buffer their K stages (not the
- * three-buffer 128 x 64 / 64 x 128 tiles). */
+ * three-buffer 128 x 64 / 64 x 128 tiles).  NO_TALL_TILES: never the
+ * 160-row tiles that replace 128 x 128 ones where those would leave a small
+ * last round of work-groups (the rows of a tile do not change any sum, so
+ * this too gives bit-identical output). */
 #define CODEC_FLAG_NO_SPLIT_K 2
 #define CODEC_FLAG_TWO_STAGE_BUFFERS 4
+#define CODEC_FLAG_NO_TALL_TILES 8
 
 typedef struct {
     int32_t hop;                 /* PCM samples per frame */
@@ -302,8 +306,8 @@ int codec_initial_chunk_size(int64_t requested, int32_t has_request, int32_t ste
 /* Test-only: the conv GEMM planner's choice for one launch shape -- host
  * logic only, no device or codec needed.  M output rows, N output columns,
  * Cin input channels per tap, taps; fp16 = 1 for fp16 operands (0: fp32);
- * n_cu compute units; flags: CODEC_FLAG_NO_SPLIT_K and/or
- * CODEC_FLAG_TWO_STAGE_BUFFERS.  *tile receives the tile's name (a static
+ * n_cu compute units; flags: any of CODEC_FLAG_NO_SPLIT_K,
+ * CODEC_FLAG_TWO_STAGE_BUFFERS and CODEC_FLAG_NO_TALL_TILES.  *tile receives the tile's name (a static
  * string; "none" when no tile fits the shape), *splits the number of K
  * splits (1: unsplit), for the split-K workspace every codec allocates.
  * CODEC_EINVAL for non-positive sizes or NULL outputs. */

@@ -25,6 +25,7 @@ CAPTURE_LATENT, CAPTURE_DEC_INPUT, CAPTURE_RVQ_SUM, CAPTURE_LAYER0 = 0, 1, 2, 3
 FLAG_PER_LAYER = 1
 FLAG_NO_SPLIT_K = 2
 FLAG_TWO_STAGE_BUFFERS = 4
+FLAG_NO_TALL_TILES = 8
 MAX_STAGES = 8
 
 ERROR_NAMES = {1: "EINVAL", 2: "ESTREAM", 3: "EDUP", 4: "ERANGE", 5: "ENOSLOT", 6: "ETOOBIG",
@@ -159,6 +160,7 @@ def make_cfg(cfg: dict) -> codec_cfg:
     c.flags = (FLAG_PER_LAYER if cfg.get("per_layer", False) else 0) | \
         (FLAG_NO_SPLIT_K if cfg.get("no_split_k", False) else 0) | \
         (FLAG_TWO_STAGE_BUFFERS if cfg.get("two_stage_buffers", False) else 0) | \
+        (FLAG_NO_TALL_TILES if cfg.get("no_tall_tiles", False) else 0) | \
         sum(1 << (8 + i) for i in cfg.get("per_layer_stages", ()))
     return c
 

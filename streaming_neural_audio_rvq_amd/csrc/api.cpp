@@ -514,10 +514,11 @@ int timed(codec *c, const char *name, int64_t units, hipStream_t s, Fn &&fn)
     return CODEC_OK;
 }
 
-ConvArgs conv_args(codec *, const Lin &L, const void *A, int A_H, int rate_in, int M,
+ConvArgs conv_args(codec *c, const Lin &L, const void *A, int A_H, int rate_in, int M,
                    const StepMeta &m)
 {
     ConvArgs a{};
+    a.tall_allowed = !(c->cfg.flags & CODEC_FLAG_NO_TALL_TILES);
     a.A = A;
     a.Wt = L.Wt;
     a.bias = L.bias;
@@ -548,6 +549,7 @@ int run_conv(codec *c, const char *name, const ConvArgs &a0, hipStream_t s, bool
     ConvArgs a = a0;
     a.splits_allowed = allow_split && !(c->cfg.flags & CODEC_FLAG_NO_SPLIT_K);
     a.deep_allowed = !(c->cfg.flags & CODEC_FLAG_TWO_STAGE_BUFFERS);
+    a.tall_allowed = !(c->cfg.flags & CODEC_FLAG_NO_TALL_TILES);
     a.partial = c->partial_now;
     const ConvPlan plan = conv_gemm_plan(a, c->dtype, c->n_cu, c->partial_cap_now);
     return timed(c, name, (int64_t)a.M, s,
@@ -868,7 +870,7 @@ int enqueue_kernels(codec *c, int B, int F, const MetaLayout &ml, float *pcm, hi
                     set_act(c, a, c->a_out);
                 }
                 snprintf(nm, sizeof nm, "s%d.ru%d", i, j);
-                if ((rc = timed(c, nm, (int64_t)a.M, s, [&] { return launch_ru_gemm(a, s); })))
+                if ((rc = timed(c, nm, (int64_t)a.M, s, [&] { return launch_ru_gemm(a, c->n_cu, s); })))
                     return rc;
                 continue;
             }
@@ -2082,6 +2084,7 @@ int codec_debug_conv_plan(int32_t M, int32_t N, int32_t Cin, int32_t taps, int32
     a.rate_in = 1;
     a.splits_allowed = !(flags & CODEC_FLAG_NO_SPLIT_K);
     a.deep_allowed = !(flags & CODEC_FLAG_TWO_STAGE_BUFFERS);
+    a.tall_allowed = !(flags & CODEC_FLAG_NO_TALL_TILES);
     const int dt = fp16 ? 1 : 0;
     const ConvPlan p = conv_gemm_plan(a, dt, n_cu, kSplitKCap);
     *tile = conv_gemm_tile_name(dt, p.tile);

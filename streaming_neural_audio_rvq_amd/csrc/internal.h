@@ -75,6 +75,7 @@ struct ConvArgs {
     int splits;             // split-K count (set by the launcher)
     int splits_allowed;     // 1: the planner may split K
     int deep_allowed;       // 1: the planner may take the three-buffer tiles
+    int tall_allowed;       // 1: the planner may take the 160-row tiles
     float *partial;         // split-K partials [splits][M][N] fp32
     // residual unit in one launch (k = 7 conv -> act7 -> 1x1 conv -> epilogue):
     // A, Wt describe the k = 7 conv, bias and everything after it the 1x1
@@ -141,7 +142,7 @@ ConvPlan conv_gemm_plan(const ConvArgs &a, int dtype, int n_cu, long partial_cap
 // One residual unit x + conv1x1(act7(conv7(a))) with its epilogue, fp16
 // operands; ru_gemm_supported says for which widths it runs.
 bool ru_gemm_supported(int Cout, int dtype);
-hipError_t launch_ru_gemm(const ConvArgs &a, hipStream_t st);
+hipError_t launch_ru_gemm(const ConvArgs &a, int n_cu, hipStream_t st);
 const char *conv_gemm_tile_name(int dtype, int tile);
 
 hipError_t launch_halo_save(const HaloTable &t, void *state, const StepMeta &m, int B,

@@ -168,8 +168,12 @@ __device__ __forceinline__ int xcd_remap(int bid, int total)
     return x * q + (x < r ? x : r) + i;
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int KSUB, bool RU = false, int NBUF = 2>
-__global__ __launch_bounds__(256) void conv_gemm_kernel(ConvArgs p)
+// MINW: waves per SIMD the register allocation must leave room for (the
+// 160-row tiles ask for 2: left to itself the compiler gives them more than
+// 256 registers, i.e. one work-group per CU)
+template <typename T, int BM, int BN, int WM, int WN, int KSUB, bool RU = false, int NBUF = 2,
+          int MINW = 1>
+__global__ __launch_bounds__(256, MINW) void conv_gemm_kernel(ConvArgs p)
 {
     constexpr int BK0 = Traits<T>::BK;
     constexpr int BK = BK0 * KSUB;
@@ -665,7 +669,11 @@ const TileDesc H_TILES[] = {
     {32, 64, 32, "h32x64"},        {64, 32, 32, "h64x32"},
     // three stage buffers: two work-groups per CU still fit (74 KB of LDS each)
     {128, 64, 64, "h128x64k64b3", true}, {64, 128, 64, "h64x128k64b3", true},
+    // 160 rows: taken instead of 128 x 128 when that tile would leave a small
+    // last round of work-groups (see tall_rows below)
+    {160, 128, 64, "h160x128k64"},
 };
+constexpr int TILE_128 = 0, TILE_TALL = 10;
 // fp16 tiles tried first, unsplit: 128 x 128 (double-buffered), then the
 // three-buffer half tiles.  Timed alone on the 128-stream layer shapes, a
 // half tile with its loads three stages deep beats a split 128 x 128 tile on
@@ -685,11 +693,13 @@ const TileDesc F_TILES[] = {
 constexpr int NH = sizeof(H_TILES) / sizeof(H_TILES[0]);
 constexpr int NF = sizeof(F_TILES) / sizeof(F_TILES[0]);
 
-template <typename T, int BM, int BN, int WM, int WN, int KSUB, bool RU = false, int NBUF = 2>
+template <typename T, int BM, int BN, int WM, int WN, int KSUB, bool RU = false, int NBUF = 2,
+          int MINW = 1>
 hipError_t launch_t(const ConvArgs &a, hipStream_t st)
 {
     int ntm = (a.M + BM - 1) / BM, ntn = a.N / BN;
-    hipLaunchKernelGGL((conv_gemm_kernel<T, BM, BN, WM, WN, KSUB, RU, NBUF>), dim3(ntm * ntn, a.splits),
+    hipLaunchKernelGGL((conv_gemm_kernel<T, BM, BN, WM, WN, KSUB, RU, NBUF, MINW>),
+                       dim3(ntm * ntn, a.splits),
                        dim3(256), 0, st, a);
     return hipGetLastError();
 }
@@ -712,6 +722,26 @@ void set_division(ConvArgs &a)
 // Tile and split count for a launch: the preferred tile that gives at least
 // two work-groups per CU; failing that, split K (at least 8 K stages per
 // split, partials within the workspace) until the CUs are covered.
+// Work-groups of the 128 x 128 tile (and of its 160-row variant) that a CU
+// holds at once: two (66 and 74 KB of LDS, at most 256 registers per lane).
+// A launch runs in rounds of 2 n_cu work-groups; when the 128-row tiles
+// overflow a whole number of rounds by a few work-groups, those few run as
+// a round of their own (at 848 frames per step the 128-stream stage-1 k7
+// conv has 530 tiles: 52 us against 33 us at 500), so 160-row tiles are
+// taken when they fit in the whole rounds (424 tiles: 37 us).  Timed alone:
+// stage-1 ConvT / k7 / 1x1 convs at 848 frames 41 / 52 / 29 us -> 32 / 37 /
+// 23 us; the stage-2 residual units (one launch each) 78 -> 75 us.
+static bool tall_rows(const ConvArgs &a, int n_cu, int bn)
+{
+    if (!a.tall_allowed || a.N % bn != 0)
+        return false;
+    const long slots = 2L * n_cu;
+    const long wg = (long)((a.M + 127) / 128) * (a.N / bn);
+    const long tail = wg % slots;
+    const long wg_tall = (long)((a.M + 159) / 160) * (a.N / bn);
+    return tail > 0 && 4 * tail <= slots && wg_tall <= wg - tail;
+}
+
 ConvPlan conv_gemm_plan(const ConvArgs &a, int dtype, int n_cu, long partial_cap)
 {
     // A larger tile reads fewer LDS and L2 bytes per MFMA (a 64 x 64 wave
@@ -734,7 +764,7 @@ ConvPlan conv_gemm_plan(const ConvArgs &a, int dtype, int n_cu, long partial_cap
             if (a.N % t[i].BN != 0 || a.Cin % t[i].BK != 0 || (t[i].deep && !a.deep_allowed))
                 continue;
             if (4L * ((a.M + t[i].BM - 1) / t[i].BM) * (a.N / t[i].BN) >= (long)u[1] * n_cu)
-                return ConvPlan{i, 1};
+                return ConvPlan{i == TILE_128 && tall_rows(a, n_cu, 128) ? TILE_TALL : i, 1};
         }
         // Little work (at most 32 64 x 64 x 64 tile stages per CU: the layers
         // of steps of a few frames): the 64 x 64 tile, which pads the fewest
@@ -774,7 +804,7 @@ ConvPlan conv_gemm_plan(const ConvArgs &a, int dtype, int n_cu, long partial_cap
             continue;
         const long tiles = (long)((a.M + t[i].BM - 1) / t[i].BM) * (a.N / t[i].BN);
         if (tiles >= target)
-            return ConvPlan{i, 1};
+            return ConvPlan{dtype && i == TILE_128 && tall_rows(a, n_cu, 128) ? TILE_TALL : i, 1};
         if (tiles > best_work) {
             best_work = tiles;
             best = ConvPlan{i, 1};
@@ -827,6 +857,7 @@ hipError_t launch_conv_gemm(const ConvArgs &a0, int dtype, hipStream_t st, ConvP
         case 7: e = launch_t<half_t, 64, 32, 4, 1, 1>(a, st); break;
         case 8: e = launch_t<half_t, 128, 64, 2, 2, 2, false, 3>(a, st); break;
         case 9: e = launch_t<half_t, 64, 128, 2, 2, 2, false, 3>(a, st); break;
+        case 10: e = launch_t<half_t, 160, 128, 2, 2, 2, false, 2, 2>(a, st); break;
         }
     } else {
         switch (plan.tile) {
@@ -854,7 +885,7 @@ bool ru_gemm_supported(int Cout, int dtype)
     return dtype == 1 && Cout == 128;
 }
 
-hipError_t launch_ru_gemm(const ConvArgs &a0, hipStream_t st)
+hipError_t launch_ru_gemm(const ConvArgs &a0, int n_cu, hipStream_t st)
 {
     if (a0.M <= 0)
         return hipSuccess;
@@ -863,9 +894,13 @@ hipError_t launch_ru_gemm(const ConvArgs &a0, hipStream_t st)
     set_division(a);
     if (a.N != a.Cout || a.s != 1 || a.Cin % 64 != 0)
         return hipErrorInvalidValue;
-    if (a.Cout == 128)
-        return launch_t<half_t, 128, 128, 2, 2, 2, true>(a, st);
-    return hipErrorInvalidValue;
+    if (a.Cout != 128)
+        return hipErrorInvalidValue;
+    // 160-row tiles by the same rule as the plain 128 x 128 tile (81 KB of
+    // LDS: two still fit in a CU's 160 KB)
+    if (tall_rows(a, n_cu, 128))
+        return launch_t<half_t, 160, 128, 2, 2, 2, true, 2, 2>(a, st);
+    return launch_t<half_t, 128, 128, 2, 2, 2, true>(a, st);
 }
 
 }  // namespace snrvq

@@ -228,6 +228,36 @@ def test_three_buffer_tiles_bitwise_equal_double_buffered():
     assert e <= tol_for(cfg)
 
 
+def test_tall_tiles_bitwise_equal_128_row_tiles():
+    """The 160-row tiles change which rows a work-group holds, not the order
+    of any sum: 112 streams x 8 frames (896 frames, where the 128-row tiles of
+    the stage-1 convs, the stage-2 ConvT and the stage-2 residual units would
+    overflow whole rounds of two work-groups per CU by a few) decode bit for
+    bit as with 128-row tiles only, over two steps; stream 0 is also checked
+    against the oracle."""
+    cfg = RI.get_config("c2", max_streams=112, max_frames_per_call=1024, no_split_k=True)
+    B, plan = 112, [8, 8]
+    F = B * plan[0]
+    assert snr.conv_plan(F * 40, 256, 256, 7, flags=snr.FLAG_NO_SPLIT_K)[0] == "h160x128k64"
+    assert snr.conv_plan(F * 8, 5 * 256, 512, 2, flags=snr.FLAG_NO_SPLIT_K)[0] == "h160x128k64"
+    w = RI.make_weights(cfg)
+    codes = [RI.stream_codes(cfg, b, sum(plan)) for b in range(B)]
+    outs = []
+    for variant in (cfg, dict(cfg, no_tall_tiles=True)):
+        say(f"case tall tiles: no_tall_tiles={variant.get('no_tall_tiles', False)}")
+        codec = open_codec(variant, w)
+        ids = [codec.stream_open() for _ in range(B)]
+        outs.append(run_lockstep(codec, ids, codes, plan))
+        codec.close()
+    for x, y in zip(*outs):
+        assert np.isfinite(x).all()
+        assert np.array_equal(x, y)
+    ref = oracle.Model(cfg, w).decode_full(codes[0])
+    e, ac = rel_err(outs[0][0], ref)
+    say(f"stream 0: err/peak {e:.3e} AC-rel {ac:.3e}")
+    assert e <= tol_for(cfg)
+
+
 def test_c4_full_scale_sampled_parity():
     """The headline workload: 128 streams at staggered offsets (prefilled),
     steps of mixed chunk sizes {1,2,4,8,16}; sampled streams' chunks are

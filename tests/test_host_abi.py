@@ -161,6 +161,13 @@ def test_conv_planner_small_steps_take_64x64_tiles():
     assert snr.conv_plan(512 * 40, 256, 256, 7) == ("h128x128k64", 1)  # 320 tiles
     assert snr.conv_plan(512, 8 * 512, 1024, 2) == ("h128x64k64b3", 1)  # 256 tiles
     assert snr.conv_plan(512 * 8, 512, 512, 7) == ("h128x64k64b3", 1)
+    # 160-row tiles where 128 x 128 tiles would overflow whole rounds of two
+    # work-groups per CU by a few (the 128-stream steps above ~819 frames)
+    assert snr.conv_plan(800 * 40, 256, 256, 7) == ("h128x128k64", 1)    # 500 tiles
+    assert snr.conv_plan(848 * 40, 256, 256, 7) == ("h160x128k64", 1)    # 530 -> 424
+    assert snr.conv_plan(848 * 8, 5 * 256, 512, 2) == ("h160x128k64", 1)  # 530 -> 430
+    assert snr.conv_plan(848 * 40, 256, 256, 7, flags=snr.FLAG_NO_TALL_TILES) == \
+        ("h128x128k64", 1)
     # no split where the flags forbid it; the 794-frame input conv keeps the large tiles
     assert snr.conv_plan(8, 1024, 1024, 7, flags=snr.FLAG_NO_SPLIT_K) == ("h64x64k64", 1)
     assert snr.conv_plan(794, 1024, 1024, 7)[0] != "h64x64k64"
@@ -177,7 +184,7 @@ def test_conv_planner_flags_and_invariants():
         N = int(rng.choice([32, 64, 128, 192, 256, 512, 1024, 1280, 1536, 2048, 4096]))
         Cin = int(rng.choice([32, 64, 128, 256, 512, 1024]))
         taps = int(rng.choice([1, 2, 7]))
-        flags = int(rng.choice([0, NO_SPLIT, TWO_BUF, NO_SPLIT | TWO_BUF]))
+        flags = int(rng.choice([0, NO_SPLIT, TWO_BUF, NO_SPLIT | TWO_BUF, snr.FLAG_NO_TALL_TILES]))
         tile, sp = snr.conv_plan(M, N, Cin, taps, flags=flags)
         bm, bn, bk = (int(v) for v in re.match(r"h(\d+)x(\d+)(?:k(\d+))?", tile).groups("32"))
         assert N % bn == 0 and Cin % bk == 0, (M, N, Cin, taps, tile)
@@ -187,6 +194,10 @@ def test_conv_planner_flags_and_invariants():
             assert sp == 1
         if flags & TWO_BUF:
             assert not tile.endswith("b3")
+        if flags & snr.FLAG_NO_TALL_TILES:
+            assert not tile.startswith("h160")
+        if tile.startswith("h160"):  # only in place of an unsplit 128 x 128 tile
+            assert sp == 1 and N % 128 == 0
     with pytest.raises(ValueError):
         snr.conv_plan(0, 64, 64, 1)
 
