@@ -101,6 +101,36 @@ def layer_model(cfg: dict) -> dict:
     return m
 
 
+# Vector ALU of the part: 256 CUs x 4 SIMDs, a wave64 instruction every 4
+# cycles per SIMD (16 lanes per cycle) at 2.4 GHz, i.e. 39.3 T lane-operations
+# per second (the published 157.3 TFLOP/s fp32 counts an FMA as two and packed
+# instructions twice); transcendentals (the hardware sine) at a quarter of it.
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+
+
+def vector_floor(cfg: dict, cls: str, units: float, flops: float, peak_tflops: float,
+                 sec: float) -> dict:
+    """The vector-ALU work a fused stage cannot avoid beside its MFMAs: five
+    activations per output row and channel (the two residual units' input and
+    inner activations, and the stage output's), each a Snake -- multiply, range
+    reduction, sine, square, fused multiply-add: four full-rate instructions
+    and one quarter-rate one, 8 lane-operation slots -- plus half a
+    conversion instruction (two values packed to fp16 per instruction).  The
+    floor is that work at the full vector rate; MFMA work at the published
+    peak beside it; the two overlapped at best, serial at worst."""
+    import rvq_inputs as RI
+    ch = RI.channels(cfg)
+    i = int(cls[1:cls.index(".")])
+    snakes = units * 5 * ch[i + 1]
+    slots = snakes * (4 + 4 + 0.5) if cfg["act"] == "snake" else snakes * 2.5
+    valu_us = slots / VALU_LANE_OPS * 1e6
+    mfma_us = flops / (peak_tflops * 1e12) * 1e6
+    return {"activations_per_launch": int(snakes), "lane_op_slots_per_launch": int(slots),
+            "valu_floor_us": round(valu_us, 1), "mfma_floor_us": round(mfma_us, 1),
+            "serial_floor_us": round(valu_us + mfma_us, 1), "measured_us": round(sec * 1e6, 1),
+            "frac_of_serial_floor": round((valu_us + mfma_us) / (sec * 1e6), 3)}
+
+
 def flops_per_frame(cfg: dict) -> float:
     lm = layer_model(cfg)
     rate = [1]
@@ -235,23 +265,22 @@ def blas_reference(torch, cfg: dict, F: int, reps: int = 20) -> dict:
         r.append(r[-1] * st)
     dcb, dl = cfg["d_cb"], cfg["d_lat"]
     d_in = dl if cfg["tf_layers"] else (dcb + 1 + 63) // 64 * 64
-    classes = {"in_conv": [(F, ch[0], 7 * d_in)]}
     S = len(cfg["strides"])
+    shapes = {"in_conv": [(F, ch[0], 7 * d_in)]}
     for i, s in enumerate(cfg["strides"]):
         ci, co = ch[i], ch[i + 1]
         convT = (F * r[i], s * co, 2 * ci)
         conv7 = (F * r[i + 1], co, 7 * co)
         conv1 = (F * r[i + 1], co, co)
-        if co <= 64:  # one fused kernel per stage
-            g = [convT, conv7, conv1, conv7, conv1]
-            if i == S - 1:
-                g.append((F * r[S], 1, 7 * co))
-            classes[f"s{i}.fused"] = g
-        else:
-            classes[f"s{i}.convT"] = [convT]
-            for j in range(2):
-                classes[f"s{i}.ru{j}.conv7"] = [conv7]
-                classes[f"s{i}.ru{j}.conv1"] = [conv1]
+        shapes[f"s{i}.convT"] = [convT]
+        shapes[f"s{i}.fused"] = [convT, conv7, conv1, conv7, conv1] + (
+            [(F * r[S], 1, 7 * co)] if i == S - 1 else [])
+        for j in range(2):
+            shapes[f"s{i}.ru{j}"] = [conv7, conv1]
+            shapes[f"s{i}.ru{j}.conv7"] = [conv7]
+            shapes[f"s{i}.ru{j}.conv1"] = [conv1]
+    # the classes this library launches for the decoder, in launch order
+    classes = {c: shapes[c] for c in launch_sequence(cfg) if c in shapes}
     classes["square 8192"] = [(8192, 8192, 8192)]
     timed = {}
     out = {}
@@ -280,6 +309,23 @@ def blas_reference(torch, cfg: dict, F: int, reps: int = 20) -> dict:
                     "tflops": round(flop / us / 1e6, 1),
                     "frac": round(flop / us / 1e6 / PEAK_F16_TFLOPS, 4)}
     return out
+
+
+def write_blas_summary(path: str, out: dict, F: int) -> None:
+    """Appends the vendor-GEMM calibration of a run to a text summary: per
+    launch class, the library's own average (HIP events in the same run) and
+    the plain GEMMs of the same shapes on torch.mm."""
+    lines = [f"Run: {out['value']} frames/s, {out['ms_per_step']} ms per step; the plain GEMMs at "
+             f"F = {F} frames (the run's mean per step).\n",
+             "| class | GEMMs (M, N, K) | vendor GEMM us | TFLOP/s | of 2.5 PFLOP/s | "
+             "this library us |", "|---|---|---:|---:|---:|---:|"]
+    for cls, v in out["blas_reference"].items():
+        g = "; ".join("x".join(str(d) for d in gm) for gm in v["gemms"])
+        lib = f"{v['library_us']:.1f}" if "library_us" in v else "-"
+        lines.append(f"| {cls} | {g} | {v['blas_us']:.1f} | {v['tflops']:.0f} | {v['frac']:.3f} | "
+                     f"{lib} |")
+    with open(path, "a") as fh:
+        fh.write("\n".join(lines) + "\n")
 
 
 def cpu_baseline(name: str, cfg: dict, weights: dict, budget_s: float) -> dict:
@@ -866,6 +912,18 @@ def rocprof_summary(args) -> int:
         mfma_summary(args, cfg, out, res)
     for path in args.pmc_any or []:
         counter_table(path, args, cfg, out, res)
+    if args.blas_json:
+        lines = open(args.blas_json).read().splitlines()
+        rec = json.loads([ln for ln in lines if ln.startswith("{")][-1])
+        out.append("## Vendor GEMMs on the decoder's shapes\n")
+        tmp = args.rocprof_summary + ".blas.tmp" if args.rocprof_summary != "-" else None
+        F = int(round(rec["config"]["mean_frames_per_step"]))
+        if tmp:
+            write_blas_summary(tmp, rec, F)
+            out.append(open(tmp).read())
+            os.remove(tmp)
+        res["blas_reference"] = {k: {kk: v[kk] for kk in ("blas_us", "tflops", "frac", "library_us")
+                                     if kk in v} for k, v in rec["blas_reference"].items()}
     if args.cotenant_trace:
         out.append("## Decode kernels alone and beside the GEMM load\n")
         out += cotenant_trace_summary(args.cotenant_trace)
@@ -950,6 +1008,7 @@ def main() -> int:
     ap.add_argument("--blas-reference", action="store_true",
                     help="also time the decoder's contractions as plain dense fp16 GEMMs on the "
                          "vendor library (torch.mm) at the workload's mean frames per step")
+    ap.add_argument("--blas-summary", help="with --blas-reference: append its table to this file")
     ap.add_argument("--stateless", action="store_true",
                     help="comparison: decode every chunk again from zero state with up to 16 "
                          "left frames (the pages' stateless variant) instead of carrying state")
@@ -966,6 +1025,8 @@ def main() -> int:
     ap.add_argument("--kt-warmup", type=int, default=2)
     ap.add_argument("--pmc-fetch", help="rocprofv3 --pmc FETCH_SIZE output directory")
     ap.add_argument("--pmc-write", help="rocprofv3 --pmc WRITE_SIZE output directory")
+    ap.add_argument("--blas-json", help="with --rocprof-summary: the output of a --blas-reference run, "
+                         "tabulated")
     ap.add_argument("--pmc-any", action="append",
                     help="rocprofv3 --pmc output directory of any counters: a per-class table "
                          "over the decode steps (repeatable)")
@@ -1147,6 +1208,9 @@ def main() -> int:
         roof["avg_launch_us"] = round(d["avg_us"], 2)
         roof["alg_bytes_per_launch"] = int(d["bytes_per_launch"])
         roof["alg_flops_per_launch"] = int(d["flops_per_launch"])
+        if dom.endswith(".fused"):
+            roof["vector_alu"] = vector_floor(cfg, dom, d["units"] / d["launches"],
+                                              d["flops_per_launch"], peak_f, sec)
 
     glat = None
     if args.graph:
@@ -1204,6 +1268,8 @@ def main() -> int:
         for k, v in out["blas_reference"].items():
             if k in kernels:
                 v["library_us"] = round(kernels[k]["avg_us"], 2)
+        if args.blas_summary:
+            write_blas_summary(args.blas_summary, out, int(round(frames / args.steps)))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.config, cfg, w, args.cpu_baseline_seconds)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 2)
