@@ -719,9 +719,6 @@ void set_division(ConvArgs &a)
 
 }  // namespace
 
-// Tile and split count for a launch: the preferred tile that gives at least
-// two work-groups per CU; failing that, split K (at least 8 K stages per
-// split, partials within the workspace) until the CUs are covered.
 // Work-groups of the 128 x 128 tile (and of its 160-row variant) that a CU
 // holds at once: two (66 and 74 KB of LDS, at most 256 registers per lane).
 // A launch runs in rounds of 2 n_cu work-groups; when the 128-row tiles
@@ -742,6 +739,9 @@ static bool tall_rows(const ConvArgs &a, int n_cu, int bn)
     return tail > 0 && 4 * tail <= slots && wg_tall <= wg - tail;
 }
 
+// Tile and split count for a launch: the preferred tile that gives at least
+// two work-groups per CU; failing that, split K (at least 8 K stages per
+// split, partials within the workspace) until the CUs are covered.
 ConvPlan conv_gemm_plan(const ConvArgs &a, int dtype, int n_cu, long partial_cap)
 {
     // A larger tile reads fewer LDS and L2 bytes per MFMA (a 64 x 64 wave
