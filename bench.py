@@ -900,14 +900,10 @@ def rocprof_summary(args) -> int:
                            round(step_s * 1e6, 1), "GB_per_s": round(step_b / step_s / 1e9, 1),
                            "frames_per_step": sum(frames) / nsteps}
         res["library_source_sha256"] = source_digest()
-        src = os.path.join(ROOT, "streaming_neural_audio_rvq_amd", "csrc")
-        h = hashlib.sha256()
-        for fn in ("kernels_stage.hip", "internal.h"):
-            h.update(open(os.path.join(src, fn), "rb").read())
-        res["stage_source_sha256"] = h.hexdigest()
-        out.append("\nThe traffic holds for the kernel source whose SHA-256 (kernels_stage.hip "
-                   "then internal.h) is recorded below; bench.py reports it only while the "
-                   "source matches.\n")
+        res["stage_source_sha256"] = stage_digest()
+        out.append("\nThe traffic holds for the code whose SHA-256 is recorded below (the stage "
+                   "kernel's: kernels_stage.hip then internal.h; the whole library's), comments "
+                   "and whitespace aside; bench.py reports it only while the code matches.\n")
     if args.pmc_mfma:
         mfma_summary(args, cfg, out, res)
     for path in args.pmc_any or []:
@@ -949,23 +945,58 @@ def stored_traffic(cls: str, units_per_launch: float):
     if not mm:
         return None
     rec = json.loads(mm.group(1))
-    src = os.path.join(ROOT, "streaming_neural_audio_rvq_amd", "csrc")
-    h = hashlib.sha256()
-    for fn in ("kernels_stage.hip", "internal.h"):
-        h.update(open(os.path.join(src, fn), "rb").read())
     t = rec.get("traffic", {}).get(cls)
-    if rec.get("stage_source_sha256") != h.hexdigest() or not t:
+    if rec.get("stage_source_sha256") != stage_digest() or not t:
         return None
     return t["bytes_per_unit"] * units_per_launch
 
 
+def code_text(path: str) -> bytes:
+    """A C/C++/HIP source without its comments and with runs of whitespace
+    collapsed: what a digest of the code should see (string and character
+    literals are kept as they are)."""
+    src = open(path, encoding="utf-8").read()
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            while i < n and src[i] != "\n":
+                i += 1
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split()).encode()
+
+
+def stage_digest() -> str:
+    """SHA-256 over the fused stage kernel's code (kernels_stage.hip, then
+    internal.h; comments and whitespace do not count)."""
+    import hashlib
+    src = os.path.join(ROOT, "streaming_neural_audio_rvq_amd", "csrc")
+    h = hashlib.sha256()
+    for fn in ("kernels_stage.hip", "internal.h"):
+        h.update(code_text(os.path.join(src, fn)))
+    return h.hexdigest()
+
+
 def source_digest() -> str:
-    """SHA-256 over every library source file (name order)."""
+    """SHA-256 over every library source file's code (name order; comments
+    and whitespace do not count)."""
     import hashlib
     src = os.path.join(ROOT, "streaming_neural_audio_rvq_amd", "csrc")
     h = hashlib.sha256()
     for fn in sorted(os.listdir(src)):
-        h.update(open(os.path.join(src, fn), "rb").read())
+        h.update(code_text(os.path.join(src, fn)))
     return h.hexdigest()
 
 
