@@ -609,6 +609,44 @@ def counter_table(path: str, args, cfg: dict, out: list, res: dict) -> None:
     out.append("")
 
 
+def derived_table(args, cfg: dict, out: list, res: dict) -> None:
+    """Ratios per launch class from the counter tables, where their counters
+    were collected: matrix pipes busy (of the SIMD cycles at the nominal
+    2.4 GHz over the class's time), LDS / other-VALU / SALU instructions per
+    MFMA, the share of wave time spent waiting (SQ_WAIT_ANY over
+    SQ_WAVE_CYCLES), and the share of busy matrix-pipe cycles in which a
+    VALU instruction issued beside it."""
+    tab = res.get("counters", {})
+    need = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_INSTS_VALU",
+            "SQ_INSTS_SALU", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES")
+    rows = [(c, v) for c, v in tab.items() if all(k in v for k in need)]
+    if not rows:
+        return
+    n_simd = 4 * args.n_cu
+    out.append("## Derived per launch class\n")
+    out.append("| class | us | MFMA busy at 2.4 GHz | LDS instr / MFMA | other VALU / MFMA | "
+               "SALU / MFMA | waiting share of wave time | VALU beside busy MFMA |")
+    out.append("|---|---:|---:|---:|---:|---:|---:|---:|")
+    der = res.setdefault("derived", {})
+    for c, v in rows:
+        m = max(v["SQ_INSTS_MFMA"], 1.0)
+        busy = v["SQ_VALU_MFMA_BUSY_CYCLES"] / (n_simd * v["us"] * 2400.0)
+        d = {"mfma_busy": busy, "lds_per_mfma": v["SQ_INSTS_LDS"] / m,
+             "valu_per_mfma": (v["SQ_INSTS_VALU"] - v["SQ_INSTS_MFMA"]) / m,
+             "salu_per_mfma": v["SQ_INSTS_SALU"] / m,
+             "wait_share": v["SQ_WAIT_ANY"] / max(v["SQ_WAVE_CYCLES"], 1.0),
+             "coexec_share": v["SQ_VALU_MFMA_COEXEC_CYCLES"] /
+             max(v["SQ_VALU_MFMA_BUSY_CYCLES"], 1.0)}
+        if v["SQ_INSTS_MFMA"] == 0:
+            out.append(f"| {c} | {v['us']:.1f} | 0 | - | - | - | {d['wait_share']:.2f} | - |")
+        else:
+            out.append(f"| {c} | {v['us']:.1f} | {busy:.3f} | {d['lds_per_mfma']:.2f} | "
+                       f"{d['valu_per_mfma']:.2f} | {d['salu_per_mfma']:.2f} | "
+                       f"{d['wait_share']:.2f} | {d['coexec_share']:.3f} |")
+        der[c] = {k: round(x, 4) for k, x in d.items()}
+    out.append("")
+
+
 def mfma_summary(args, cfg: dict, out: list, res: dict) -> None:
     """Matrix-core use over the decode steps of a counter run with
     SQ_INSTS_MFMA and SQ_VALU_MFMA_BUSY_CYCLES: MFMA instructions (every one a
@@ -908,6 +946,8 @@ def rocprof_summary(args) -> int:
         mfma_summary(args, cfg, out, res)
     for path in args.pmc_any or []:
         counter_table(path, args, cfg, out, res)
+    if args.pmc_any:
+        derived_table(args, cfg, out, res)
     if args.blas_json:
         lines = open(args.blas_json).read().splitlines()
         rec = json.loads([ln for ln in lines if ln.startswith("{")][-1])
