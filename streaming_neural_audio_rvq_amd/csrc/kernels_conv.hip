@@ -288,18 +288,27 @@ __global__ __launch_bounds__(256, MINW) void conv_gemm_kernel(ConvArgs p)
     }
 
     Chunk ra[DIRECT ? 1 : A_N], rb[DIRECT ? 1 : B_N];
-    // a K stage of BK never straddles two taps (C_in is a multiple of BK);
-    // the (tap, channel) of the next stage advances without a division
-    int g_tap = (ks0 * BK) / p.Cin, g_c0 = ks0 * BK - g_tap * p.Cin;
-    auto gload = [&](int ks, T *Ab, T *Bb) {
-        const int k0 = ks * BK;
-        const int tap = g_tap, c0 = g_c0;
+    // a K stage of BK never straddles two taps (C_in is a multiple of BK).
+    // Stages are loaded in order, so the element offsets of the next stage's
+    // loads advance by BK, and by dil Cin - Cin more where a tap ends (the A
+    // rows of tap t sit (taps - 1 - t) dil rows back): a few scalar adds per
+    // stage, no division or 64-bit multiply
+    int g_c0, a_off, b_off = ks0 * BK;
+    {
+        const int tap0 = (ks0 * BK) / p.Cin;
+        g_c0 = ks0 * BK - tap0 * p.Cin;
+        a_off = g_c0 - (p.taps - 1 - tap0) * p.dil * p.Cin;
+    }
+    const int tap_jump = (p.dil - 1) * p.Cin;
+    auto gload = [&](T *Ab, T *Bb) {
+        const int off = a_off, k0 = b_off;
+        a_off += BK;
+        b_off += BK;
         g_c0 += BK;
         if (g_c0 == p.Cin) {
             g_c0 = 0;
-            g_tap++;
+            a_off += tap_jump;
         }
-        long off = (long)c0 - (long)(p.taps - 1 - tap) * p.dil * p.Cin;
         if constexpr (DIRECT) {
 #pragma unroll
             for (int i = 0; i < A_N; i++)
@@ -421,14 +430,19 @@ __global__ __launch_bounds__(256, MINW) void conv_gemm_kernel(ConvArgs p)
         // of LPS times the number of younger stages in flight
         static_assert(A_FULL && B_FULL, "uniform loads per wave");
         constexpr int LPS = A_N + B_N;
-        auto bufA = [&](int j) { return (T *)(smem + (j % NBUF) * SMEM_BUF); };
-        auto bufB = [&](int j) { return bufA(j) + BM * LD; };
+        // byte offsets of the buffer read next and of the one loaded next,
+        // each stepping through the NBUF buffers in turn
+        int rd = 0, wr = 0;
+        auto step = [](int o) { return o + SMEM_BUF == NBUF * SMEM_BUF ? 0 : o + SMEM_BUF; };
+        auto bufA = [&](int o) { return (T *)(smem + o); };
+        auto bufB = [&](int o) { return bufA(o) + BM * LD; };
         load_bias();
         int issued = ks0;
 #pragma unroll
         for (int i = 0; i < NBUF - 1; i++)
             if (issued < ks1) {
-                gload(issued, bufA(issued - ks0), bufB(issued - ks0));
+                gload(bufA(wr), bufB(wr));
+                wr = step(wr);
                 issued++;
             }
         if (ks0 >= ks1) {
@@ -453,17 +467,19 @@ __global__ __launch_bounds__(256, MINW) void conv_gemm_kernel(ConvArgs p)
             // (its release fence waits for every outstanding memory op)
             __asm__ volatile("s_barrier" ::: "memory");
             if (issued < ks1) {
-                gload(issued, bufA(issued - ks0), bufB(issued - ks0));
+                gload(bufA(wr), bufB(wr));
+                wr = step(wr);
                 issued++;
             }
             if (ks == ks0)
                 mma_stage(bufA(0), bufB(0), std::true_type());
             else
-                mma_stage(bufA(ks - ks0), bufB(ks - ks0), std::false_type());
+                mma_stage(bufA(rd), bufB(rd), std::false_type());
+            rd = step(rd);
         }
     } else {  // two stage buffers
         if (ks0 < ks1) {
-            gload(ks0, A0, B0);
+            gload(A0, B0);
             sstore(A0, B0);
         }
         load_bias();
@@ -472,7 +488,7 @@ __global__ __launch_bounds__(256, MINW) void conv_gemm_kernel(ConvArgs p)
         // first K stage (buffer 0) peeled: its MFMAs start from the bias
         if (ks0 < ks1) {
             if (ks0 + 1 < ks1)
-                gload(ks0 + 1, A1, B1);
+                gload(A1, B1);
             mma_stage(A0, B0, std::true_type());
             if (ks0 + 1 < ks1)
                 sstore(A1, B1);
@@ -490,7 +506,7 @@ __global__ __launch_bounds__(256, MINW) void conv_gemm_kernel(ConvArgs p)
             T *const Ac = buf ? A1 : A0, *const Bc = buf ? B1 : B0;
             T *const An = buf ? A0 : A1, *const Bn = buf ? B0 : B1;
             if (ks + 1 < ks1)
-                gload(ks + 1, An, Bn);
+                gload(An, Bn);
             mma_stage(Ac, Bc, std::false_type());
             if (ks + 1 < ks1)
                 sstore(An, Bn);
