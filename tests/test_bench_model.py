@@ -55,3 +55,23 @@ def test_flops_per_frame_values():
     assert b.flops_per_frame(RI.get_config("c2")) / 1e6 == pytest.approx(467.476, abs=1e-3)
     assert b.flops_per_frame(RI.get_config("c3")) / 1e6 == pytest.approx(715.26, abs=0.01)
     assert b.flops_per_frame(RI.get_config("c1")) / 1e6 == pytest.approx(0.3927, abs=1e-4)
+
+
+def test_code_digest_ignores_comments_not_code(tmp_path):
+    """The provenance digest that ties stored counter summaries to the
+    library's code: comments and whitespace do not change it, code and string
+    literals do."""
+    b = _bench()
+    a = tmp_path / "a.hip"
+    a.write_text('int f() { return 1; } // one\n/* block\n comment */ const char *s = "a//b";\n')
+    c = tmp_path / "c.hip"
+    c.write_text('int f()  {\n  return 1;   }\nconst char *s = "a//b"; // other words\n')
+    d = tmp_path / "d.hip"
+    d.write_text('int f() { return 2; }\nconst char *s = "a//b";\n')
+    e = tmp_path / "e.hip"
+    e.write_text('int f() { return 1; }\nconst char *s = "a/b";\n')
+    assert b.code_text(str(a)) == b.code_text(str(c))
+    assert b.code_text(str(a)) != b.code_text(str(d))
+    assert b.code_text(str(a)) != b.code_text(str(e))
+    assert b"//" in b.code_text(str(a))  # inside the string literal
+    assert b"one" not in b.code_text(str(a)) and b"block" not in b.code_text(str(a))
