@@ -311,6 +311,38 @@ def blas_reference(torch, cfg: dict, F: int, reps: int = 20) -> dict:
     return out
 
 
+# (config, timed steps, warm-up steps) of the short runs beside the headline
+OTHER_RUNS = (("c2", 32, 4), ("c3", 16, 2), ("c5", 3, 1))
+
+
+def other_workloads() -> dict:
+    """Short runs of the other workloads (child processes of this script, one
+    at a time, each under its own time limit): frames/s, audio-s/s and ms per
+    step of each, or the reason it has none."""
+    import subprocess
+    res = {}
+    for name, steps, warmup in OTHER_RUNS:
+        cmd = [sys.executable, os.path.abspath(__file__), "--config", name, "--steps",
+               str(steps), "--warmup", str(warmup), "--no-cpu-baseline", "--no-profile",
+               "--no-other-configs"]
+        print(f"bench.py: {name} ({steps} steps)", file=sys.stderr, flush=True)
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+        except subprocess.TimeoutExpired:
+            res[name] = {"error": "time limit"}
+            continue
+        lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+        if r.returncode != 0 or not lines:
+            res[name] = {"error": f"exit {r.returncode}", "stderr": r.stderr[-300:]}
+            continue
+        rec = json.loads(lines[-1])
+        res[name] = {k: rec[k] for k in ("value", "unit", "ms_per_step", "audio_sec_per_s")
+                     if k in rec}
+        res[name]["workload"] = rec["config"]["workload"]
+        res[name]["steps"] = steps
+    return res
+
+
 def write_blas_summary(path: str, out: dict, F: int) -> None:
     """Appends the vendor-GEMM calibration of a run to a text summary: per
     launch class, the library's own average (HIP events in the same run) and
@@ -1080,6 +1112,9 @@ def main() -> int:
                     help="also time the decoder's contractions as plain dense fp16 GEMMs on the "
                          "vendor library (torch.mm) at the workload's mean frames per step")
     ap.add_argument("--blas-summary", help="with --blas-reference: append its table to this file")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the short runs of the other workloads (c2, c3, c5) that the "
+                         "default 128-stream run reports beside its own line")
     ap.add_argument("--stateless", action="store_true",
                     help="comparison: decode every chunk again from zero state with up to 16 "
                          "left frames (the pages' stateless variant) instead of carrying state")
@@ -1120,6 +1155,14 @@ def main() -> int:
               f"WORLD_SIZE {world}); streams would shard across GPUs with no collective, "
               "which is not built.", file=sys.stderr)
         return 2
+
+    # the other workloads, each a short run of this script in a child process
+    # (before this process touches the GPU), reported beside the headline line
+    others = None
+    if (args.config == "c4" and not args.no_other_configs and not
+            (args.graph or args.stateless or args.cotenant or args.blas_reference or
+             args.copy_mib)):
+        others = other_workloads()
 
     import torch
 
@@ -1328,6 +1371,8 @@ def main() -> int:
         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(bpf * fps / 1e9 / PEAK_HBM_GBS, 4),
         "source": "FETCH_SIZE + WRITE_SIZE of every dispatch of the step (committed counter "
                   "summary) x this run's frames/s"}
+    if others:
+        out["other_workloads"] = others
     if cot:
         out["cotenant"] = cot
     if glat:
