@@ -111,6 +111,7 @@ struct codec {
     double *inv_freq = nullptr;
     void *u16 = nullptr, *a16 = nullptr, *att16 = nullptr, *f16 = nullptr;
     float *h32 = nullptr, *qkv32 = nullptr, *kring = nullptr, *vring = nullptr;
+    float *rot = nullptr;  // [F][hd/2] (cos, sin) of the step's rotary angles
 
     // Decoders without a transformer fold the projection into the input conv
     // (fold): the gather writes z' = [z, 1, 0...] rows of dz values into the
@@ -625,6 +626,7 @@ int enqueue_transformer(codec *c, int B, int F, const StepMeta &m, hipStream_t s
         return rc;
     AttnArgs at{};
     at.qkv = c->qkv32;
+    at.rot = c->rot;
     at.att = c->att16;
     at.kring = c->kring;
     at.vring = c->vring;
@@ -638,6 +640,12 @@ int enqueue_transformer(codec *c, int B, int F, const StepMeta &m, hipStream_t s
     at.W = g.tf_window;
     at.n_layers = g.tf_layers;
     at.dtype = c->dtype;
+    // the rotary angles depend on the frame only: one table for every layer
+    if ((rc = timed(c, "tf.rope", F, s, [&] {
+             return launch_rope_table(c->rot, c->inv_freq, m.frame_stream, m.cu, m.pos, F,
+                                      g.tf_head_dim, s);
+         })))
+        return rc;
     for (int l = 0; l < g.tf_layers; l++) {
         at.layer = l;
         if ((rc = timed(c, "tf.ln", F, s, [&] {
@@ -649,23 +657,18 @@ int enqueue_transformer(codec *c, int B, int F, const StepMeta &m, hipStream_t s
         a.out32 = c->qkv32;
         if ((rc = run_conv(c, "tf.qkv", a, s)))
             return rc;
-        if ((rc = timed(c, "tf.rope", F, s, [&] {
-                 return launch_rope(c->qkv32, c->inv_freq, m.frame_stream, m.cu, m.pos, F,
-                                    g.tf_heads, g.tf_head_dim, s);
-             })))
-            return rc;
         if ((rc = timed(c, "tf.attention", F, s, [&] { return launch_window_attention(at, s); })))
-            return rc;
-        if ((rc = timed(c, "tf.kv_append", B, s, [&] { return launch_kv_append(at, B, s); })))
             return rc;
         a = conv_args(c, c->tf_o[l], c->att16, 0, 1, F, m);
         a.res = c->h32;
         a.out32 = c->h32;
         if ((rc = run_conv(c, "tf.o_proj", a, s)))
             return rc;
-        if ((rc = timed(c, "tf.ln", F, s, [&] {
+        // the second LayerNorm's launch also appends this layer's K/V rows to
+        // the ring (after the attention that read the ring's old rows)
+        if ((rc = timed(c, "tf.ln+kv_append", F, s, [&] {
                  return launch_layer_norm(c->h32, c->ln2_g[l], c->ln2_b[l], F, dm, c->a16,
-                                          c->dtype, s);
+                                          c->dtype, s, &at);
              })))
             return rc;
         a = conv_args(c, c->tf_fc1[l], c->a16, 0, 1, F, m);
@@ -1423,6 +1426,7 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
             (rc = dev_alloc(c, &c->f16, F * g.tf_mlp * es, ws)) ||
             (rc = dev_alloc(c, (void **)&c->h32, F * dm * 4, ws)) ||
             (rc = dev_alloc(c, (void **)&c->qkv32, F * 3 * dm * 4, ws)) ||
+            (rc = dev_alloc(c, (void **)&c->rot, F * g.tf_head_dim * 4, ws)) ||
             (rc = dev_alloc(c, (void **)&c->kring, B * g.tf_layers * (W1 ? W1 : 1) * dm * 4, ws)) ||
             (rc = dev_alloc(c, (void **)&c->vring, B * g.tf_layers * (W1 ? W1 : 1) * dm * 4, ws)))
             return cleanup_fail(rc);

@@ -207,20 +207,27 @@ hipError_t launch_stage_fused(const StageArgs &a, int C, int S, int T, bool fina
 // ---- transformer ops (kernels_tf.hip) ----
 #define SNRVQ_MAX_WINDOW 32  // keys per query, including its own frame
 struct AttnArgs {
-    float *qkv;               // [F][3 dm] fp32, bias included; q, k rotated in place
+    float *qkv;               // [F][3 dm] fp32, bias included (q, k not rotated)
+    const float *rot;         // [F][hd/2][2] cos, sin of each frame's rotary angles
     void *att;                // [F][dm] compute type
-    float *kring, *vring;     // [slots][layers][W-1][dm] fp32
+    float *kring, *vring;     // [slots][layers][W-1][dm] fp32; K rotated
     const int32_t *frame_stream, *cu, *slot, *pos;
     int F, H, hd, W, layer, n_layers;
     int dtype;
 };
-// y[f] = LN(x[f]) in the compute type (x fp32 [F][D], D % 64 == 0).
+// y[f] = LN(x[f]) in the compute type (x fp32 [F][D], D % 64 == 0).  With
+// ring != nullptr the same launch also appends the layer's K (rotated) and V
+// rows of each stream's last min(n_b, W-1) frames to the K/V ring (ring->
+// layer); the caller orders it after that layer's attention.
 hipError_t launch_layer_norm(const float *x, const float *g, const float *b, int F, int D,
-                             void *y, int dtype, hipStream_t st);
-hipError_t launch_rope(float *qkv, const double *inv_freq, const int32_t *frame_stream,
-                       const int32_t *cu, const int32_t *pos, int F, int H, int hd,
-                       hipStream_t st);
+                             void *y, int dtype, hipStream_t st,
+                             const AttnArgs *ring = nullptr);
+// rot[f][i] = (cos, sin) of pos(f) inv_freq[i], i < hd / 2 (the angle in
+// fp64, reduced, then both rounded to fp32): the rotary table of the step's
+// frames, applied to q and k inside the attention and the ring append.
+hipError_t launch_rope_table(float *rot, const double *inv_freq, const int32_t *frame_stream,
+                             const int32_t *cu, const int32_t *pos, int F, int hd,
+                             hipStream_t st);
 hipError_t launch_window_attention(const AttnArgs &a, hipStream_t st);
-hipError_t launch_kv_append(const AttnArgs &a, int B, hipStream_t st);
 
 }  // namespace snrvq
