@@ -15,7 +15,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsnrvq.so")
+# SNRVQ_LIBRARY names another build of the same library (the host-sanitized
+# libsnrvq_hostsan.so); by default the in-tree libsnrvq.so
+LIB_PATH = os.environ.get("SNRVQ_LIBRARY") or os.path.join(HERE, "libsnrvq.so")
 
 CODEC_OK, CODEC_EINVAL, CODEC_ESTREAM, CODEC_EDUP, CODEC_ERANGE = 0, 1, 2, 3, 4
 CODEC_ENOSLOT, CODEC_ETOOBIG, CODEC_ENOMEM, CODEC_EHIP = 5, 6, 7, 8
