@@ -106,23 +106,27 @@ def layer_model(cfg: dict) -> dict:
 # per second (the published 157.3 TFLOP/s fp32 counts an FMA as two and packed
 # instructions twice); transcendentals (the hardware sine) at a quarter of it.
 VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+# vector-ALU lane-operation slots of one Snake (multiply, range reduction,
+# sine, square, fused multiply-add), measured: 24.8-26 cycles per 64-lane
+# wave on one SIMD (bench.py --ceilings: four full-rate instructions and the
+# sine at about half rate), i.e. 6.2 slots of 16 lanes per cycle
+SNAKE_SLOTS = 6.2
 
 
 def vector_floor(cfg: dict, cls: str, units: float, flops: float, peak_tflops: float,
                  sec: float) -> dict:
     """The vector-ALU work a fused stage cannot avoid beside its MFMAs: five
     activations per output row and channel (the two residual units' input and
-    inner activations, and the stage output's), each a Snake -- multiply, range
-    reduction, sine, square, fused multiply-add: four full-rate instructions
-    and one quarter-rate one, 8 lane-operation slots -- plus half a
-    conversion instruction (two values packed to fp16 per instruction).  The
-    floor is that work at the full vector rate; MFMA work at the published
-    peak beside it; the two overlapped at best, serial at worst."""
+    inner activations, and the stage output's), each a Snake at its measured
+    cost (SNAKE_SLOTS lane-operation slots) plus half a conversion
+    instruction (two values packed to fp16 per instruction).  The floor is
+    that work at the full vector rate; MFMA work at the published peak beside
+    it; the two overlapped at best, serial at worst."""
     import rvq_inputs as RI
     ch = RI.channels(cfg)
     i = int(cls[1:cls.index(".")])
     snakes = units * 5 * ch[i + 1]
-    slots = snakes * (4 + 4 + 0.5) if cfg["act"] == "snake" else snakes * 2.5
+    slots = snakes * (SNAKE_SLOTS + 0.5) if cfg["act"] == "snake" else snakes * 2.5
     valu_us = slots / VALU_LANE_OPS * 1e6
     mfma_us = flops / (peak_tflops * 1e12) * 1e6
     return {"activations_per_launch": int(snakes), "lane_op_slots_per_launch": int(slots),
@@ -1090,6 +1094,114 @@ def stored_step_hbm():
     return st["bytes_per_step"] / st["frames_per_step"]
 
 
+def ceilings(summary: str | None) -> int:
+    """The part's own rates (libsnrvq_probes.so): MFMA throughput with no
+    memory traffic, conflict-free LDS reads, Snake throughput on the vector
+    ALU, and MFMA with Snake work in the same waves -- in separate blocks and
+    interleaved -- against the sum of their times alone; each with the shader
+    clock its waves saw.  One JSON line; with `summary`, a markdown table
+    appended to that file."""
+    import ctypes as C
+    lib_path = os.path.join(ROOT, "streaming_neural_audio_rvq_amd", "libsnrvq_probes.so")
+    if not os.path.exists(lib_path):
+        raise SystemExit(f"{lib_path} is missing: build it first "
+                         "(python -c 'import __graft_entry__ as g; g.build()')")
+
+    class Res(C.Structure):
+        _fields_ = [("us", C.c_double), ("rate", C.c_double), ("clock_ghz", C.c_double)]
+
+    L = C.CDLL(lib_path)
+    n_cu = L.probe_cu_count()
+    reps = 5
+
+    def call(fn, *a):
+        r = Res()
+        rc = fn(*[C.c_int(v) for v in a], C.c_int(reps), C.byref(r))
+        if rc:
+            raise SystemExit(f"probe {fn.__name__}{a} failed: {rc}")
+        return {"us": round(r.us, 2), "rate": r.rate, "clock_ghz": round(r.clock_ghz, 3)}
+
+    out = {"n_cu": n_cu, "mfma": [], "lds": [], "overlap": []}
+    for kind, name in ((0, "16x16x32 f16"), (1, "32x32x16 f16")):
+        for wps in (1, 2, 3):
+            r = call(L.probe_mfma, kind, wps, 20000)
+            r.update(shape=name, waves_per_simd=wps, tflops=round(r.pop("rate"), 1))
+            # cycles per MFMA on one SIMD at the clock the waves saw (multiply-adds
+            # per MFMA: 8192 for 16x16x32, 16384 for 32x32x16)
+            macs = 8192 if kind == 0 else 16384
+            r["cycles_per_mfma"] = round(2 * macs * n_cu * 4 * r["clock_ghz"] * 1e9
+                                         / (r["tflops"] * 1e12), 2)
+            out["mfma"].append(r)
+            print(json.dumps(r), flush=True)
+    for wps in (1, 2, 4):
+        r = call(L.probe_lds, wps, 20000)
+        r.update(waves_per_simd=wps, tbps=round(r.pop("rate"), 2))
+        r["bytes_per_clk_cu"] = round(r["tbps"] * 1e12 / (n_cu * r["clock_ghz"] * 1e9), 1)
+        out["lds"].append(r)
+        print(json.dumps(r), flush=True)
+    out["gload"] = []
+    for wps in (1, 2, 4):
+        r = call(L.probe_gload, wps, 4000)
+        r.update(waves_per_simd=wps, tbps=round(r.pop("rate"), 2))
+        r["bytes_per_clk_cu"] = round(r["tbps"] * 1e12 / (n_cu * r["clock_ghz"] * 1e9), 1)
+        out["gload"].append(r)
+        print(json.dumps(r), flush=True)
+    for wps in (2, 3):
+        t = {}
+        for mode, name in ((0, "snake"), (1, "mfma"), (2, "blocked"), (3, "interleaved")):
+            r = call(L.probe_overlap, mode, wps, 4000)
+            t[name] = r
+        alone = t["snake"]["us"] + t["mfma"]["us"]
+        rec = {"waves_per_simd": wps, "us_snake": t["snake"]["us"], "us_mfma": t["mfma"]["us"],
+               "us_blocked": t["blocked"]["us"], "us_interleaved": t["interleaved"]["us"],
+               "blocked_of_sum": round(t["blocked"]["us"] / alone, 3),
+               "interleaved_of_sum": round(t["interleaved"]["us"] / alone, 3),
+               "snakes_per_s": t["snake"]["rate"],
+               # vector-ALU cycles of one wave's Snake (64 lanes) on its SIMD
+               "cycles_per_wave_snake": round(t["snake"]["clock_ghz"] * 1e9 * n_cu * 4 * 64
+                                              / t["snake"]["rate"], 2),
+               "clock_ghz": t["snake"]["clock_ghz"]}
+        out["overlap"].append(rec)
+        print(json.dumps(rec), flush=True)
+    print(json.dumps(out), flush=True)
+    if summary:
+        lines = ["", "## Ceilings of the part (`bench.py --ceilings`)", "",
+                 f"{n_cu} compute units. Each probe: one untimed launch, then {reps} timed "
+                 "launches (HIP events) of CUs x waves-per-SIMD work-groups of 256 threads; "
+                 "the clock is the waves' cycle counter against the 100 MHz counter.", "",
+                 "| MFMA | waves/SIMD | us | TFLOP/s | of 2.5 PFLOP/s | clock GHz | cycles per MFMA |",
+                 "|---|---:|---:|---:|---:|---:|---:|"]
+        for r in out["mfma"]:
+            lines.append(f"| {r['shape']} | {r['waves_per_simd']} | {r['us']} | {r['tflops']} | "
+                         f"{r['tflops'] / 2500:.3f} | {r['clock_ghz']} | {r['cycles_per_mfma']} |")
+        lines += ["", "| LDS reads | waves/SIMD | us | TB/s | bytes per clock per CU | clock GHz |",
+                  "|---|---:|---:|---:|---:|---:|"]
+        for r in out["lds"]:
+            lines.append(f"| ds_read_b128, conflict-free | {r['waves_per_simd']} | {r['us']} | "
+                         f"{r['tbps']} | {r['bytes_per_clk_cu']} | {r['clock_ghz']} |")
+        lines += ["", "| global -> LDS direct loads (L2-resident) | waves/SIMD | us | TB/s | "
+                  "bytes per clock per CU | clock GHz |", "|---|---:|---:|---:|---:|---:|"]
+        for r in out["gload"]:
+            lines.append(f"| global_load_lds 16 B/lane, 8 KiB per wave in flight | "
+                         f"{r['waves_per_simd']} | {r['us']} | {r['tbps']} | "
+                         f"{r['bytes_per_clk_cu']} | {r['clock_ghz']} |")
+        lines += ["", "MFMA and Snake work in the same waves (16 MFMAs 16x16x32 f16 and 32 Snakes "
+                  "per iteration): time in separate blocks and interleaved (one MFMA, two Snakes), "
+                  "against the sum of the two alone.", "",
+                  "| waves/SIMD | Snakes alone us | MFMAs alone us | blocked us | interleaved us | "
+                  "blocked / sum | interleaved / sum | Snakes/s | cycles per wave Snake | clock GHz |",
+                  "|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+        for r in out["overlap"]:
+            lines.append(f"| {r['waves_per_simd']} | {r['us_snake']} | {r['us_mfma']} | "
+                         f"{r['us_blocked']} | {r['us_interleaved']} | {r['blocked_of_sum']} | "
+                         f"{r['interleaved_of_sum']} | {r['snakes_per_s']:.3g} | "
+                         f"{r['cycles_per_wave_snake']} | {r['clock_ghz']} |")
+        lines += ["", "```json", json.dumps(out), "```", ""]
+        with open(summary, "a") as fh:
+            fh.write("\n".join(lines))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -1144,9 +1256,15 @@ def main() -> int:
     ap.add_argument("--pmc-steps", type=int, default=2)
     ap.add_argument("--pmc-warmup", type=int, default=1)
     ap.add_argument("--top", type=int, default=30)
+    ap.add_argument("--ceilings", action="store_true",
+                    help="instead of decoding: the part's own MFMA, LDS and vector-ALU rates "
+                         "(libsnrvq_probes.so)")
+    ap.add_argument("--ceilings-summary", help="with --ceilings: append the tables to this file")
     args = ap.parse_args()
     if args.rocprof_summary:
         return rocprof_summary(args)
+    if args.ceilings:
+        return ceilings(args.ceilings_summary)
     if args.graph:
         args.no_profile = True  # graph steps record no per-kernel events
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -64,6 +64,25 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+LIB_PROBES = os.path.join(HERE, "libsnrvq_probes.so")
+
+
+def build_probes(verbose: bool = False) -> str:
+    """libsnrvq_probes.so: the micro-benchmarks of probes/ceilings.hip
+    (include/snrvq_probes.h), a library of their own."""
+    os.makedirs(BUILD, exist_ok=True)
+    src = os.path.join(HERE, "probes", "ceilings.hip")
+    tmp = LIB_PROBES + ".tmp"
+    cmd = [HIPCC, *COMMON, "-shared", src, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for ceilings.hip:\n{r.stderr}")
+    os.replace(tmp, LIB_PROBES)
+    if verbose:
+        print("built", LIB_PROBES)
+    return LIB_PROBES
+
+
 def asan_runtime() -> str:
     """Path of the compiler's shared ASan runtime (to preload)."""
     clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "lib", "llvm", "bin",
@@ -99,3 +118,4 @@ def build_hostsan(verbose: bool = False) -> str:
 if __name__ == "__main__":
     build(verbose=True)
     build_hostsan(verbose=True)
+    build_probes(verbose=True)

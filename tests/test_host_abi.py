@@ -1,6 +1,7 @@
 """CPU-only checks of the HIP library's host side: it loads, exports every
 function its header declares, and its host-only policy and argument checks
 behave as specified.  No kernel runs here."""
+import ctypes as C
 import json
 import os
 import re
@@ -30,6 +31,22 @@ def test_library_exports_every_declared_function():
     for name in declared:
         assert hasattr(L, name), name
     assert sorted(snr.EXPORTS) == declared
+
+
+def test_probe_library_exports_its_header():
+    """The micro-benchmark library (include/snrvq_probes.h) exports every
+    function its header declares; without a GPU it counts no CUs and refuses
+    to run."""
+    text = open(os.path.join(ROOT, "include", "snrvq_probes.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"^\s*int\s+(\w+)\s*\(", text, flags=re.M)))
+    assert names == ["probe_cu_count", "probe_gload", "probe_lds", "probe_mfma", "probe_overlap"]
+    L = C.CDLL(os.path.join(ROOT, "streaming_neural_audio_rvq_amd", "libsnrvq_probes.so"))
+    for name in names:
+        assert hasattr(L, name), name
+    if L.probe_cu_count() == 0:  # no device here
+        res = (C.c_double * 3)()
+        assert L.probe_mfma(0, 1, 10, 1, res) == 1
 
 
 def test_chunk_plan_printed_example():
