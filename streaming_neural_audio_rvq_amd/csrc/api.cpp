@@ -634,6 +634,8 @@ int enqueue_transformer(codec *c, int B, int F, const StepMeta &m, hipStream_t s
     at.cu = m.cu;
     at.slot = m.slot;
     at.pos = m.pos;
+    at.attn_q = m.attn_q;
+    at.n_qblocks = m.n_qblocks;
     at.F = F;
     at.H = g.tf_heads;
     at.hd = g.tf_head_dim;
@@ -702,9 +704,13 @@ struct MetaLayout {
     StepMeta m{};
 };
 
+// Attention query blocks of a step of B streams and F frames, at most: each
+// stream's frames in blocks of SNRVQ_ATTN_QB, the last shorter.
+inline int attn_qblock_bound(int B, int F) { return (F + SNRVQ_ATTN_QB - 1) / SNRVQ_ATTN_QB + B; }
+
 // Metadata layout of a step of B streams and F frames (int32 offsets).
 struct MetaOffsets {
-    size_t codes, fs, cu, slot, fresh, pos, tile[CODEC_MAX_STAGES], total;
+    size_t codes, fs, cu, slot, fresh, pos, tile[CODEC_MAX_STAGES], attn, total;
 };
 MetaOffsets meta_offsets(const codec *c, int B, int F, bool codes_on_device)
 {
@@ -722,6 +728,10 @@ MetaOffsets meta_offsets(const codec *c, int B, int F, bool codes_on_device)
             o.tile[i] = o.total;
             o.total = round4(o.total + B + 1);
         }
+    if (c->cfg.tf_layers) {
+        o.attn = o.total;
+        o.total = round4(o.total + SNRVQ_ATTN_Q_INTS * (size_t)attn_qblock_bound(B, F));
+    }
     return o;
 }
 
@@ -776,6 +786,33 @@ MetaLayout fill_meta(codec *c, int32_t *hp, int B, const int *slots, const int32
         m.n_tiles[i] = tile_bound ? (int)(((int64_t)F * c->rate[i + 1] + c->fuse_T[i] - 1) /
                                               c->fuse_T[i] + B)
                                   : tc[B];
+    }
+    // attention: each stream's frames in query blocks of SNRVQ_ATTN_QB, the
+    // last shorter; per block its first frame, frame count, the position of
+    // its first frame and of the stream's first frame of the step, and the
+    // stream's slot; blocks of no frames up to the bound
+    if (g.tf_layers) {
+        int32_t *aq = hp + o.attn;
+        const int bound = attn_qblock_bound(B, F);
+        int nq = 0, f0 = 0;
+        for (int b = 0; b < B; b++) {
+            const int32_t p0 = hp[o.pos + b];
+            for (int q = 0; q < n[b]; q += SNRVQ_ATTN_QB, nq++) {
+                int32_t *e = aq + (size_t)SNRVQ_ATTN_Q_INTS * nq;
+                e[0] = f0 + q;
+                e[1] = std::min(SNRVQ_ATTN_QB, n[b] - q);
+                e[2] = p0 + q;
+                e[3] = p0;
+                e[4] = slots[b];
+                e[5] = e[6] = e[7] = 0;
+            }
+            f0 += n[b];
+        }
+        for (int q = nq; q < bound; q++)
+            for (int k = 0; k < SNRVQ_ATTN_Q_INTS; k++)
+                aq[(size_t)SNRVQ_ATTN_Q_INTS * q + k] = 0;
+        m.attn_q = dm + o.attn;
+        m.n_qblocks = tile_bound ? bound : nq;
     }
     MetaLayout out;
     out.total = o.total;
@@ -1492,7 +1529,8 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
 
     // ---- step metadata: device buffer + pinned staging arena ----
     c->meta_cap = round4(F * g.K) + round4(F) + round4(B + 1) + 3 * round4(B) +
-                  CODEC_MAX_STAGES * round4(B + 1) + 4;
+                  CODEC_MAX_STAGES * round4(B + 1) +
+                  (g.tf_layers ? round4(SNRVQ_ATTN_Q_INTS * (size_t)attn_qblock_bound(B, F)) : 0) + 4;
     if ((rc = dev_alloc(c, &c->meta_dev, c->meta_cap * 4, ws)))
         return cleanup_fail(rc);
     if ((rc = dev_alloc(c, (void **)&c->bad_codes, sizeof(unsigned long long), ws)))

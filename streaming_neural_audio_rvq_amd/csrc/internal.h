@@ -131,8 +131,10 @@ struct StepMeta {
     int32_t *fresh;        // [B]
     int32_t *pos;          // [B]
     int32_t *tile_cu[CODEC_MAX_STAGES];  // fused stage i: first tile of each stream [B+1]
+    int32_t *attn_q;                      // attention query blocks, SNRVQ_ATTN_Q_INTS each (see AttnArgs)
     int B;                                // streams in the step
     int n_tiles[CODEC_MAX_STAGES];        // fused stage i: tiles in the step
+    int n_qblocks;                        // attention query blocks (a bound for graphs)
 };
 
 // ---- launchers (kernels_*.hip) ----
@@ -206,13 +208,18 @@ hipError_t launch_stage_fused(const StageArgs &a, int C, int S, int T, bool fina
 
 // ---- transformer ops (kernels_tf.hip) ----
 #define SNRVQ_MAX_WINDOW 32  // keys per query, including its own frame
+#define SNRVQ_ATTN_QB 16     // frames of one stream per attention work-group
+#define SNRVQ_ATTN_Q_INTS 8  // per query block: first frame, frames (0: none), position of
+                             // the first frame, of the stream's first frame of the step, slot
 struct AttnArgs {
     float *qkv;               // [F][3 dm] fp32, bias included (q, k not rotated)
     const float *rot;         // [F][hd/2][2] cos, sin of each frame's rotary angles
     void *att;                // [F][dm] compute type
     float *kring, *vring;     // [slots][layers][W-1][dm] fp32; K rotated
     const int32_t *frame_stream, *cu, *slot, *pos;
+    const int32_t *attn_q;    // [n_qblocks][SNRVQ_ATTN_Q_INTS] query blocks of the step
     int F, H, hd, W, layer, n_layers;
+    int n_qblocks;            // query blocks launched
     int dtype;
 };
 // y[f] = LN(x[f]) in the compute type (x fp32 [F][D], D % 64 == 0).  With

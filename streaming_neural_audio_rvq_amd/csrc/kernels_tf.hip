@@ -6,7 +6,8 @@
 // with k = 1, with bias, GELU and residual fused into its epilogue.  The
 // rotary angles of the step's frames are tabulated once per step; q and k are
 // rotated where they are read (attention) or stored (ring append, which rides
-// on the launch of the layer's second LayerNorm).
+// on the launch of the layer's second LayerNorm).  The attention stages each
+// block of frames' key window in LDS once.
 //
 // K/V ring: per slot and layer, W-1 rows of post-rotary K and of V (fp32),
 // the frame at absolute position p living in row p mod (W-1).
@@ -121,110 +122,152 @@ __device__ __forceinline__ void rope_pair(float a, float b, float c, float s, fl
     y = b * c + a * s;
 }
 
-// One wave per (frame, head), hd == 64.  Keys j in [max(0, p - (W-1)), p],
-// ascending: those before the stream's first frame of this step come from
-// the ring, the rest from this step's qkv.  Scores: lanes kk and kk + 32 own
-// key kk and take its dot product with q over half the dimensions each (all
-// keys' loads in flight at once, one cross-lane add per key); softmax over
-// the lanes; output: lane e owns dimension e and sums the value rows in key
-// order with the probabilities broadcast from their lanes.
+// One work-group per (query block, head), hd == 64: the block's frames are
+// up to SNRVQ_ATTN_QB consecutive frames of one stream (the host lists each
+// block's frames, positions and slot), and frame f at absolute position p attends
+// to keys j in [max(0, p - (W-1)), p], ascending.  The block first stages in
+// LDS its frames' q rows (rotated) and the K (rotated) and V rows of every key
+// they need -- keys before the stream's first frame of this step from the
+// ring, the rest from this step's qkv, rotated here -- so the frames of a
+// block share them.  Then wave w takes frames w, w + 4, ... of the block.
+// Scores: lanes kk and kk + 32 own key kk and take its dot product with q over
+// half the dimensions each (pairs 16u .. 16u + 15 of the rotate-half pairs
+// (i, i + 32), u = lane / 32), adding the halves with one cross-lane add;
+// softmax over the lanes; output: lane e owns dimension e and sums the value
+// rows in key order with the probabilities broadcast from their lanes.
+constexpr int ATT_KROWS = SNRVQ_ATTN_QB + SNRVQ_MAX_WINDOW - 1;  // keys a block can need
+constexpr int ATT_KP = 68;  // LDS row pitch, floats: 16-byte reads of 16 rows on distinct banks
+
+// Rotated f4 q4 (dims 4 q4 .. 4 q4 + 3) of a 64-wide q or K row r of frame
+// row rf of the rotary table: dims below 32 pair with the f4 8 further on.
+__device__ __forceinline__ f4 rope_f4(const float *r, const float *rf, int q4)
+{
+    const bool lo4 = q4 < 8;
+    const f4 own = *(const f4 *)(r + 4 * q4);
+    const f4 other = *(const f4 *)(r + 4 * (lo4 ? q4 + 8 : q4 - 8));
+    f4 out;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const int i = 4 * (lo4 ? q4 : q4 - 8) + e;
+        float x, y;
+        if (lo4)
+            rope_pair(own[e], other[e], rf[2 * i], rf[2 * i + 1], x, y);
+        else
+            rope_pair(other[e], own[e], rf[2 * i], rf[2 * i + 1], x, y);
+        out[e] = lo4 ? x : y;
+    }
+    return out;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void window_attention_kernel(AttnArgs a)
 {
-    const int lane = threadIdx.x & 63;
-    const long wid = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int H = a.H, hd = a.hd, dm = H * hd, W1 = a.W - 1;
-    if (wid >= (long)a.F * H)
+    __shared__ __attribute__((aligned(16))) float ks[ATT_KROWS * ATT_KP];
+    __shared__ __attribute__((aligned(16))) float vs[ATT_KROWS * ATT_KP];
+    __shared__ __attribute__((aligned(16))) float qs[SNRVQ_ATTN_QB * ATT_KP];
+    const int qb = blockIdx.x, h = blockIdx.y;
+    const int32_t *e = a.attn_q + (long)qb * SNRVQ_ATTN_Q_INTS;
+    const int f0 = e[0], nq = e[1];
+    if (nq <= 0)  // graph launches size the grid for the most blocks a step can have
         return;
-    const int h = (int)(wid % H);
-    const int f = (int)(wid / H);
-    const int b = a.frame_stream[f];
-    const long p0 = a.pos[b];
-    const long p = p0 + (f - a.cu[b]);
-    const long jlo = p - W1 > 0 ? p - W1 : 0;
-    const int nk = (int)(p - jlo + 1);
-    const long ring_base = ((long)a.slot[b] * a.n_layers + a.layer) * W1 * dm + h * hd;
-    const float scale = 1.0f / sqrtf((float)hd);
-    // key kk: ring slot (jlo + kk) mod (W-1) while j < p0, else this step's row
-    const int nring = (int)(p0 - jlo > 0 ? p0 - jlo : 0);  // keys held in the ring
-    const int slot0 = W1 > 0 ? (int)(jlo % W1) : 0;
-    const long row0 = (long)a.cu[b] * 3 * dm + h * hd;  // this step's first frame (q part)
-    const long step0 = jlo + nring - p0;                 // step row of key nring
-    // element offset of key kk's K row (V row: + dm) in kring / qkv
-    auto key_row = [&](int kk, bool &in_ring) -> long {
-        in_ring = kk < nring;
-        if (in_ring) {
-            int sl = slot0 + kk;
-            sl = sl >= W1 ? sl - W1 : sl;
-            return ring_base + (long)sl * dm;
-        }
-        return row0 + (step0 + kk - nring) * 3 * dm + dm;
-    };
+    const long pf0 = e[2];  // position of frame f0
+    const long p0 = e[3];   // position of the stream's first frame of this step
+    const int slot = e[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = a.H, hd = a.hd, dm = H * hd, W1 = a.W - 1;
+    const int f1 = f0 + nq;
+    const long jlo = pf0 - W1 > 0 ? pf0 - W1 : 0;  // first key staged
+    const int nkeys = (int)(pf0 + nq - 1 - jlo + 1);
+    const long ring_base = ((long)slot * a.n_layers + a.layer) * W1 * dm + h * hd;
 
-    // scores: key kk = lane mod 32 (W <= 32).  Lanes kk and kk + 32 split the
-    // head's 32 rotate-half pairs (i, i + 32) between them, pairs 16u .. 16u + 15
-    // for u = lane / 32, and add their two partial sums.  The query and this
-    // step's keys are rotated here with their frames' table rows (the ring's
-    // keys already are).
-    const int u = lane >> 5;
-    const int kk = (lane & 31) < nk ? (lane & 31) : nk - 1;
-    bool k_in_ring;
-    const long krow = key_row(kk, k_in_ring);
-    const float *kp = (k_in_ring ? a.kring : a.qkv) + krow + 16 * u;
-    const float *qp = a.qkv + (long)f * 3 * dm + h * hd + 16 * u;
-    const float *rq = a.rot + (long)f * hd + 32 * u;  // (cos, sin) of pairs 16u ..
-    float dot = 0.f;
+    // stage the key rows jlo .. jlo + nkeys - 1 and the q rows f0 .. f1 - 1 of
+    // head h, 16 f4 per row: item c < (nkeys + nq) 16 of thread c mod 256,
+    // all of a thread's loads issued before its first LDS store
+    constexpr int ITEMS = (ATT_KROWS + SNRVQ_ATTN_QB) * 16 / 256;
+    static_assert((ATT_KROWS + SNRVQ_ATTN_QB) * 16 <= ITEMS * 256 + 255, "items");
+    f4 kv[ITEMS + 1], vv[ITEMS + 1];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {  // pairs 16u + 4i .. 16u + 4i + 3
-        const f4 ql = *(const f4 *)(qp + 4 * i), qh = *(const f4 *)(qp + 32 + 4 * i);
-        f4 kl = *(const f4 *)(kp + 4 * i), kh = *(const f4 *)(kp + 32 + 4 * i);
-        const f4 r0 = *(const f4 *)(rq + 8 * i), r1 = *(const f4 *)(rq + 8 * i + 4);
-        const float cq[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-        if (!k_in_ring) {
-            const float *rk = a.rot + ((long)a.cu[b] + (step0 + kk - nring)) * hd + 32 * u;
-            const f4 t0 = *(const f4 *)(rk + 8 * i), t1 = *(const f4 *)(rk + 8 * i + 4);
-            const float ck[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+    for (int it = 0; it <= ITEMS; it++) {
+        const int c = tid + it * 256;
+        const int r = c >> 4, q4 = c & 15;
+        if (c >= (nkeys + nq) * 16)
+            continue;
+        if (r >= nkeys) {  // q row of frame f0 + r - nkeys
+            const long f = f0 + (r - nkeys);
+            kv[it] = rope_f4(a.qkv + f * 3 * dm + h * hd, a.rot + f * hd, q4);
+            continue;
+        }
+        const long j = jlo + r;
+        if (j < p0) {  // in the ring (row j mod (W-1)), K already rotated
+            const long o = ring_base + (j % W1) * dm + 4 * q4;
+            kv[it] = *(const f4 *)(a.kring + o);
+            vv[it] = *(const f4 *)(a.vring + o);
+        } else {  // this step's frame, K rotated as in the ring append
+            const long fk = f0 + (j - pf0);
+            const float *kr = a.qkv + fk * 3 * dm + dm + h * hd;
+            kv[it] = rope_f4(kr, a.rot + fk * hd, q4);
+            vv[it] = *(const f4 *)(kr + dm + 4 * q4);
+        }
+    }
+#pragma unroll
+    for (int it = 0; it <= ITEMS; it++) {
+        const int c = tid + it * 256;
+        const int r = c >> 4, q4 = c & 15;
+        if (c >= (nkeys + nq) * 16)
+            continue;
+        if (r >= nkeys) {
+            *(f4 *)(qs + (r - nkeys) * ATT_KP + 4 * q4) = kv[it];
+        } else {
+            *(f4 *)(ks + r * ATT_KP + 4 * q4) = kv[it];
+            *(f4 *)(vs + r * ATT_KP + 4 * q4) = vv[it];
+        }
+    }
+    __syncthreads();
+
+    const float scale = 1.0f / sqrtf((float)hd);
+    const int u = lane >> 5;
+    for (int f = f0 + wave; f < f1; f += 4) {
+        const long p = pf0 + (f - f0);
+        const long jf = p - W1 > 0 ? p - W1 : 0;
+        const int nk = (int)(p - jf + 1);
+        const int r0 = (int)(jf - jlo);  // LDS row of this frame's key 0
+        const int kk = (lane & 31) < nk ? (lane & 31) : nk - 1;
+        const float *kp = ks + (r0 + kk) * ATT_KP + 16 * u;
+        const float *qp = qs + (f - f0) * ATT_KP + 16 * u;
+        float dot = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {  // pairs 16u + 4i .. 16u + 4i + 3
+            const f4 ql = *(const f4 *)(qp + 4 * i), qh = *(const f4 *)(qp + 32 + 4 * i);
+            const f4 kl = *(const f4 *)(kp + 4 * i), kh = *(const f4 *)(kp + 32 + 4 * i);
+            float lo2 = 0.f, hi2 = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                float x, y;
-                rope_pair(kl[e], kh[e], ck[2 * e], ck[2 * e + 1], x, y);
-                kl[e] = x;
-                kh[e] = y;
+                lo2 += ql[e] * kl[e];
+                hi2 += qh[e] * kh[e];
             }
+            dot += lo2 + hi2;
         }
-        float lo = 0.f, hi = 0.f;
+        dot += __shfl_xor(dot, 32, 64);
+        const float s = lane < nk ? dot * scale : -INFINITY;  // lanes >= 32: none
+        float mx = s;
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            float qx, qy;
-            rope_pair(ql[e], qh[e], cq[2 * e], cq[2 * e + 1], qx, qy);
-            lo += qx * kl[e];
-            hi += qy * kh[e];
-        }
-        dot += lo + hi;
-    }
-    dot += __shfl_xor(dot, 32, 64);
-    const float s = lane < nk ? dot * scale : -INFINITY;  // lanes >= 32: none
-    float mx = s;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    const float pk = lane < nk ? expf(s - mx) : 0.f;
-    const float den = wave_sum(pk);
+        for (int o = 32; o >= 1; o >>= 1)
+            mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        const float pk = lane < nk ? expf(s - mx) : 0.f;
+        const float den = wave_sum(pk);
 
-    // output: lane e, value rows in key order (all W loads issued at once:
-    // keys past nk read key nk - 1 and add nothing)
-    float acc = 0.f;
+        // output: lane e, value rows in key order (keys past nk read key
+        // nk - 1 and add nothing)
+        float acc = 0.f;
 #pragma unroll
-    for (int k2 = 0; k2 < SNRVQ_MAX_WINDOW; k2++) {
-        const int kc = k2 < nk ? k2 : nk - 1;
-        const float pr = __shfl(pk, kc, 64);
-        bool v_in_ring;
-        const long vrow = key_row(kc, v_in_ring);
-        const float *vp = v_in_ring ? a.vring + vrow : a.qkv + vrow + dm;
-        const float vv = vp[lane];
-        acc += k2 < nk ? pr * vv : 0.f;
+        for (int k2 = 0; k2 < SNRVQ_MAX_WINDOW; k2++) {
+            const int kc = k2 < nk ? k2 : nk - 1;
+            const float pr = __shfl(pk, kc, 64);
+            const float vv = vs[(r0 + kc) * ATT_KP + lane];
+            acc += k2 < nk ? pr * vv : 0.f;
+        }
+        st<T>((T *)a.att + (long)f * dm + h * hd + lane, acc / den);
     }
-    st<T>((T *)a.att + (long)f * dm + h * hd + lane, acc / den);
 }
 
 // Ring append of frame f: kept if it is among its stream's last min(n_b, W-1)
@@ -242,29 +285,14 @@ __device__ __forceinline__ void kv_append_frame(const AttnArgs &a, int f)
         return;
     const long ring_base = ((long)a.slot[b] * a.n_layers + a.layer) * W1 * dm;
     const int sl = (int)(((long)a.pos[b] + t) % W1);
-    const f4 *ks = (const f4 *)(a.qkv + (long)f * 3 * dm + dm), *vs = ks + dm / 4;
+    const float *kr = a.qkv + (long)f * 3 * dm + dm;
+    const float *rf = a.rot + (long)f * a.hd;
     f4 *kd = (f4 *)(a.kring + ring_base + (long)sl * dm);
     f4 *vd = (f4 *)(a.vring + ring_base + (long)sl * dm);
-    const int half = a.hd / 2;
-    const float *rf = a.rot + (long)f * a.hd;
     for (int c = threadIdx.x; c < dm / 4; c += 256) {
-        // dims d .. d + 3 of a head, paired with d + half .. (or d - half ..)
-        const int d = (c * 4) % a.hd;
-        const bool lo = d < half;
-        const f4 own = ks[c], other = ks[lo ? c + half / 4 : c - half / 4];
-        f4 out;
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int i = (lo ? d : d - half) + e;
-            float x, y;
-            if (lo)
-                rope_pair(own[e], other[e], rf[2 * i], rf[2 * i + 1], x, y);
-            else
-                rope_pair(other[e], own[e], rf[2 * i], rf[2 * i + 1], x, y);
-            out[e] = lo ? x : y;
-        }
-        kd[c] = out;
-        vd[c] = vs[c];
+        const int hh = c / 16, q4 = c % 16;  // head, f4 within its 64 dims
+        kd[c] = rope_f4(kr + hh * 64, rf, q4);
+        vd[c] = *(const f4 *)(kr + dm + 4 * c);
     }
 }
 
@@ -324,10 +352,11 @@ hipError_t launch_rope_table(float *rot, const double *inv_freq, const int32_t *
 
 hipError_t launch_window_attention(const AttnArgs &a, hipStream_t st)
 {
-    long waves = (long)a.F * a.H;
-    if (waves <= 0)
+    if (a.F <= 0 || a.n_qblocks <= 0)
         return hipSuccess;
-    dim3 grid((unsigned)((waves + 3) / 4));
+    if (a.hd != 64 || a.W < 1 || a.W > SNRVQ_MAX_WINDOW)
+        return hipErrorInvalidValue;
+    dim3 grid((unsigned)a.n_qblocks, (unsigned)a.H);
     if (a.dtype)
         hipLaunchKernelGGL(window_attention_kernel<half_t>, grid, dim3(256), 0, st, a);
     else
