@@ -389,6 +389,54 @@ def test_c3_full_scale_sampled_parity():
         assert e <= tol_for(cfg)
 
 
+def test_c3_query_blocks_short_window_and_graph():
+    """The attention's query blocks (up to 16 frames of one stream per
+    work-group): two streams with ragged chunks of up to 40 frames in one call
+    (three blocks of one stream), a 5-frame window whose ring wraps every 4
+    frames, and the same decode through decode_chunk_graph (blocks listed up to
+    the frame bucket's bound, the spare ones empty).  Against the oracle: each
+    stream's PCM, and the transformer's output of the last call."""
+    cfg = RI.get_config("c3", max_streams=4, max_frames_per_call=96, tf_window=5)
+    w = RI.make_weights(cfg)
+    m = oracle.Model(cfg, w)
+    plans = [[40, 3, 1, 20], [1, 17, 5, 16]]  # per stream, decoded in the same calls
+    codes = [RI.stream_codes(cfg, b, sum(plans[b]), part=13) for b in range(2)]
+    refs = [m.stream().decode(codes[b], capture=True) for b in range(2)]
+    say("case c3 query blocks: window 5, chunks", plans)
+    for use_graph in (False, True):
+        c = open_codec(cfg, w)
+        ids = [c.stream_open() for _ in range(2)]
+        outs, at = [[], []], [0, 0]
+        for k in range(len(plans[0])):
+            n = [plans[0][k], plans[1][k]]
+            packed = np.concatenate([codes[b][at[b]:at[b] + n[b]] for b in range(2)])
+            pcm = torch.empty(sum(n) * c.hop, dtype=torch.float32, device="cuda")
+            if use_graph:
+                c.decode_chunk_graph(ids, n, packed, pcm)
+            else:
+                c.decode_chunk(ids, n, packed, pcm)
+            host = pcm.cpu().numpy()
+            outs[0].append(host[:n[0] * c.hop])
+            outs[1].append(host[n[0] * c.hop:sum(n) * c.hop])
+            at = [at[b] + n[b] for b in range(2)]
+        if not use_graph:
+            cap = torch.empty(sum(n) * cfg["d_lat"], dtype=torch.float32, device="cuda")
+            c.debug_capture(snr.CAPTURE_DEC_INPUT, cap)
+            cap = cap.cpu().numpy().reshape(sum(n), cfg["d_lat"])
+        for b in range(2):
+            pcm_ref, _, x_ref = refs[b]
+            e, ac = rel_err(np.concatenate(outs[b]), pcm_ref)
+            say(f"c3 query blocks {'graph' if use_graph else 'eager'} stream {b}: "
+                f"err/peak {e:.3e} (AC-rel {ac:.3e})")
+            assert e <= tol_for(cfg)
+            if not use_graph:
+                rows = cap[:n[0]] if b == 0 else cap[n[0]:]
+                ex, _ = rel_err(rows, x_ref[-n[b]:])
+                say(f"  transformer output of the last call: err/peak {ex:.3e}")
+                assert ex <= tol_for(cfg)
+        c.close()
+
+
 # --------------------------------------------------------------------------
 # Fused per-stage kernels vs the per-layer launch sequence: same arithmetic
 # --------------------------------------------------------------------------
