@@ -1076,6 +1076,21 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
+def measured_mfma_peak():
+    """The highest v_mfma_f32_16x16x32_f16 rate of the committed ceilings
+    summary (bench.py --ceilings), TFLOP/s, or None when absent."""
+    import re
+    path = os.path.join(ROOT, "profiles", "part_ceilings__mi355x.md")
+    if not os.path.exists(path):
+        return None
+    mm = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not mm:
+        return None
+    rates = [r["tflops"] for r in json.loads(mm.group(1)).get("mfma", [])
+             if r.get("shape") == "16x16x32 f16"]
+    return max(rates) if rates else None
+
+
 def stored_step_hbm():
     """HBM bytes per decoded frame of the whole decode step (every kernel),
     from the committed counter summary of the 128-stream workload, or None
@@ -1443,6 +1458,13 @@ def main() -> int:
         if dom.endswith(".fused"):
             roof["vector_alu"] = vector_floor(cfg, dom, d["units"] / d["launches"],
                                               d["flops_per_launch"], peak_f, sec)
+        mp = measured_mfma_peak()
+        if roof["bound"] == "mfma" and mp and cfg["weight_dtype"] == "bf16":
+            # context beside the published peak: what the part's matrix cores
+            # delivered to the kernels' MFMA shape with no memory traffic
+            roof["measured_peak"] = {"value": mp, "unit": "TFLOP/s",
+                                     "frac": round(roof["achieved"] / mp, 4),
+                                     "source": "profiles/part_ceilings__mi355x.md"}
 
     glat = None
     if args.graph:

@@ -75,3 +75,11 @@ def test_code_digest_ignores_comments_not_code(tmp_path):
     assert b.code_text(str(a)) != b.code_text(str(e))
     assert b"//" in b.code_text(str(a))  # inside the string literal
     assert b"one" not in b.code_text(str(a)) and b"block" not in b.code_text(str(a))
+
+
+def test_measured_mfma_peak_is_read_from_the_committed_ceilings():
+    """The bench line's measured-peak context comes from the committed
+    ceilings summary: the best 16x16x32 f16 MFMA rate, below the published
+    2.5 PFLOP/s."""
+    mp = _bench().measured_mfma_peak()
+    assert mp is not None and 1000.0 < mp <= 2516.6
