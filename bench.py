@@ -1154,6 +1154,16 @@ def ceilings(summary: str | None) -> int:
         r["bytes_per_clk_cu"] = round(r["tbps"] * 1e12 / (n_cu * r["clock_ghz"] * 1e9), 1)
         out["lds"].append(r)
         print(json.dumps(r), flush=True)
+    out["hbm"] = []
+    for bpc in (1, 2, 4, 16):
+        r = Res()
+        rc = L.probe_hbm(C.c_int(2048), C.c_int(bpc), C.c_int(reps), C.byref(r))
+        if rc:
+            raise SystemExit(f"probe_hbm failed: {rc}")
+        rec = {"mib_per_buffer": 2048, "blocks_per_cu": bpc, "us": round(r.us, 1),
+               "gbps": round(r.rate, 1), "frac_of_8tbps": round(r.rate / PEAK_HBM_GBS, 3)}
+        out["hbm"].append(rec)
+        print(json.dumps(rec), flush=True)
     out["gload"] = []
     for wps in (1, 2, 4):
         r = call(L.probe_gload, wps, 4000)
@@ -1194,6 +1204,11 @@ def ceilings(summary: str | None) -> int:
         for r in out["lds"]:
             lines.append(f"| ds_read_b128, conflict-free | {r['waves_per_simd']} | {r['us']} | "
                          f"{r['tbps']} | {r['bytes_per_clk_cu']} | {r['clock_ghz']} |")
+        lines += ["", "| HBM streaming y = x + 1 (2 x 2 GiB) | work-groups per CU | us | GB/s (read + write) | "
+                  "of 8 TB/s |", "|---|---:|---:|---:|---:|"]
+        for r in out["hbm"]:
+            lines.append(f"| float4 loads and stores | {r['blocks_per_cu']} | {r['us']} | {r['gbps']} | "
+                         f"{r['frac_of_8tbps']} |")
         lines += ["", "| global -> LDS direct loads (L2-resident) | waves/SIMD | us | TB/s | "
                   "bytes per clock per CU | clock GHz |", "|---|---:|---:|---:|---:|---:|"]
         for r in out["gload"]:

@@ -44,6 +44,12 @@ int probe_lds(int waves_per_simd, int iters, int reps, probe_result *res);
  * for before the next.  rate: TB/s over all CUs.  waves_per_simd 1..4. */
 int probe_gload(int waves_per_simd, int iters, int reps, probe_result *res);
 
+/* HBM streaming: y = x + 1 over two buffers of `mib` MiB each (64..8192),
+ * grid of CUs x blocks_per_cu work-groups (1..32), 16-byte loads and stores.
+ * rate: GB/s of reads plus writes.  clock_ghz is not measured (0).  The two
+ * buffers are allocated and freed by the call. */
+int probe_hbm(int mib, int blocks_per_cu, int reps, probe_result *res);
+
 /* MFMA and Snake chains in the same waves, 8 MFMAs (16x16x32 f16) and 16
  * Snakes (x + sin^2(2 pi frac(x a)) / alpha, 5 VALU instructions) per
  * iteration: mode 0 Snakes only, 1 MFMAs only, 2 both in separate blocks,

@@ -173,6 +173,14 @@ __global__ __launch_bounds__(256) void gload_kernel(int iters, const float *src,
     rec_end(out, t0, r0, (float)(v[0] ^ v[3]));
 }
 
+// HBM streaming: y = x + 1 over n float4 elements, grid-stride, 16 bytes per
+// lane per load and store (read and write traffic equal).
+__global__ __launch_bounds__(256) void stream_kernel(const f4 *x, f4 *y, long n)
+{
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256)
+        y[i] = x[i] + 1.0f;
+}
+
 // MFMA chains and Snake chains in the same waves.  MODE 0: Snakes only;
 // 1: MFMAs only; 2: per iteration all MFMAs, then all Snakes (scheduling
 // barriers keep the blocks apart); 3: the same work interleaved, one MFMA
@@ -342,6 +350,47 @@ int probe_gload(int waves_per_simd, int iters, int reps, probe_result *res)
     const double bytes = (double)blocks * 4 * iters * 8 * 1024;
     if (!rc)
         res->rate = bytes / (res->us * 1e-6) / 1e12;  // TB/s over all CUs
+    return rc;
+}
+
+int probe_hbm(int mib, int blocks_per_cu, int reps, probe_result *res)
+{
+    if (mib < 64 || mib > 8192 || blocks_per_cu < 1 || blocks_per_cu > 32 || reps <= 0 || !res)
+        return 1;
+    const long n = (long)mib * (1L << 20) / 16;  // float4 elements per buffer
+    f4 *x = nullptr, *y = nullptr;
+    if (hipMalloc((void **)&x, n * 16) != hipSuccess)
+        return 2;
+    if (hipMalloc((void **)&y, n * 16) != hipSuccess) {
+        (void)hipFree(x);
+        return 2;
+    }
+    int rc = hipMemset(x, 0, n * 16) == hipSuccess ? 0 : 3;
+    const int blocks = n_cu() * blocks_per_cu;
+    hipEvent_t e0, e1;
+    if (!rc && (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess))
+        rc = 3;
+    float ms = 0.f;
+    if (!rc) {
+        hipLaunchKernelGGL(stream_kernel, dim3(blocks), dim3(256), 0, 0, x, y, n);
+        if (hipEventRecord(e0, 0) != hipSuccess)
+            rc = 3;
+        for (int i = 0; i < reps && !rc; i++)
+            hipLaunchKernelGGL(stream_kernel, dim3(blocks), dim3(256), 0, 0, x, y, n);
+        if (!rc && (hipEventRecord(e1, 0) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                    hipGetLastError() != hipSuccess ||
+                    hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+            rc = 3;
+        (void)hipEventDestroy(e0);
+        (void)hipEventDestroy(e1);
+    }
+    if (!rc) {
+        res->us = 1000.0 * ms / reps;
+        res->rate = 2.0 * n * 16 / (res->us * 1e-6) / 1e9;  // GB/s, reads + writes
+        res->clock_ghz = 0.0;
+    }
+    (void)hipFree(x);
+    (void)hipFree(y);
     return rc;
 }
 

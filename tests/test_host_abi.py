@@ -40,7 +40,8 @@ def test_probe_library_exports_its_header():
     text = open(os.path.join(ROOT, "include", "snrvq_probes.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"^\s*int\s+(\w+)\s*\(", text, flags=re.M)))
-    assert names == ["probe_cu_count", "probe_gload", "probe_lds", "probe_mfma", "probe_overlap"]
+    assert names == ["probe_cu_count", "probe_gload", "probe_hbm", "probe_lds", "probe_mfma",
+                     "probe_overlap"]
     L = C.CDLL(os.path.join(ROOT, "streaming_neural_audio_rvq_amd", "libsnrvq_probes.so"))
     for name in names:
         assert hasattr(L, name), name
