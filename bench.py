@@ -1076,18 +1076,29 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_mfma_peak():
-    """The highest v_mfma_f32_16x16x32_f16 rate of the committed ceilings
-    summary (bench.py --ceilings), TFLOP/s, or None when absent."""
+def stored_ceilings() -> dict:
+    """The JSON record of the committed ceilings summary (bench.py
+    --ceilings), or {} when absent."""
     import re
     path = os.path.join(ROOT, "profiles", "part_ceilings__mi355x.md")
     if not os.path.exists(path):
-        return None
+        return {}
     mm = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
-    if not mm:
-        return None
-    rates = [r["tflops"] for r in json.loads(mm.group(1)).get("mfma", [])
+    return json.loads(mm.group(1)) if mm else {}
+
+
+def measured_mfma_peak():
+    """The highest v_mfma_f32_16x16x32_f16 rate of the committed ceilings
+    summary, TFLOP/s, or None when absent."""
+    rates = [r["tflops"] for r in stored_ceilings().get("mfma", [])
              if r.get("shape") == "16x16x32 f16"]
+    return max(rates) if rates else None
+
+
+def measured_hbm_peak():
+    """The highest HBM streaming rate (reads + writes) of the committed
+    ceilings summary, GB/s, or None when absent."""
+    rates = [r["gbps"] for r in stored_ceilings().get("hbm", [])]
     return max(rates) if rates else None
 
 
@@ -1526,6 +1537,11 @@ def main() -> int:
         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(bpf * fps / 1e9 / PEAK_HBM_GBS, 4),
         "source": "FETCH_SIZE + WRITE_SIZE of every dispatch of the step (committed counter "
                   "summary) x this run's frames/s"}
+    hp = measured_hbm_peak()
+    if out["step_hbm"] and hp:
+        out["step_hbm"]["measured_peak"] = {
+            "value": hp, "unit": "GB/s", "frac": round(out["step_hbm"]["achieved"] / hp, 4),
+            "source": "profiles/part_ceilings__mi355x.md"}
     if others:
         out["other_workloads"] = others
     if cot:

@@ -81,5 +81,8 @@ def test_measured_mfma_peak_is_read_from_the_committed_ceilings():
     """The bench line's measured-peak context comes from the committed
     ceilings summary: the best 16x16x32 f16 MFMA rate, below the published
     2.5 PFLOP/s."""
-    mp = _bench().measured_mfma_peak()
+    b = _bench()
+    mp = b.measured_mfma_peak()
     assert mp is not None and 1000.0 < mp <= 2516.6
+    hp = b.measured_hbm_peak()
+    assert hp is not None and 1000.0 < hp <= 8000.0
