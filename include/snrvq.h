@@ -244,8 +244,11 @@ int codec_device_status(codec_t *codec, int64_t *bad_codes);
 /* ---- inspection (tests) -------------------------------------------------- */
 
 #define CODEC_CAPTURE_LATENT 0    /* projected RVQ sum, [sum n][d_lat] (decoders with a
-                                     transformer: without one the projection is folded into
-                                     the input conv and never stored) */
+                                     transformer; the step composes the projection into the
+                                     transformer's input projection, so the capture runs the
+                                     projection GEMM on the step's stored RVQ sum first, on
+                                     `stream`.  Without a transformer the projection is folded
+                                     into the input conv and this capture is refused) */
 #define CODEC_CAPTURE_DEC_INPUT 1 /* input of the conv decoder (after the transformer) */
 #define CODEC_CAPTURE_RVQ_SUM 2   /* the gathered codebook sum z, [sum n][d_cb] */
 /* Conv operands of the decoder, in network order (S = n_stages):

@@ -433,6 +433,47 @@ std::vector<float> fold_projection(const std::vector<float> &Win /*[Co][Dl][7]*/
     return out;
 }
 
+// The transformer's input projection composed with the codebook-space
+// projection (nothing between the two linear maps: the latent feeds only the
+// transformer): h = W_in (W_p z + b_p) + b_in = (W_in W_p) z + (W_in b_p + b_in).
+// Summed in fp64 over the latent index ascending, then rounded once to fp32.
+// Wf: [Dm][Dcb] (row-major, the k = 1 GEMM's packed layout); bf: [Dm].
+void fold_tf_input(const std::vector<float> &Win /*[Dm][Dl]*/, const std::vector<float> &bin,
+                   const std::vector<float> &Wp /*[Dl][Dcb]*/, const std::vector<float> &bp,
+                   int Dm, int Dl, int Dcb, std::vector<float> &Wf, std::vector<float> &bf)
+{
+    Wf.assign((size_t)Dm * Dcb, 0.f);
+    bf.assign(Dm, 0.f);
+    auto rows = [&](int o0, int o1) {
+        std::vector<double> acc(Dcb);
+        for (int o = o0; o < o1; o++) {
+            std::fill(acc.begin(), acc.end(), 0.0);
+            double bacc = 0.0;
+            for (int m = 0; m < Dl; m++) {
+                const double w = Win[(size_t)o * Dl + m];
+                const float *wp = Wp.data() + (size_t)m * Dcb;
+                for (int cc = 0; cc < Dcb; cc++)
+                    acc[cc] += w * wp[cc];
+                bacc += w * bp[m];
+            }
+            for (int cc = 0; cc < Dcb; cc++)
+                Wf[(size_t)o * Dcb + cc] = (float)acc[cc];
+            bf[o] = (float)(bacc + bin[o]);
+        }
+    };
+    unsigned nt = std::thread::hardware_concurrency();
+    nt = nt < 1 ? 1 : (nt > 16 ? 16 : nt);
+    std::vector<std::thread> th;
+    const int per = (Dm + (int)nt - 1) / (int)nt;
+    for (unsigned t = 0; t < nt; t++) {
+        const int o0 = (int)t * per, o1 = std::min(Dm, o0 + per);
+        if (o0 < o1)
+            th.emplace_back(rows, o0, o1);
+    }
+    for (auto &x : th)
+        x.join();
+}
+
 int make_lin(codec *c, const std::vector<float> &packed, const std::vector<float> &bias, int N,
              int Cout, int Cin, int taps, int dil, int s, Lin *L)
 {
@@ -619,7 +660,7 @@ int enqueue_transformer(codec *c, int B, int F, const StepMeta &m, hipStream_t s
 {
     const codec_cfg &g = c->cfg;
     const int dm = c->dm;
-    ConvArgs a = conv_args(c, c->tf_in, c->u16, 0, 1, F, m);
+    ConvArgs a = conv_args(c, c->tf_in, c->z, 0, 1, F, m);  // projection folded in
     a.out32 = c->h32;
     int rc = run_conv(c, "tf.in_proj", a, s);
     if (rc)
@@ -845,14 +886,9 @@ int enqueue_kernels(codec *c, int B, int F, const MetaLayout &ml, float *pcm, hi
     if (rc)
         return rc;
 
+    // the codebook-space projection is folded into the next layer: the input
+    // conv (decoders without a transformer) or the transformer's input projection
     ConvArgs a;
-    if (!c->fold) {
-        a = conv_args(c, c->proj, c->z, 0, 1, F, m);
-        a.out16 = g.tf_layers ? c->u16 : c->u_ext;
-        a.out_H = g.tf_layers ? 0 : 6;
-        if ((rc = run_conv(c, "proj", a, s)))
-            return rc;
-    }
     if (g.tf_layers && (rc = enqueue_transformer(c, B, F, m, s)))
         return rc;
 
@@ -1349,8 +1385,12 @@ int codec_open(const codec_tensor *weights, int32_t n_weights, const codec_cfg *
     if (g.tf_layers) {
         const int dm = g.tf_heads * g.tf_head_dim, mlp = g.tf_mlp;
         c->dm = dm;
-        if ((rc = make_lin(c, W("tf.in_proj.weight"), W("tf.in_proj.bias"), dm, dm, g.d_lat, 1,
-                           1, 1, &c->tf_in)))
+        // the input projection runs on the RVQ sum directly, the codebook-space
+        // projection composed into it (c->proj stays for latent captures)
+        std::vector<float> wf, bf;
+        fold_tf_input(W("tf.in_proj.weight"), W("tf.in_proj.bias"), W("rvq.proj.weight"),
+                      W("rvq.proj.bias"), dm, g.d_lat, g.d_cb, wf, bf);
+        if ((rc = make_lin(c, wf, bf, dm, dm, g.d_cb, 1, 1, 1, &c->tf_in)))
             return cleanup_fail(rc);
         for (int l = 0; l < g.tf_layers; l++) {
             std::string p = "tf.layer." + std::to_string(l) + ".";
@@ -1952,6 +1992,17 @@ int codec_debug_capture(codec_t *c, int32_t what, float *dst, int64_t capacity,
         ext = tf_latent ? c->u16 : c->u_ext;
         H = tf_latent ? 0 : 6;
         C = c->cfg.d_lat;
+        if (tf_latent && c->lastF <= c->allocF && c->lastB <= c->allocB) {
+            // the step ran the projection folded into the transformer's input
+            // projection: the latent is computed here, from the step's RVQ sum
+            HIPCHK(c, hipSetDevice(c->dev));
+            ConvArgs a = conv_args(c, c->proj, c->z, 0, 1, c->lastF, c->last_meta);
+            a.out16 = c->u16;
+            a.out_H = 0;
+            const int rc = run_conv(c, "proj", a, (hipStream_t)stream);
+            if (rc)
+                return rc;
+        }
     } else if (what == CODEC_CAPTURE_RVQ_SUM) {
         ext = c->z;
         H = c->fold ? 6 : 0;
