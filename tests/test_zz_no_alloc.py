@@ -14,12 +14,20 @@ from _util import host_weights, rel_err, tol_for
 pytestmark = pytest.mark.gpu
 
 
-def test_noalloc_matches_decode_chunk_device():
-    cfg = RI.get_config("c2", max_streams=16, max_frames_per_call=256)
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_noalloc_matches_decode_chunk_device(name):
+    """c2: the Qwen-shaped decoder; c3: the Fish-shaped decoder, whose
+    transformer's per-step tables (attention query blocks) also live in the
+    static array's metadata region."""
+    if name == "c2":
+        cfg = RI.get_config("c2", max_streams=16, max_frames_per_call=256)
+        calls = [[8, 3, 16, 1, 8, 4], [2, 1, 4]]  # the second call smaller, same streams
+    else:
+        cfg = RI.get_config("c3", max_streams=8, max_frames_per_call=64)
+        calls = [[8, 3, 20, 1], [2, 1, 4]]
     w = RI.make_weights(cfg)
     codec = snr.Codec(cfg, host_weights(cfg, w))
     H = codec.hop
-    calls = [[8, 3, 16, 1, 8, 4], [2, 1, 4]]  # the second call smaller, same streams
     B = len(calls[0])
     total = [sum(c[b] for c in calls if b < len(c)) for b in range(B)]
     codes = [RI.stream_codes(cfg, b, total[b], part=12) for b in range(B)]
