@@ -52,7 +52,6 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
-typedef uint32_t Chunk __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f4 mma(h8 a, h8 b, f4 c)
 {
@@ -191,15 +190,30 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
     // One activation buffer holds a1, then a2 (a1 is dead once the first
     // unit's conv7 is done), then a_out (FINAL; a2 is dead once the second
     // unit's conv7 is done).  Streamed weights (ConvT chunks included)
-    // alternate between two buffers.
+    // rotate through three buffers.
     constexpr int ACT_ELEMS = L::ELEMS;
-    constexpr int W_ELEMS = RES ? RES_ELEMS : 2 * W_BUF;
+    constexpr int W_ELEMS = RES ? RES_ELEMS : 3 * W_BUF;
 
-    __shared__ __attribute__((aligned(16))) half_t acts[ACT_ELEMS];
+    // Streamed weights arrive by direct global -> LDS loads.  The compiler
+    // orders those against LDS reads per LDS variable: with one array it
+    // leaves the waits to the kernel, with several it waits for every load in
+    // flight before the first LDS read that follows them.  The streamed shapes
+    // therefore carve their buffers out of one array (weights last: the
+    // activation offsets stay within a DS instruction's offset field); the
+    // resident shapes keep one array per buffer.
+    constexpr int OFF_PRM = (ACT_ELEMS * 2 + 15) & ~15;
+    constexpr int OFF_WOUT = OFF_PRM + P_COUNT * C * 4;
+    constexpr int OFF_W = OFF_WOUT + (((FINAL ? 7 * C / 2 : 8) * 4 + 15) & ~15);
+    __shared__ __attribute__((aligned(16))) char smem[RES ? 16 : OFF_W + W_ELEMS * 2];
+    __shared__ __attribute__((aligned(16))) half_t acts_r[RES ? ACT_ELEMS : 8];
+    __shared__ __attribute__((aligned(16))) half_t wsm_r[RES ? W_ELEMS : 8];
+    __shared__ __attribute__((aligned(16))) float prm_r[RES ? P_COUNT * C : 4];
+    __shared__ __attribute__((aligned(16))) h2 wout_r[RES && FINAL ? 7 * C / 2 : 8];
+    half_t *const acts = RES ? acts_r : (half_t *)smem;
+    half_t *const wsm = RES ? wsm_r : (half_t *)(smem + OFF_W);
+    float *const prm = RES ? prm_r : (float *)(smem + OFF_PRM);
+    h2 *const wout_s = RES ? wout_r : (h2 *)(smem + OFF_WOUT);  // final conv weights, fp16 [tap][channel]
     half_t *const a1s = acts, *const a2s = acts;
-    __shared__ __attribute__((aligned(16))) half_t wsm[W_ELEMS];
-    __shared__ __attribute__((aligned(16))) float prm[P_COUNT * C];
-    __shared__ __attribute__((aligned(16))) h2 wout_s[FINAL ? 7 * C / 2 : 8];  // final conv weights, fp16 [tap][channel]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
@@ -243,93 +257,86 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
     //   then per residual unit u, chunk c < NRC - 1: conv7 taps TPC c ..
     //   TPC c + TPC - 1 (C rows in w7_row order, TPC C columns); the last
     //   chunk: tap 6 (C x C, w7_row order) followed by the 1x1 weights (C x C)
-    //   -> wsm, buffer j & 1
-    constexpr int CT_PIECES = NT * CTW / 8, RU_PIECES = C * 2 * C / 8;
-    constexpr int PIECES = CT_PIECES > RU_PIECES ? CT_PIECES : RU_PIECES;
-    constexpr int PPT = (PIECES + NTH - 1) / NTH;  // 16-byte pieces per thread
-    Chunk pa[PPT], pb[PPT];                        // chunks jc + 1 and jc + 2
-    auto chunk_load = [&](int j, Chunk(&r)[PPT]) {
-        j %= NCH;
-        if (j < NCT) {
-            constexpr int ppr = CTW / 8;
-#pragma unroll
-            for (int i = 0; i < PPT; i++) {
-                const int k = tid + i * NTH;
-                if (k < CT_PIECES) {
-                    const int row = k / ppr, c8 = (k - row * ppr) * 8;
-                    r[i] = *(const Chunk *)(p.WT + (long)row * KT + j * CTW + c8);
-                }
-            }
-        } else {
-            const int u = (j - NCT) / NRC, c = (j - NCT) % NRC;
-            const bool last = c == NRC - 1;
-            const int ppr = (last ? 2 * C : TPC * C) / 8;
-#pragma unroll
-            for (int i = 0; i < PPT; i++) {
-                const int k = tid + i * NTH;
-                if (k < C * ppr) {
-                    const int row = k / ppr, c8 = (k - row * ppr) * 8;
-                    const half_t *src = !last || c8 < C
-                                            ? p.W7[u] + (long)row * K7 + TPC * c * C + c8
-                                            : p.W1[u] + (long)row * C + (c8 - C);
-                    r[i] = *(const Chunk *)src;
-                }
-            }
-        }
+    // go global -> LDS directly (16 bytes per lane, no register staging) into
+    // three buffers in turn: chunk jc is read from wsm + wcur while chunks
+    // jc + 1 and jc + 2 are in flight.  In a wave's instruction i the 64 lanes
+    // fill LDS pieces (i NW + wave) 64 .. + 63 (16 bytes each) of the chunk's
+    // layout; each lane loads the global piece that belongs there.
+    constexpr int CT_P = NT * CTW / 8, RU_P = C * TPC * C / 8, LAST_P = 2 * C * C / 8;
+    constexpr int MAXP = CT_P > RU_P ? (CT_P > LAST_P ? CT_P : LAST_P) : (RU_P > LAST_P ? RU_P : LAST_P);
+    constexpr int PPW = 64 * NW;  // pieces one instruction of every wave fills
+    static_assert(RES || (CT_P % PPW == 0 && RU_P % PPW == 0 && LAST_P % PPW == 0), "pieces");
+    constexpr int MAXL = MAXP / PPW;
+    auto pieces = [](int jt) {
+        return jt < NCT ? CT_P : ((jt - NCT) % NRC == NRC - 1 ? LAST_P : RU_P);
     };
-    auto chunk_store = [&](int j, const Chunk(&r)[PPT]) {
-        j %= NCH;
-        half_t *const dst = wsm + (j & 1) * W_BUF;
-        if (j < NCT) {
+    auto src_of = [&](int jt, int u) -> const half_t * {
+        if (jt < NCT) {
             constexpr int ppr = CTW / 8;
-#pragma unroll
-            for (int i = 0; i < PPT; i++) {
-                const int k = tid + i * NTH;
-                if (k < CT_PIECES) {
-                    const int row = k / ppr, c8 = (k - row * ppr) * 8;
-                    *(Chunk *)(dst + row * CTW + (CTW == 64 ? c8 ^ x128(row) : c8 ^ x64(row))) =
-                        r[i];
-                }
-            }
-        } else {
-            const bool last = (j - NCT) % NRC == NRC - 1;
-            const int ppr = (last ? 2 * C : TPC * C) / 8;
-#pragma unroll
-            for (int i = 0; i < PPT; i++) {
-                const int k = tid + i * NTH;
-                if (k < C * ppr) {
-                    const int row = k / ppr, c8 = (k - row * ppr) * 8;
-                    const int lr = w7_row(row);
-                    const int o = !last    ? lr * TPC * C + (c8 ^ xtap(lr))
-                                  : c8 < C ? lr * C + (c8 ^ x128(lr))
-                                           : C * C + row * C + ((c8 - C) ^ x128(row));
-                    *(Chunk *)(dst + o) = r[i];
-                }
-            }
+            const int row = u / ppr, c8 = ((u % ppr) * 8) ^ (CTW == 64 ? x128(row) : x64(row));
+            return p.WT + (long)row * KT + jt * CTW + c8;
         }
+        const int unit = (jt - NCT) / NRC, c = (jt - NCT) % NRC;
+        if (c < NRC - 1) {
+            constexpr int ppr = TPC * C / 8;
+            const int lr = u / ppr, c8 = ((u % ppr) * 8) ^ xtap(lr);
+            return p.W7[unit] + (long)ch7(lr >> 4, lr & 15) * K7 + TPC * c * C + c8;
+        }
+        constexpr int ppr = C / 8, HALF = C * C / 8;
+        if (u < HALF) {  // tap 6, rows in w7_row order
+            const int lr = u / ppr, c8 = ((u % ppr) * 8) ^ x128(lr);
+            return p.W7[unit] + (long)ch7(lr >> 4, lr & 15) * K7 + 6 * C + c8;
+        }
+        const int v = u - HALF, row = v / ppr, c8 = ((v % ppr) * 8) ^ x128(row);
+        return p.W1[unit] + (long)row * C + c8;
     };
-    // this thread is done with chunk jc: chunk jc + 1 goes to LDS, the loads
-    // of chunk jc + 3 start; then the work-group barrier
-    int jc = 0;
+    auto dload = [&](int j, int off) {
+        const int jt = j % NCH, np = pieces(jt);
+#pragma unroll
+        for (int i = 0; i < MAXL; i++)
+            if (i * PPW < np) {
+                const int blk = i * NW + wave;
+                __builtin_amdgcn_global_load_lds(
+                    (const void __attribute__((address_space(1))) *)src_of(jt, blk * 64 + lane),
+                    (void __attribute__((address_space(3))) *)(wsm + off + blk * 512), 16, 0, 0);
+            }
+    };
+    // wait until at most n (1 .. 3) vector memory operations are outstanding
+    auto wait_vm = [](int n) {
+        if (n <= 1)
+            __builtin_amdgcn_s_waitcnt(0x3f71);
+        else if (n == 2)
+            __builtin_amdgcn_s_waitcnt(0x3f72);
+        else
+            __builtin_amdgcn_s_waitcnt(0x3f73);
+    };
+    // this thread is done with chunk jc: the loads of chunk jc + 2 start (into
+    // the buffer of chunk jc - 1, free since the last barrier), chunk jc + 1
+    // must have landed (its loads are older than jc + 2's), then the barrier
+    int jc = 0, wcur = 0, wnext2 = 2 * W_BUF;
+    auto rot3 = [](int o) { return o + W_BUF == 3 * W_BUF ? 0 : o + W_BUF; };
+    auto lds_barrier = [&]() {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+        __asm__ volatile("s_barrier" ::: "memory");
+    };
     auto advance = [&]() {
         if constexpr (!RES) {
-            chunk_store(jc + 1, pa);
-#pragma unroll
-            for (int i = 0; i < PPT; i++)
-                pa[i] = pb[i];
-            chunk_load(jc + 3, pb);
+            dload(jc + 2, wnext2);
+            wait_vm(pieces((jc + 2) % NCH) / PPW);
+            lds_barrier();
+            wcur = rot3(wcur);
+            wnext2 = rot3(wnext2);
             jc++;
+        } else {
+            __syncthreads();
         }
-        __syncthreads();
     };
 
     if constexpr (!RES) {
-        chunk_load(0, pa);
-        chunk_store(0, pa);
-        chunk_load(1, pa);
-        chunk_load(2, pb);
+        dload(0, 0);
+        dload(1, W_BUF);
     }
-    __syncthreads();  // parameters and weights are in LDS
+    __syncthreads();  // parameters and weights are in LDS (chunk 1 landed too)
 
     const int n_tiles = p.tile_cu[p.n_streams];
     for (int g = blockIdx.x; g < n_tiles; g += gridDim.x) {
@@ -379,7 +386,7 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
 #pragma unroll
             for (int ks = 0; ks < NKT; ks++) {
                 // streamed: K step ks is columns (32 ks) mod CTW of chunk 32 ks / CTW
-                const half_t *wp = RES ? wTs + ks * 32 : wsm + ((ks * 32 / CTW) & 1) * W_BUF;
+                const half_t *wp = RES ? wTs + ks * 32 : wsm + wcur;
                 const int wld = RES ? LDT : CTW;
                 const int wk = RES ? lg * 8
                                    : ((ks * 32) % CTW + lg * 8) ^ (CTW == 64 ? x128(l16) : x64(l16));
@@ -488,7 +495,7 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
             } else {
 #pragma unroll 1
                 for (int c = 0; c < NRC - 1; c++) {  // taps TPC c .. TPC c + TPC - 1
-                    const half_t *wb = wsm + ((NCT + u * NRC + c) & 1) * W_BUF;
+                    const half_t *wb = wsm + wcur;
 #pragma unroll 1
                     for (int t2 = 0; t2 < TPC; t2++) {
                         int ro[S];
@@ -500,7 +507,7 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
                     advance();
                 }
                 // tap 6: first half of the unit's last chunk
-                const half_t *wb = wsm + ((NCT + u * NRC + NRC - 1) & 1) * W_BUF;
+                const half_t *wb = wsm + wcur;
                 int ro[S];
                 tap_offsets(6, ro);
 #pragma unroll
@@ -510,7 +517,10 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
             // the unit's input is dead from here on: its rows take the next
             // activation, whose left context a stream's first tile reads from
             // the halo fill's buffers
-            __syncthreads();
+            if constexpr (RES)
+                __syncthreads();
+            else
+                lds_barrier();  // not waiting for the weight loads in flight
             if (first && (u == 0 || FINAL)) {
                 const half_t *sx = u == 0 ? p.a2_ext + ((long)b * 18 + (long)cu0 * p.r_out) * C
                                           : p.ao_ext + ((long)b * 6 + (long)cu0 * p.r_out) * C;
@@ -523,8 +533,7 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
             // per unit: Snake(conv7 + b7) -> 1x1 conv -> + b1 + x.  The lane's conv7
             // accumulators of blocks 2k, 2k+1 hold channels 32k + 8 lg + 0..7 of
             // its row: exactly its B operand of the 1x1 conv's K step k.
-            const half_t *w1p = RES ? w1s + u * C * LD1
-                                    : wsm + ((NCT + u * NRC + NRC - 1) & 1) * W_BUF + C * C;
+            const half_t *w1p = RES ? w1s + u * C * LD1 : wsm + wcur + C * C;
             const int w1ld = RES ? LD1 : C;
 #pragma unroll
             for (int r = 0; r < S; r++) {
@@ -639,6 +648,8 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
             __syncthreads();  // a_out is read before the next tile writes a1
         }
     }  // tile loop
+    if constexpr (!RES)
+        __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): no load into LDS outlives the work-group
 
     // The last stage's work-groups also save the per-layer halos of the step
     // (every earlier layer's output is final by now; this kernel neither
