@@ -170,13 +170,13 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
     // by row (x64 / x128 below)
     static_assert(!RES || C == 32, "resident weights: 32 channels");
     constexpr int LDT = KT + 16, LD7 = K7 + 48, LD1 = C;  // resident pitches
-    // streamed (64 channels): ConvT chunks of CTW K columns (64 when two
+    // streamed (64 channels): ConvT chunks of CTW K columns (64 when three
     // buffers of it fit beside the activations, else 32); per residual unit
-    // chunks of TPC conv7 taps (two where the registers allow: fewer
-    // barriers), the last one tap 6 with the 1x1 weights
+    // chunks of TPC = 2 conv7 taps (one tap per chunk: twice the barriers,
+    // 6% slower at stride 4), the last one tap 6 with the 1x1 weights
     static_assert(RES || C == 64, "streamed weights: 64 channels");
     constexpr int CTW = NT * 64 <= 12288 ? 64 : 32;
-    constexpr int TPC = S == 3 ? 2 : 1;
+    constexpr int TPC = 2;
     constexpr int NCT = KT / CTW;         // ConvT chunks
     constexpr int NRC = 6 / TPC + 1;      // chunks per residual unit
     constexpr int NCH = NCT + 2 * NRC;    // chunks per tile (streamed)
