@@ -172,18 +172,22 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
     constexpr int LDT = KT + 16, LD7 = K7 + 48, LD1 = C;  // resident pitches
     // streamed (64 channels): ConvT chunks of CTW K columns (64 when three
     // buffers of it fit beside the activations, else 32); per residual unit
-    // chunks of TPC = 2 conv7 taps (one tap per chunk: twice the barriers,
-    // 6% slower at stride 4), the last one tap 6 with the 1x1 weights
+    // chunks of TPC conv7 taps, the last one tap 6 with the 1x1 weights.
+    // Fewer, larger chunks mean fewer barriers: three taps at stride 3 (its
+    // buffers are sized by the ConvT chunk anyway), two at stride 4 (three
+    // would fill the LDS and spill registers: 14% slower; one: 6% slower)
     static_assert(RES || C == 64, "streamed weights: 64 channels");
     constexpr int CTW = NT * 64 <= 12288 ? 64 : 32;
-    constexpr int TPC = 2;
+    constexpr int TPC = S == 3 ? 3 : 2;
     constexpr int NCT = KT / CTW;         // ConvT chunks
     constexpr int NRC = 6 / TPC + 1;      // chunks per residual unit
     constexpr int NCH = NCT + 2 * NRC;    // chunks per tile (streamed)
     // chunk permutation of the rows of a conv7 chunk (TPC C columns)
+    // (rows of 2 C halves: x256; of 3 C: x128, since 384-byte rows already
+    // put odd rows half a bank line from even ones)
     auto xtap = [](int r) { return TPC == 2 ? x256(r) : x128(r); };
     constexpr int RES_ELEMS = NT * LDT + 2 * C * LD7 + 2 * C * LD1;
-    constexpr int RU_BUF = C * 2 * C;  // one residual-unit chunk
+    constexpr int RU_BUF = C * (TPC > 2 ? TPC : 2) * C;  // one residual-unit chunk
     constexpr int CT_BUF = NT * CTW;   // one ConvT chunk
     constexpr int W_BUF = RU_BUF > CT_BUF ? RU_BUF : CT_BUF;
 
