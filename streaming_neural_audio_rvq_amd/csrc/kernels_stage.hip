@@ -270,7 +270,8 @@ __global__ __launch_bounds__(NW * 64, (stage_wg_per_cu<NW, RES>())) void stage_k
     constexpr int MAXP = CT_P > RU_P ? (CT_P > LAST_P ? CT_P : LAST_P) : (RU_P > LAST_P ? RU_P : LAST_P);
     constexpr int PPW = 64 * NW;  // pieces one instruction of every wave fills
     static_assert(RES || (CT_P % PPW == 0 && RU_P % PPW == 0 && LAST_P % PPW == 0), "pieces");
-    constexpr int MAXL = MAXP / PPW;
+    constexpr int MAXL = MAXP / PPW;  // load instructions per wave and chunk, at most
+    static_assert(RES || MAXL <= 3, "wait_vm below covers up to three loads per chunk");
     auto pieces = [](int jt) {
         return jt < NCT ? CT_P : ((jt - NCT) % NRC == NRC - 1 ? LAST_P : RU_P);
     };
