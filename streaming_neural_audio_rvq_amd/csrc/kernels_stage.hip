@@ -35,8 +35,9 @@
 // 4 consecutive channels of one row, so every epilogue works on 4 channels
 // at once.  With 32 channels the whole stage's weights (64 KiB) stay in LDS
 // for the kernel's lifetime.  With 64 channels (229 KiB) the weights stream
-// through two LDS buffers in K chunks, loaded cooperatively two chunks ahead
-// through registers; the chunk sequence runs on across phases and tiles.
+// through three LDS buffers in K chunks, loaded cooperatively two chunks
+// ahead straight from global memory into LDS; the chunk sequence runs on
+// across phases and tiles.
 //
 // Work-groups are persistent (one per CU) and walk the step's tiles; a
 // stream's rows are cut into tiles of T rows, the last one shorter.  The
