@@ -169,8 +169,8 @@ __device__ __forceinline__ int xcd_remap(int bid, int total)
 }
 
 // MINW: waves per SIMD the register allocation must leave room for (the
-// 160-row tiles ask for 2: left to itself the compiler gives them more than
-// 256 registers, i.e. one work-group per CU)
+// 128 x 128 and 160-row tiles ask for 2: left to itself the compiler gives
+// them more than 256 registers, i.e. one work-group per CU)
 template <typename T, int BM, int BN, int WM, int WN, int KSUB, bool RU = false, int NBUF = 2,
           int MINW = 1>
 __global__ __launch_bounds__(256, MINW) void conv_gemm_kernel(ConvArgs p)
@@ -613,8 +613,25 @@ __global__ __launch_bounds__(256, MINW) void conv_gemm_kernel(ConvArgs p)
         }
         return;
     }
-    // one code path per activation; per row block, the residual loads of all
-    // N fragments are issued together before any is used
+    // one code path per activation.  The residual loads: where the epilogue
+    // also writes the fp32 stream (the first residual unit of a stage), all
+    // of the tile's are issued together before any is used, so they take one
+    // memory round trip instead of one per row block (stage-2 residual unit
+    // 75 -> 72 us at 128 streams); where it writes only the 16-bit
+    // activation, those of one row block at a time (the batched form was
+    // 2-3 us slower there)
+    f4 rr[FM][FN];
+    const bool res_all = p.res && p.out32;
+    if (res_all) {
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+            const int m = m0 + rbase + i * 16 + lrow;
+            const int mc = m < p.M ? m : p.M - 1;  // loads stay in bounds
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+                rr[i][j] = *(const f4 *)(p.res + (long)mc * p.Cout + nj[j]);
+        }
+    }
     with_act(p.out16 ? p.act : ACT_NONE, [&](auto act) {
 #pragma unroll
         for (int i = 0; i < FM; i++) {
@@ -626,13 +643,14 @@ __global__ __launch_bounds__(256, MINW) void conv_gemm_kernel(ConvArgs p)
             for (int j = 0; j < FN; j++)
                 v[j] = acc[i][j];  // bias included
             if (p.res) {
-                f4 rr[FN];
+                if (!res_all) {
+#pragma unroll
+                    for (int j = 0; j < FN; j++)
+                        rr[i][j] = *(const f4 *)(p.res + (long)mc * p.Cout + nj[j]);
+                }
 #pragma unroll
                 for (int j = 0; j < FN; j++)
-                    rr[j] = *(const f4 *)(p.res + (long)mc * p.Cout + nj[j]);
-#pragma unroll
-                for (int j = 0; j < FN; j++)
-                    v[j] = v[j] + rr[j];
+                    v[j] = v[j] + rr[i][j];
             }
             if (m >= p.M)
                 continue;
@@ -863,7 +881,7 @@ hipError_t launch_conv_gemm(const ConvArgs &a0, int dtype, hipStream_t st, ConvP
     hipError_t e = hipErrorInvalidValue;
     if (dtype) {
         switch (plan.tile) {
-        case 0: e = launch_t<half_t, 128, 128, 2, 2, 2>(a, st); break;
+        case 0: e = launch_t<half_t, 128, 128, 2, 2, 2, false, 2, 2>(a, st); break;
         case 1: e = launch_t<half_t, 128, 64, 2, 2, 2>(a, st); break;
         case 2: e = launch_t<half_t, 64, 128, 2, 2, 2>(a, st); break;
         case 3: e = launch_t<half_t, 64, 64, 2, 2, 2>(a, st); break;
@@ -916,7 +934,7 @@ hipError_t launch_ru_gemm(const ConvArgs &a0, int n_cu, hipStream_t st)
     // LDS: two still fit in a CU's 160 KB)
     if (tall_rows(a, n_cu, 128))
         return launch_t<half_t, 160, 128, 2, 2, 2, true, 2, 2>(a, st);
-    return launch_t<half_t, 128, 128, 2, 2, 2, true>(a, st);
+    return launch_t<half_t, 128, 128, 2, 2, 2, true, 2, 2>(a, st);
 }
 
 }  // namespace snrvq
