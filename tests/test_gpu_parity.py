@@ -721,15 +721,16 @@ def test_elu_decoder_vs_oracle():
 # split (a split depends on the step's rows and changes the summation order),
 # so a stream's arithmetic does not depend on the other streams of its step.
 # --------------------------------------------------------------------------
-def test_fused_stage_stream_table_lds_and_global_agree():
-    B = 520
+@pytest.mark.parametrize("B", [512, 520])
+def test_fused_stage_stream_table_lds_and_global_agree(B):
+    # 512: the full LDS table against halves of it; 520: the global search
     cfg = RI.get_config("c2", max_streams=B, max_frames_per_call=2 * B, no_split_k=True)
     say("case stream table", B, "streams")
     w = RI.make_weights(cfg)
     codec = open_codec(cfg, w)
     n = [1 + (b % 2) for b in range(B)]
     codes = [RI.stream_codes(cfg, b, n[b], part=5) for b in range(B)]
-    whole = decode_full_gpu(codec, codes)          # one call of 520 streams
+    whole = decode_full_gpu(codec, codes)          # one call of all B streams
     halves = decode_full_gpu(codec, codes[:B // 2]) + decode_full_gpu(codec, codes[B // 2:])
     for b in range(B):
         assert np.array_equal(whole[b], halves[b]), b
